@@ -1,0 +1,213 @@
+"""Routed MoE FFN over 2/3-bit block-quantized experts on one MI355X (gfx950).
+
+Thin ctypes binding over ``libmoe.so`` (the C ABI in ``include/moe.h``). Every
+step of the layer runs in the library's HIP kernels; this module only checks
+tensor placement, allocates outputs and workspace with PyTorch and passes raw
+device pointers plus the current HIP stream. There is no CPU fallback: without
+the built library every call raises.
+
+Calls, in the order a layer uses them:
+    idx, gates = route_topk(logits, k)
+    grp        = group(idx, E, has_shared)                  # optional
+    ex         = Experts(qtype, E, has_shared, H, I, codes, hi, dm)
+    y          = ffn_q(x, ex, idx, gates, grouping=grp, mode="fast" | "check")
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+Q2, Q3 = 2, 3
+FAST, CHECK_F32 = 0, 2
+MAX_E = 2048
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def lib() -> C.CDLL:
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_quantized_moe_topk_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+        L.moe_status_string.argtypes = [i32]
+        L.moe_status_string.restype = C.c_char_p
+        L.moe_route_topk.argtypes = [P, i32, i32, i32, P, P, P]
+        L.moe_route_topk.restype = C.c_int
+        L.moe_group_workspace_size.argtypes = [i32, i32, i32]
+        L.moe_group_workspace_size.restype = sz
+        L.moe_group.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+        L.moe_group.restype = C.c_int
+        L.moe_experts_create.argtypes = [C.POINTER(P), i32, i32, i32, i32, i32, P, P, P]
+        L.moe_experts_create.restype = C.c_int
+        L.moe_experts_destroy.argtypes = [P]
+        L.moe_experts_destroy.restype = C.c_int
+        L.moe_ffn_q_workspace_size.argtypes = [P, i32, i32, i32]
+        L.moe_ffn_q_workspace_size.restype = sz
+        L.moe_ffn_q.argtypes = [P, i32, i32, P, P, P, i32, P, P, P, P, P, i32, P, sz, P]
+        L.moe_ffn_q.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise MoeError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_cuda(name: str, t: torch.Tensor, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def route_topk(logits: torch.Tensor, k: int):
+    """Top-k experts per token and their softmax gates: (idx int32 [T,k], gates f32 [T,k])."""
+    _need_cuda("logits", logits, torch.float32)
+    T, E = logits.shape
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    gates = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk", lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(idx), _ptr(gates),
+                                                  _stream()))
+    return idx, gates
+
+
+@dataclass
+class Grouping:
+    counts: torch.Tensor   # int32 [E+1]
+    offsets: torch.Tensor  # int32 [E+2]
+    perm: torch.Tensor     # int32 [A]
+    slot_of: torch.Tensor  # int32 [A]
+
+
+def group(idx: torch.Tensor, E: int, has_shared: bool) -> Grouping:
+    """Stable grouping of the assignments of ``idx`` by expert."""
+    _need_cuda("idx", idx, torch.int32)
+    T, k = idx.shape
+    dev = idx.device
+    A = T * (k + int(bool(has_shared)))
+    g = Grouping(torch.empty(E + 1, dtype=torch.int32, device=dev),
+                 torch.empty(E + 2, dtype=torch.int32, device=dev),
+                 torch.empty(max(A, 1), dtype=torch.int32, device=dev),
+                 torch.empty(max(A, 1), dtype=torch.int32, device=dev))
+    nbytes = lib().moe_group_workspace_size(T, k, E)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check("moe_group", lib().moe_group(_ptr(idx), T, k, E, int(bool(has_shared)), _ptr(g.counts),
+                                        _ptr(g.offsets), _ptr(g.perm), _ptr(g.slot_of), _ptr(ws),
+                                        nbytes, _stream()))
+    g.perm = g.perm[:A]
+    g.slot_of = g.slot_of[:A]
+    return g
+
+
+class Experts:
+    """One layer's packed experts (device planes in the canonical layout)."""
+
+    def __init__(self, qtype: int, E: int, has_shared: bool, H: int, I: int,
+                 codes: torch.Tensor, hi: torch.Tensor | None, dm: torch.Tensor):
+        _need_cuda("codes", codes, torch.uint8)
+        _need_cuda("dm", dm, (torch.uint16, torch.int16))
+        if hi is not None:
+            _need_cuda("hi", hi, torch.uint8)
+        E_tot = E + int(bool(has_shared))
+        nb = 3 * H * I // 32
+        if codes.numel() != E_tot * nb * 8 or dm.numel() != E_tot * nb * 2:
+            raise ValueError("plane sizes do not match the shape")
+        if qtype == Q3 and (hi is None or hi.numel() != E_tot * nb * 4):
+            raise ValueError("Q3 needs a high-bit plane of E_tot * NB * 4 bytes")
+        self.qtype, self.E, self.has_shared, self.H, self.I = qtype, E, bool(has_shared), H, I
+        self._planes = (codes, hi, dm)  # keep alive for the handle's lifetime
+        h = C.c_void_p()
+        _check("moe_experts_create",
+               lib().moe_experts_create(C.byref(h), qtype, E, int(bool(has_shared)), H, I,
+                                        _ptr(codes), _ptr(hi), _ptr(dm)))
+        self._h = h
+
+    @property
+    def handle(self) -> C.c_void_p:
+        return self._h
+
+    def workspace_size(self, T: int, k: int, mode: int = FAST) -> int:
+        return int(lib().moe_ffn_q_workspace_size(self._h, T, k, mode))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().moe_experts_destroy(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_MODES = {"fast": FAST, "check": CHECK_F32, FAST: FAST, CHECK_F32: CHECK_F32}
+
+
+def ffn_q(x: torch.Tensor, ex: Experts, idx: torch.Tensor, gates: torch.Tensor,
+          grouping: Grouping | None = None, mode="fast", workspace: torch.Tensor | None = None,
+          out: torch.Tensor | None = None) -> torch.Tensor:
+    """Expert FFN + gate-weighted combine for every token of ``x``.
+
+    ``x``: [T, H] float32 or bfloat16. Returns ``y`` [T, H] with x's dtype in
+    fast mode, float32 in check mode.
+    """
+    mode = _MODES[mode]
+    _need_cuda("x", x, (torch.float32, torch.bfloat16))
+    _need_cuda("idx", idx, torch.int32)
+    _need_cuda("gates", gates, torch.float32)
+    T, H = x.shape
+    k = idx.shape[1]
+    if H != ex.H or idx.shape[0] != T or tuple(gates.shape) != (T, k):
+        raise ValueError("shape mismatch between x, idx, gates and the experts")
+    xdt = F32 if x.dtype == torch.float32 else BF16
+    ydtype = torch.float32 if mode == CHECK_F32 else x.dtype
+    y = out if out is not None else torch.empty((T, H), dtype=ydtype, device=x.device)
+    _need_cuda("out", y, ydtype)
+    nbytes = ex.workspace_size(T, k, mode)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    g = grouping
+    _check("moe_ffn_q", lib().moe_ffn_q(
+        _ptr(x), xdt, T, ex.handle, _ptr(idx), _ptr(gates), k,
+        _ptr(g.counts) if g else None, _ptr(g.offsets) if g else None,
+        _ptr(g.perm) if g else None, _ptr(g.slot_of) if g else None,
+        _ptr(y), mode, _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+__all__ = ["route_topk", "group", "Grouping", "Experts", "ffn_q", "lib", "status_string",
+           "MoeError", "Q2", "Q3", "F32", "BF16", "FAST", "CHECK_F32", "MAX_E", "LIB_PATH"]

@@ -1,0 +1,191 @@
+// Host implementation of the C ABI declared in include/moe.h: argument checks,
+// workspace layout and kernel dispatch. Nothing here allocates device memory.
+#include <new>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace moe {
+bool gemv_supported(int H, int I);
+}
+
+using moe::Experts;
+
+struct moe_experts {
+  Experts d;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte layout of the moe_ffn_q workspace.
+struct FfnLayout {
+  size_t counts, offsets, perm, slot_of, group, sched, h, o, total;
+};
+
+FfnLayout ffn_layout(const Experts& ex, int T, int k, int mode) {
+  FfnLayout L{};
+  const size_t A = (size_t)T * (k + ex.has_shared);
+  size_t off = 0;
+  L.counts = off;  off = align_up(off + sizeof(int32_t) * (ex.E + 1));
+  L.offsets = off; off = align_up(off + sizeof(int32_t) * (ex.E + 2));
+  L.perm = off;    off = align_up(off + sizeof(int32_t) * A);
+  L.slot_of = off; off = align_up(off + sizeof(int32_t) * A);
+  L.group = off;   off = align_up(off + moe::group_scratch_bytes(T, k, ex.E));
+  L.sched = off;   off = align_up(off + sizeof(int32_t) * moe::sched_words(ex.E_tot, (int)A));
+  L.h = off;       off = align_up(off + (mode == MOE_CHECK_F32 ? 4 : 2) * A * (size_t)ex.I);
+  L.o = off;       off = align_up(off + sizeof(float) * A * (size_t)ex.H);
+  L.total = off;
+  return L;
+}
+
+inline char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape, type or mode";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* idx, float* gates,
+                   void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_E) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * E > 0x7FFFFFFFLL || (long long)T * k > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !idx || !gates) return MOE_ERR_INVALID_ARG;
+  return status_of(moe::launch_topk(logits, T, E, k, idx, gates, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_group_workspace_size(int32_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_E) return 0;
+  return moe::group_scratch_bytes(T, k, E);
+}
+
+int moe_group(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t has_shared,
+              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_of, void* ws,
+              size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || E < 1 || (has_shared != 0 && has_shared != 1)) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_E) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * (k + has_shared) > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!idx || !perm || !slot_of)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::group_scratch_bytes(T, k, E);
+  if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE;
+  return status_of(moe::launch_group(idx, T, k, E, has_shared, counts, offsets, perm, slot_of, ws,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int moe_experts_create(moe_experts** out, int32_t qtype, int32_t E, int32_t has_shared, int32_t H,
+                       int32_t I, const void* codes, const void* hi, const void* dm) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (qtype != MOE_Q2 && qtype != MOE_Q3) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || (has_shared != 0 && has_shared != 1) || H < 64 || I < 64) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_E) return MOE_ERR_UNSUPPORTED;
+  if (H % 64 || I % 64) return MOE_ERR_UNSUPPORTED;
+  if (!codes || !dm || (qtype == MOE_Q3) != (hi != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(dm) || (hi && !aligned16(hi))) return MOE_ERR_INVALID_ARG;
+  moe_experts* ex = new (std::nothrow) moe_experts;
+  if (!ex) return MOE_ERR_INVALID_ARG;
+  ex->d.qtype = qtype;
+  ex->d.E = E;
+  ex->d.has_shared = has_shared;
+  ex->d.E_tot = E + has_shared;
+  ex->d.H = H;
+  ex->d.I = I;
+  ex->d.nb = (size_t)3 * H * I / 32;
+  ex->d.codes = static_cast<const uint8_t*>(codes);
+  ex->d.hi = static_cast<const uint8_t*>(hi);
+  ex->d.dm = static_cast<const uint16_t*>(dm);
+  *out = ex;
+  return MOE_OK;
+}
+
+int moe_experts_destroy(moe_experts* ex) {
+  delete ex;
+  return MOE_OK;
+}
+
+size_t moe_ffn_q_workspace_size(const moe_experts* ex, int32_t T, int32_t k, int32_t mode) {
+  if (!ex || T < 0 || k < 1 || k > ex->d.E) return 0;
+  if (mode != MOE_FAST && mode != MOE_CHECK_F32) return 0;
+  return ffn_layout(ex->d, T, k, mode).total;
+}
+
+int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, const int32_t* idx,
+              const float* gates, int32_t k, const int32_t* counts, const int32_t* offsets,
+              const int32_t* perm, const int32_t* slot_of, void* y, int32_t mode, void* ws,
+              size_t ws_bytes, void* stream) {
+  if (!ex || T < 0 || k < 1 || k > ex->d.E) return MOE_ERR_INVALID_ARG;
+  if (xdtype != MOE_F32 && xdtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_FAST && mode != MOE_CHECK_F32) return MOE_ERR_INVALID_ARG;
+  const Experts& d = ex->d;
+  const long long A = (long long)T * (k + d.has_shared);
+  if (A > 0x7FFFFFFFLL || A * d.H > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  const int given = (counts != nullptr) + (offsets != nullptr) + (perm != nullptr) + (slot_of != nullptr);
+  if (given != 0 && given != 4) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !idx || !gates || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  const FfnLayout L = ffn_layout(d, T, k, mode);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  moe::FfnArgs a{};
+  a.x = x;
+  a.xdtype = xdtype;
+  a.T = T;
+  a.k = k;
+  a.idx = idx;
+  a.gates = gates;
+  a.y = y;
+  a.sched = reinterpret_cast<int*>(at(ws, L.sched));
+  a.h = at(ws, L.h);
+  a.o = reinterpret_cast<float*>(at(ws, L.o));
+  if (given == 4) {
+    a.counts = counts;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.slot_of = slot_of;
+  } else {
+    int32_t* c = reinterpret_cast<int32_t*>(at(ws, L.counts));
+    int32_t* o = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+    int32_t* p = reinterpret_cast<int32_t*>(at(ws, L.perm));
+    int32_t* so = reinterpret_cast<int32_t*>(at(ws, L.slot_of));
+    hipError_t e = moe::launch_group(idx, T, k, d.E, d.has_shared, c, o, p, so, at(ws, L.group), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    a.counts = c;
+    a.offsets = o;
+    a.perm = p;
+    a.slot_of = so;
+  }
+  hipError_t e;
+  if (mode == MOE_CHECK_F32) {
+    e = moe::launch_sched(d, a, 0, s);
+    if (e == hipSuccess) e = moe::launch_ffn_check(d, a, s);
+    if (e == hipSuccess) e = moe::launch_combine(d, a, 1, s);
+  } else {
+    const int gemv_max = moe::gemv_supported(d.H, d.I) ? moe::kGemvMaxTokens : 0;
+    e = moe::launch_sched(d, a, gemv_max, s);
+    if (e == hipSuccess) e = moe::launch_ffn_fast(d, a, s);
+    if (e == hipSuccess) e = moe::launch_combine(d, a, xdtype == MOE_F32, s);
+  }
+  return status_of(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+// Stable grouping of token-to-expert assignments by expert (counting sort).
+//
+// Prefill multiplies each expert once for all the tokens routed to it in a
+// chunk ("Strata - the details", "Faster prompts"), which needs the chunk's
+// assignments grouped by expert. The grouping here is a stable counting sort
+// on the flat assignment id t*k + j:
+//   1. every wave owns a segment of kSeg consecutive ids and counts its experts;
+//   2. an exclusive scan over (expert, segment) in expert-major order gives each
+//      segment the first output slot of each of its experts;
+//   3. every wave walks its segment in id order, 64 ids at a time; lanes holding
+//      the same expert find each other with one ballot per key bit, take ranks
+//      by lane order, and the group's last lane advances the expert's counter.
+// Order inside an expert is therefore ascending id, identical on every run.
+// Small inputs run all three steps in one workgroup; large ones in 3 launches.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSeg = 1024;  // assignment ids per wave segment
+
+__device__ inline int key_bits(int E) { return E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1)); }
+
+// Count the experts of ids [f0, f1) into hist[e * stride] (LDS, zeroed by caller).
+__device__ inline void wave_count(const int32_t* __restrict__ idx, int f0, int f1, int E,
+                                  int* hist, int stride) {
+  const int lane = threadIdx.x & 63;
+  for (int f = f0 + lane; f < f1; f += 64) {
+    const int e = idx[f];
+    if (e >= 0 && e < E) atomicAdd(&hist[e * stride], 1);
+  }
+}
+
+// Stable scatter of ids [f0, f1) using the running counters cnt[e * stride].
+__device__ inline void wave_scatter(const int32_t* __restrict__ idx, int f0, int f1, int E,
+                                    int* cnt, int stride, int32_t* __restrict__ perm,
+                                    int32_t* __restrict__ slot_of) {
+  const int lane = threadIdx.x & 63;
+  const int nbits = key_bits(E);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = f0; base < f1; base += 64) {
+    const int f = base + lane;
+    const int e = f < f1 ? idx[f] : -1;
+    const bool ok = e >= 0 && e < E;
+    uint64_t mask = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const uint64_t bal = __ballot(bit);
+      mask &= bit ? bal : ~bal;
+    }
+    if (ok) {
+      const int rank = __popcll(mask & below);
+      const int n = __popcll(mask);
+      const int pos = cnt[e * stride] + rank;
+      perm[pos] = f;
+      slot_of[f] = pos;
+      if (rank == n - 1) cnt[e * stride] = pos + 1;
+    }
+  }
+}
+
+// Block-wide exclusive scan of data[0..n) in place; returns the total.
+// blockDim.x must be a multiple of 64 and at most 1024.
+__device__ int block_exclusive_scan(int* data, int n, int* tmp /* LDS, >= 1024 */) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += data[i];
+  tmp[tid] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the per-thread sums
+  for (int off = 1; off < nt; off <<= 1) {
+    const int v = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += v;
+    __syncthreads();
+  }
+  int run = tid == 0 ? 0 : tmp[tid - 1];
+  const int total = tmp[nt - 1];
+  __syncthreads();
+  for (int i = lo; i < hi; ++i) {
+    const int v = data[i];
+    data[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  return total;
+}
+
+__device__ inline void write_offsets(const int* base, int nseg, int E, int T, int k, int has_shared,
+                                     int32_t* counts, int32_t* offsets) {
+  const int AR = T * k;
+  for (int e = threadIdx.x; e <= E + 1; e += blockDim.x) {
+    if (e < E) offsets[e] = base[e * nseg];
+    else if (e == E) offsets[E] = AR;
+    else offsets[E + 1] = AR + (has_shared ? T : 0);
+  }
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+    if (e < E) counts[e] = (e + 1 < E ? base[(e + 1) * nseg] : AR) - base[e * nseg];
+    else counts[E] = has_shared ? T : 0;
+  }
+}
+
+__device__ inline void write_shared(int T, int k, int has_shared, int32_t* perm, int32_t* slot_of) {
+  if (!has_shared) return;
+  const int AR = T * k;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
+    perm[AR + t] = AR + t;
+    slot_of[AR + t] = AR + t;
+  }
+}
+
+// All three steps in one workgroup of 1024 threads (16 waves = 16 segments).
+__global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ idx, int T, int k,
+                                                    int E, int has_shared, int nseg,
+                                                    int32_t* counts, int32_t* offsets,
+                                                    int32_t* perm, int32_t* slot_of) {
+  extern __shared__ int lds[];  // [E * nseg] bases, then [1024] scan scratch
+  int* hist = lds;
+  int* tmp = lds + E * nseg;
+  const int AR = T * k;
+  for (int i = threadIdx.x; i < E * nseg; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const int seg = threadIdx.x >> 6;
+  const int f0 = min(AR, seg * kSeg), f1 = min(AR, f0 + kSeg);
+  if (seg < nseg) wave_count(idx, f0, f1, E, hist + seg, nseg);
+  __syncthreads();
+  block_exclusive_scan(hist, E * nseg, tmp);
+  write_offsets(hist, nseg, E, T, k, has_shared, counts, offsets);
+  __syncthreads();  // the bases are read above before the scatter advances them
+  if (seg < nseg) wave_scatter(idx, f0, f1, E, hist + seg, nseg, perm, slot_of);
+  write_shared(T, k, has_shared, perm, slot_of);
+}
+
+// Large inputs, step 1: per-segment counts into hist[e * nseg + seg] (global).
+__global__ __launch_bounds__(256) void group_count(const int32_t* __restrict__ idx, int T, int k,
+                                                   int E, int has_shared, int nseg, int* hist,
+                                                   int32_t* perm, int32_t* slot_of) {
+  extern __shared__ int lds[];  // [4][E]
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int* h = lds + w * E;
+  for (int e = lane; e < E; e += 64) h[e] = 0;
+  __syncthreads();
+  const int AR = T * k;
+  const int seg = blockIdx.x * 4 + w;
+  if (seg < nseg) {
+    const int f0 = seg * kSeg, f1 = min(AR, f0 + kSeg);
+    wave_count(idx, f0, f1, E, h, 1);
+  }
+  __syncthreads();
+  if (seg < nseg)
+    for (int e = lane; e < E; e += 64) hist[e * nseg + seg] = h[e];
+  write_shared(T, k, has_shared, perm, slot_of);
+}
+
+// Step 2: one workgroup scans hist in place and writes counts / offsets.
+__global__ __launch_bounds__(1024) void group_scan(int T, int k, int E, int has_shared, int nseg,
+                                                   int* hist, int32_t* counts, int32_t* offsets) {
+  __shared__ int tmp[1024];
+  block_exclusive_scan(hist, E * nseg, tmp);
+  write_offsets(hist, nseg, E, T, k, has_shared, counts, offsets);
+}
+
+// Step 3: per-segment stable scatter from the scanned bases.
+__global__ __launch_bounds__(256) void group_scatter(const int32_t* __restrict__ idx, int T, int k,
+                                                     int E, int nseg, const int* hist,
+                                                     int32_t* perm, int32_t* slot_of) {
+  extern __shared__ int lds[];  // [4][E]
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int seg = blockIdx.x * 4 + w;
+  if (seg >= nseg) return;  // no barrier below: each wave only touches its own LDS row
+  int* cnt = lds + w * E;
+  for (int e = lane; e < E; e += 64) cnt[e] = hist[e * nseg + seg];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int AR = T * k;
+  const int f0 = seg * kSeg, f1 = min(AR, f0 + kSeg);
+  wave_scatter(idx, f0, f1, E, cnt, 1, perm, slot_of);
+}
+
+inline int nseg_of(int T, int k) { return (T * k + kSeg - 1) / kSeg; }
+// One workgroup when its LDS (bases + scan scratch) stays within 64 KiB.
+inline bool use_fused(int T, int k, int E) {
+  const int n = nseg_of(T, k);
+  return n <= 16 && (size_t)E * n + 1024 <= 16384;
+}
+
+}  // namespace
+
+size_t group_scratch_bytes(int T, int k, int E) {
+  if (use_fused(T, k, E)) return 0;
+  return (size_t)E * nseg_of(T, k) * sizeof(int);
+}
+
+hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* slot_of, void* scratch,
+                        hipStream_t s) {
+  const int nseg = nseg_of(T, k);
+  if (use_fused(T, k, E)) {
+    const size_t lds = ((size_t)E * nseg + 1024) * sizeof(int);
+    hipLaunchKernelGGL(group_fused, dim3(1), dim3(1024), lds, s, idx, T, k, E, has_shared, nseg,
+                       counts, offsets, perm, slot_of);
+    return hipGetLastError();
+  }
+  int* hist = static_cast<int*>(scratch);
+  const int blocks = (nseg + 3) / 4;
+  const size_t lds = (size_t)4 * E * sizeof(int);
+  hipLaunchKernelGGL(group_count, dim3(blocks), dim3(256), lds, s, idx, T, k, E, has_shared, nseg,
+                     hist, perm, slot_of);
+  hipLaunchKernelGGL(group_scan, dim3(1), dim3(1024), 0, s, T, k, E, has_shared, nseg, hist,
+                     counts, offsets);
+  hipLaunchKernelGGL(group_scatter, dim3(blocks), dim3(256), lds, s, idx, T, k, E, nseg, hist,
+                     perm, slot_of);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,167 @@
+/*
+ * moe.h -- C ABI of the routed mixture-of-experts FFN layer over block-quantized
+ * expert weights, for one AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one the Strata pages describe: a router scores the 512
+ * experts of a layer and each token is sent to the 10 best; shared experts run
+ * for every token ("Strata - the details", section "How it works"; the Strata
+ * README, "How does it work?"); every expert is three matrices, its gate, up and
+ * down rows ("Strata - the details", "Low-RAM mode without experts.bin"), stored
+ * as 2-bit or 3-bit block-quantized packs ("Speed (measured)", "Which model?").
+ * It runs over decode verify windows of a few tokens ("How it works":
+ * speculation) and over prefill chunks of up to 8,192 tokens ("Faster prompts").
+ *
+ * Conventions shared by every call
+ *   - Every buffer pointer is a DEVICE pointer (HBM), unless a comment says
+ *     otherwise. The caller allocates and owns every buffer; the library never
+ *     allocates device memory and keeps no pointer after a call returns, except
+ *     the weight planes a moe_experts handle refers to.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls validate their arguments on the host, enqueue kernels on `stream`
+ *     and return without synchronising. Results are ready when the stream is.
+ *   - Return value: MOE_OK, or a negative moe_status. Argument errors are
+ *     detected on the host before anything is enqueued; nothing is written then.
+ *     MOE_ERR_HIP means a kernel launch failed (hipGetLastError); faults inside
+ *     a kernel surface at the caller's next synchronisation of the stream.
+ *   - Element counts are int32; sizes in bytes are size_t.
+ *   - No call keeps global state; calls on different streams may run
+ *     concurrently as long as they do not share output or workspace buffers.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* a size, pointer or enum is out of range     */
+#define MOE_ERR_UNSUPPORTED (-2) /* valid, but outside what the kernels handle */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace smaller than the *_size() query  */
+#define MOE_ERR_HIP (-4)         /* a HIP runtime call or launch failed         */
+
+/* ---- enums -------------------------------------------------------------- */
+#define MOE_F32 0  /* activations x and output y are float32               */
+#define MOE_BF16 1 /* activations x and output y are bfloat16 (uint16 bits) */
+
+#define MOE_Q2 2 /* 2-bit codes, w = d*q + m, q in 0..3, 32-weight blocks */
+#define MOE_Q3 3 /* 3-bit codes, w = d*q + m, q in 0..7, 32-weight blocks */
+
+/* FFN compute modes.
+ * MOE_FAST: dequantised weights and activations enter the matrix cores as fp16
+ *   (decode experts: exact codes, bf16 activations, fp32 block scaling), fp32
+ *   accumulation, intermediate h rounded to fp16/bf16, y rounded to the
+ *   activation dtype. Expected agreement with an exact evaluation: about 1e-3
+ *   relative L2 per token row. Requires |x|, |h| < 65504 (fp16 range).
+ * MOE_CHECK_F32: every step in fp32 on the vector ALUs (parity mode); y is
+ *   always float32. Agreement about 1e-6. */
+#define MOE_FAST 0
+#define MOE_CHECK_F32 2
+
+/* ---- limits ------------------------------------------------------------- */
+#define MOE_MAX_E 2048 /* routed experts per layer */
+
+/* ---- routing ------------------------------------------------------------ */
+
+/* Top-k expert selection and gates, per token.
+ *
+ * Per token t (the router step of "How it works"; 10 of 512 experts per token):
+ *   idx[t][0..k-1]  = the k experts with the largest logits, in descending rank;
+ *                     equal logits (IEEE equality, +0 == -0) go to the lower
+ *                     expert index; NaN ranks below every number.
+ *   gates[t][j]     = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0), l_j the
+ *                     logit of idx[t][j]: a softmax over the selected logits,
+ *                     equal to a softmax over all E renormalised over the top k.
+ * logits: [T][E] float32, row-major.  idx: [T][k] int32.  gates: [T][k] float32.
+ * Requires 1 <= E <= MOE_MAX_E, 1 <= k <= E, T >= 0 (T == 0: no launch).
+ * Gates are finite when the selected logits are finite. */
+int moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *idx,
+                   float *gates, void *stream);
+
+/* ---- grouping ----------------------------------------------------------- */
+
+/* Workspace bytes moe_group needs for these sizes (device memory, any content). */
+size_t moe_group_workspace_size(int32_t T, int32_t k, int32_t E);
+
+/* Stable grouping of the token-to-expert assignments by expert (a counting sort;
+ * the pages' prefill groups the chunk's tokens per expert before the expert
+ * matrices run: "Faster prompts").
+ *
+ * Assignment ids: routed assignment (t, j) has id t*k + j; with has_shared, the
+ * shared expert's assignment of token t has id T*k + t and belongs to group E.
+ * A = T*(k + has_shared) assignments in all.
+ *   counts [E+1]  : assignments per expert (counts[E] = T with a shared expert, else 0)
+ *   offsets[E+2]  : exclusive prefix sum of counts; offsets[E+1] = A
+ *   perm   [A]    : the assignment ids of group e at perm[offsets[e] .. offsets[e+1]),
+ *                   in ascending id order (so ascending token order)
+ *   slot_of[A]    : inverse of perm: perm[slot_of[a]] == a
+ * idx [T][k] int32, every entry in [0, E). Entries outside that range are not
+ * detected; the kernels stay in bounds and skip them, and the affected outputs
+ * are unspecified.
+ * ws: device scratch of at least moe_group_workspace_size(T, k, E) bytes. */
+int moe_group(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t has_shared,
+              int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *slot_of, void *ws,
+              size_t ws_bytes, void *stream);
+
+/* ---- experts ------------------------------------------------------------ */
+
+/* An immutable description of one layer's packed experts. The handle is a small
+ * host object; it refers to the caller's device planes, which must stay alive
+ * and unchanged until moe_experts_destroy.
+ *
+ * Packed layout (fixed by this library; the pages publish none):
+ *   experts 0..E-1 routed, then the shared expert (index E) when has_shared;
+ *   each expert holds NB = 3*H*I/32 blocks of 32 weights: its gate matrix [I][H],
+ *   then up [I][H], then down [H][I], each row-major with blocks along a row.
+ *   codes: NB * 8 bytes per expert. Weight j (0..31) of a block is in byte j/4 at
+ *          bits 2*(j%4) (the low two bits of the code for Q3).
+ *   hi   : Q3 only, NB * 4 bytes per expert; bit j of the block's little-endian
+ *          32-bit word is bit 2 of code j. Pass NULL for Q2.
+ *   dm   : NB * 2 uint16 per expert: fp16 bits of d, then of m, per block.
+ *   Weight value: w = d*q + m.
+ * Plane bases must be 16-byte aligned. Requires H, I multiples of 256 (the
+ * decode kernels' row chunk), 1 <= E <= MOE_MAX_E. */
+typedef struct moe_experts moe_experts;
+
+int moe_experts_create(moe_experts **out, int32_t qtype, int32_t E, int32_t has_shared,
+                       int32_t H, int32_t I, const void *codes, const void *hi,
+                       const void *dm);
+int moe_experts_destroy(moe_experts *ex);
+
+/* ---- expert FFN and combine ---------------------------------------------- */
+
+/* Workspace bytes moe_ffn_q needs for T tokens, k experts per token, `mode`,
+ * including room for the grouping when the caller does not pass one. */
+size_t moe_ffn_q_workspace_size(const moe_experts *ex, int32_t T, int32_t k, int32_t mode);
+
+/* The routed expert FFN with gate-weighted combine, for T tokens.
+ *
+ * For every token t (expert = gate/up/down rows, "Low-RAM mode without
+ * experts.bin"; shared experts for every token, "How it works"):
+ *   o(e, x) = Wd_e . ( silu(Wg_e . x) * (Wu_e . x) ),   silu(z) = z / (1 + e^-z)
+ *   y[t]    = sum_{j<k} gates[t][j] * o(idx[t][j], x[t])  +  o(shared, x[t])
+ * with every weight dequantised as w = d*q + m from the handle's planes.
+ *
+ * x     : [T][H], dtype xdtype (MOE_F32 or MOE_BF16).
+ * idx   : [T][k] int32 in [0, E); gates: [T][k] float32 (any values).
+ * counts/offsets/perm/slot_of: a grouping of idx exactly as moe_group writes
+ *         it, or all four NULL to have it computed inside `ws`.
+ * y     : [T][H]; dtype xdtype in MOE_FAST, float32 in MOE_CHECK_F32.
+ * ws    : device scratch of at least moe_ffn_q_workspace_size(ex, T, k, mode).
+ * T == 0 is valid and launches nothing. */
+int moe_ffn_q(const void *x, int32_t xdtype, int32_t T, const moe_experts *ex,
+              const int32_t *idx, const float *gates, int32_t k, const int32_t *counts,
+              const int32_t *offsets, const int32_t *perm, const int32_t *slot_of, void *y,
+              int32_t mode, void *ws, size_t ws_bytes, void *stream);
+
+/* A static, human-readable description of a status code (host string). */
+const char *moe_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Bars: top-k indices and every grouping array bit-exact; gates within 1e-6
+absolute; FFN output rows within relative L2 1e-4 (fp32 check mode) and 1e-2
+(fast mode) of the float64 oracle. Inputs are the seeded synthetic layers.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import CONFIGS, make_layer, make_logits
+from gpu_util import (experts_of, log, oracle_rows, rel_l2_rows, torch_cuda, upload, y_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    torch_cuda()
+
+TOL_CHECK = 1e-4
+TOL_FAST = 1e-2
+
+_cache = {}
+
+
+def layer_for(cid, seed=0, layer=0):
+    key = (cid, seed, layer)
+    if key not in _cache:
+        lay = make_layer(CONFIGS[cid], seed=seed, layer=layer)
+        _cache[key] = (lay, upload(lay))
+    return _cache[key]
+
+
+def gpu_route(logits_np, k):
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    idx, gates = moe.route_topk(torch.from_numpy(np.ascontiguousarray(logits_np)).cuda(), k)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), gates.cpu().numpy()
+
+
+def check_route(logits_np, k, what):
+    log(f"[route] {what} T={logits_np.shape[0]} E={logits_np.shape[1]} k={k}")
+    idx_o, g_o = oracle.route(logits_np, k)
+    idx_g, g_g = gpu_route(logits_np, k)
+    assert np.array_equal(idx_g, idx_o), what
+    assert np.max(np.abs(g_g - g_o), initial=0.0) <= 1e-6, what
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2, 4])
+def test_route_bit_exact(cid):
+    cfg = CONFIGS[cid]
+    check_route(make_logits(cfg, seed=0), cfg.k, f"cfg{cid}")
+
+
+def test_route_prefill_8k_all_layers():
+    cfg = CONFIGS[3]
+    for layer in range(cfg.layers):
+        check_route(make_logits(cfg, seed=0, layer=layer), cfg.k, f"cfg3 layer {layer}")
+
+
+def test_route_adversarial():
+    rng = np.random.default_rng(7)
+    check_route(rng.integers(0, 4, size=(300, 64)).astype(np.float32), 10, "ties")
+    check_route(np.full((17, 16), 0.5, np.float32), 16, "all equal, k=E")
+    check_route(np.full((3, 16), -2.0, np.float32), 1, "all equal, k=1")
+    lg = np.array([[-0.0, 0.0, np.nan, -1.0, np.nan, 0.5, -np.inf, 3e38]], np.float32)
+    idx_o, _ = oracle.route(lg, 8)
+    idx_g, _ = gpu_route(lg, 8)
+    assert np.array_equal(idx_g, idx_o)
+    check_route(rng.standard_normal((9, 2048)).astype(np.float32), 64, "E=2048 k=64")
+    check_route(rng.standard_normal((5, 1)).astype(np.float32), 1, "E=1")
+    check_route(rng.standard_normal((1, 700)).astype(np.float32), 700, "k=E=700")
+
+
+def gpu_group(idx_np, E, shared):
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    g = moe.group(torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).cuda(), E, shared)
+    torch.cuda.synchronize()
+    return (g.counts.cpu().numpy(), g.offsets.cpu().numpy(), g.perm.cpu().numpy(),
+            g.slot_of.cpu().numpy())
+
+
+def check_group(idx_np, E, shared, what):
+    log(f"[group] {what} T={idx_np.shape[0]} k={idx_np.shape[1]} E={E} shared={shared}")
+    ref = oracle.group(idx_np, E, shared)
+    got = gpu_group(idx_np, E, shared)
+    for name, a, b in zip(("counts", "offsets", "perm", "slot_of"), got, ref):
+        assert np.array_equal(a, b), f"{what}: {name} differs"
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4])
+def test_group_bit_exact(cid):
+    cfg = CONFIGS[cid]
+    idx, _ = oracle.route(make_logits(cfg, seed=0), cfg.k)
+    check_group(idx, cfg.E, bool(cfg.shared), f"cfg{cid}")
+
+
+def test_group_edges():
+    rng = np.random.default_rng(3)
+    check_group(np.tile(np.array([5, 0, 2], np.int32), (5000, 1)), 8, True, "one expert per slot")
+    check_group(rng.integers(0, 64, size=(20000, 10)).astype(np.int32), 64, False, "T=20000 E=64")
+    check_group(rng.integers(0, 2048, size=(3000, 7)).astype(np.int32), 2048, True, "E=2048")
+    check_group(np.zeros((1, 1), np.int32), 1, False, "T=1 E=1")
+    check_group(rng.integers(0, 3, size=(1700, 2)).astype(np.int32), 3, True, "E=3 ragged")
+
+
+def run_ffn(lay, dev, idx_np, gates_np, mode, use_gpu_grouping=False):
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfg = lay["cfg"]
+    ex = experts_of(lay, dev)
+    idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).cuda()
+    gates = torch.from_numpy(np.ascontiguousarray(gates_np, dtype=np.float32)).cuda()
+    grp = moe.group(idx, cfg.E, bool(cfg.shared)) if use_gpu_grouping else None
+    y = moe.ffn_q(dev["x"], ex, idx, gates, grouping=grp, mode=mode)
+    torch.cuda.synchronize()
+    out = y_to_f64(y)
+    ex.close()
+    return out
+
+
+@pytest.mark.parametrize("mode,tol", [("check", TOL_CHECK), ("fast", TOL_FAST)])
+@pytest.mark.parametrize("cid", [0, 1, 4, 2])
+def test_ffn_parity(cid, mode, tol):
+    lay, dev = layer_for(cid)
+    cfg = lay["cfg"]
+    idx, gates = oracle.route(lay["logits"], cfg.k)
+    log(f"[ffn] cfg{cid} mode={mode} T={cfg.T}")
+    y = run_ffn(lay, dev, idx, gates, mode, use_gpu_grouping=(cid % 2 == 0))
+    ref = oracle_rows(lay, idx, gates)
+    err = rel_l2_rows(y, ref)
+    log(f"[ffn] cfg{cid} {mode}: max rel-L2 {err.max():.3e}  p99 {np.percentile(err, 99):.3e}  "
+        f"mean {err.mean():.3e}")
+    assert err.max() <= tol
+
+
+@pytest.mark.parametrize("cid", [0, 1, 4])
+def test_layer_end_to_end(cid):
+    """route -> group -> ffn all on the GPU, against the oracle's own route."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    lay, dev = layer_for(cid)
+    cfg = lay["cfg"]
+    log(f"[layer] cfg{cid}")
+    idx, gates = moe.route_topk(dev["logits"], cfg.k)
+    grp = moe.group(idx, cfg.E, bool(cfg.shared))
+    ex = experts_of(lay, dev)
+    y = moe.ffn_q(dev["x"], ex, idx, gates, grouping=grp, mode="fast")
+    torch.cuda.synchronize()
+    idx_o, g_o = oracle.route(lay["logits"], cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_o)
+    ref = oracle_rows(lay, idx_o, g_o)
+    assert rel_l2_rows(y_to_f64(y), ref).max() <= TOL_FAST
+    ex.close()
+
+
+@pytest.mark.parametrize("layer", [0, 47])
+def test_prefill_8k_sampled_rows(layer):
+    """Full-size 8,192-token layer of the 48-layer stack; 256 sampled rows checked."""
+    lay, dev = make_layer(CONFIGS[3], seed=0, layer=layer), None
+    dev = upload(lay)
+    cfg = lay["cfg"]
+    idx, gates = oracle.route(lay["logits"], cfg.k)
+    rows = np.random.default_rng(layer).choice(cfg.T, 256, replace=False).astype(np.int32)
+    ref = oracle_rows(lay, idx, gates, rows=rows)
+    for mode, tol in (("fast", TOL_FAST), ("check", TOL_CHECK)):
+        log(f"[ffn] cfg3 layer {layer} mode={mode}")
+        y = run_ffn(lay, dev, idx, gates, mode, use_gpu_grouping=True)
+        err = rel_l2_rows(y[rows], ref)
+        log(f"[ffn] cfg3 layer {layer} {mode}: max rel-L2 {err.max():.3e}")
+        assert err.max() <= tol
+
+
+def test_group_size_invariance():
+    """A token evaluated alone and inside its verify window agree within tolerance."""
+    lay, dev = layer_for(1)
+    cfg = lay["cfg"]
+    idx, gates = oracle.route(lay["logits"], cfg.k)
+    full = run_ffn(lay, dev, idx, gates, "fast")
+    for t in range(cfg.T):
+        one = dict(lay, cfg=cfg.with_(T=1), x=lay["x"][t:t + 1], logits=lay["logits"][t:t + 1])
+        d1 = upload(one)
+        y1 = run_ffn(one, d1, idx[t:t + 1], gates[t:t + 1], "fast")
+        err = rel_l2_rows(y1, full[t:t + 1])[0]
+        log(f"[invariance] token {t}: rel-L2 alone vs batch {err:.2e} "
+            f"bitwise={'yes' if np.array_equal(y1, full[t:t + 1]) else 'no'}")
+        assert err <= TOL_FAST
+
+
+def test_edge_all_tokens_one_expert_and_k_equals_E():
+    cfg = CONFIGS[0].with_(T=200)
+    lay = make_layer(cfg, seed=4)
+    dev = upload(lay)
+    # every token picks expert 3 first (MFMA tiles, ragged tail of 200 = 3*64 + 8)
+    lg = lay["logits"].copy()
+    lg[:, 3] += 100.0
+    idx, gates = oracle.route(lg, cfg.k)
+    assert np.all(idx[:, 0] == 3)
+    for mode, tol in (("fast", TOL_FAST), ("check", TOL_CHECK)):
+        y = run_ffn(lay, dev, idx, gates, mode, use_gpu_grouping=True)
+        assert rel_l2_rows(y, oracle_rows(lay, idx, gates)).max() <= tol
+    # k = E: every expert holds every token
+    cfg16 = CONFIGS[0].with_(k=16)
+    lay16 = dict(make_layer(CONFIGS[0], seed=5), cfg=cfg16)
+    dev16 = upload(lay16)
+    idx, gates = oracle.route(lay16["logits"], 16)
+    for mode, tol in (("fast", TOL_FAST), ("check", TOL_CHECK)):
+        y = run_ffn(lay16, dev16, idx, gates, mode)
+        assert rel_l2_rows(y, oracle_rows(lay16, idx, gates)).max() <= tol
+
+
+def test_edge_zero_and_max_scales():
+    """d = 0 blocks (w = m), and all-3 codes with the largest generated scales."""
+    lay = make_layer(CONFIGS[0], seed=6)
+    dm = lay["dm"].reshape(lay["dm"].shape[0], -1, 2).copy()
+    dm[:, ::3, 0] = 0                        # every third block has d = 0
+    codes = lay["codes"].copy()
+    codes[:, 1::5] = 0xFF                    # some bytes hold the largest code
+    lay = dict(lay, dm=dm.reshape(lay["dm"].shape), codes=codes)
+    dev = upload(lay)
+    idx, gates = oracle.route(lay["logits"], CONFIGS[0].k)
+    for mode, tol in (("fast", TOL_FAST), ("check", TOL_CHECK)):
+        y = run_ffn(lay, dev, idx, gates, mode)
+        assert rel_l2_rows(y, oracle_rows(lay, idx, gates)).max() <= tol
+
+
+def test_edge_empty_batch():
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    lay, dev = layer_for(0)
+    cfg = lay["cfg"]
+    idx, gates = moe.route_topk(dev["logits"][:0], cfg.k)
+    assert idx.shape == (0, cfg.k)
+    ex = experts_of(lay, dev)
+    y = moe.ffn_q(dev["x"][:0], ex, idx, gates)
+    torch.cuda.synchronize()
+    assert y.shape == (0, cfg.H)
+    ex.close()
