@@ -1,0 +1,443 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer over 2-bit block-quantized experts (one MI355X).
+
+A step is one pass of the whole hot path over one batch: top-k routing, the
+grouping of assignments by expert, and the expert FFN with combine (dequant,
+gate/up, SwiGLU, down, gate-weighted sum, shared expert).
+
+Default run (prints ONE JSON line):
+  * decode: the 4-token verify-window layer (hidden 2048, 512 routed experts + 1
+    shared, top-10, intermediate 512, Q2). Steps rotate over --rotation distinct
+    seeded layer instances (each with its own weights and logits), so the touched
+    weights cannot stay in the 256 MB last-level cache between visits. Steps are
+    replayed from HIP graphs (one graph per pass over the rotation). `value`
+    is tokens/s.
+  * prefill: the 8,192-token chunk through the 48-layer stack (24,576 routed
+    experts, ~29 GB of Q2 planes resident in HBM); per-layer and end-to-end
+    tokens/s, reported under "prefill_8k".
+  * roofline: the dominant kernel of each regime, timed with HIP events around
+    its launches (an eager pass over the same steps), against MI355X peaks.
+  * cpu_baseline: the CPU oracle timed on a bounded sample of the decode steps.
+
+Inputs are synthetic and seeded (package ``synth``); nothing is read from disk.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS_F16 = 2500.0  # MI355X dense fp16/bf16 matrix peak, published
+
+SEPARATE_CALLS = False  # --separate-calls: moe_route_topk + moe_group instead of moe_route_group
+LAYER_CALL = True       # decode steps call moe_layer (--stage-calls: route_group + ffn_q)
+
+METRIC = "MoE-layer tokens/s (4-tok decode, 8K prefill); HBM GB/s and MFMA % of peak"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def expert_plane_bytes(cfg) -> dict:
+    """Bytes of one expert's gate+up planes and of its down planes."""
+    bits = 4 if cfg.qtype == 3 else 3   # code bits + 32 bits of (d, m) per 32 weights
+    mat = cfg.H * cfg.I * bits // 8
+    return {"gateup": 2 * mat, "down": mat}
+
+
+class LayerInstance:
+    """Device buffers and prebuilt C-ABI argument lists for one layer step."""
+
+    def __init__(self, cfg, host: dict, ws_bytes_fn):
+        import torch
+        import bit_quantized_moe_topk_amd as moe
+        self.cfg = cfg
+        dev = "cuda"
+        self.logits = torch.from_numpy(host["logits"]).to(dev)
+        x = torch.from_numpy(np.ascontiguousarray(host["x"]))
+        if host["x"].dtype == np.uint16:
+            x = x.view(torch.int16).view(torch.bfloat16)
+        self.x = x.to(dev)
+        self.codes = torch.from_numpy(host["codes"].reshape(-1)).to(dev)
+        self.dm = torch.from_numpy(host["dm"].reshape(-1).view(np.int16)).to(dev)
+        self.hi = None if host["hi"] is None else torch.from_numpy(host["hi"].reshape(-1)).to(dev)
+        self.ex = moe.Experts(cfg.qtype, cfg.E, bool(cfg.shared), cfg.H, cfg.I, self.codes,
+                              self.hi, self.dm)
+        T, k, E = cfg.T, cfg.k, cfg.E
+        A = T * (k + cfg.shared)
+        i32 = torch.int32
+        self.idx = torch.empty((T, k), dtype=i32, device=dev)
+        self.gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E + 1, dtype=i32, device=dev)
+        self.offsets = torch.empty(E + 2, dtype=i32, device=dev)
+        self.perm = torch.empty(A, dtype=i32, device=dev)
+        self.slot_of = torch.empty(A, dtype=i32, device=dev)
+        self.y = torch.empty((T, cfg.H), dtype=self.x.dtype, device=dev)
+
+    def bind(self, gws, fws, lws):
+        """Fix the argument tuples for the three C-ABI calls (shared workspaces)."""
+        P = lambda t: C.c_void_p(t.data_ptr())  # noqa: E731
+        cfg = self.cfg
+        xdt = 0 if self.x.dtype.is_floating_point and self.x.element_size() == 4 else 1
+        self.a_route = (P(self.logits), cfg.T, cfg.E, cfg.k, P(self.idx), P(self.gates))
+        self.a_route_group = (P(self.logits), cfg.T, cfg.E, cfg.k, cfg.shared, P(self.idx),
+                              P(self.gates), P(self.counts), P(self.offsets), P(self.perm),
+                              P(self.slot_of), P(gws) if gws is not None else None,
+                              0 if gws is None else gws.numel())
+        self.a_group = (P(self.idx), cfg.T, cfg.k, cfg.E, cfg.shared, P(self.counts),
+                        P(self.offsets), P(self.perm), P(self.slot_of),
+                        P(gws) if gws is not None else None, 0 if gws is None else gws.numel())
+        self.a_layer = (P(self.logits), P(self.x), xdt, cfg.T, self.ex.handle, cfg.k, P(self.idx),
+                        P(self.gates), P(self.y), 0, P(lws), lws.numel())
+        self.a_ffn = (P(self.x), xdt, cfg.T, self.ex.handle, P(self.idx), P(self.gates), cfg.k,
+                      P(self.counts), P(self.offsets), P(self.perm), P(self.slot_of), P(self.y),
+                      0, P(fws), fws.numel())
+
+    def step(self, L, stream) -> None:
+        if LAYER_CALL:
+            st = L.moe_layer(*self.a_layer, stream)
+            if st:
+                raise RuntimeError(f"moe_layer failed: {st}")
+            return
+        if SEPARATE_CALLS:
+            r = L.moe_route_topk(*self.a_route, stream)
+            g = L.moe_group(*self.a_group, stream)
+        else:
+            r = 0
+            g = L.moe_route_group(*self.a_route_group, stream)
+        f = L.moe_ffn_q(*self.a_ffn, stream)
+        if r or g or f:
+            raise RuntimeError(f"C-ABI call failed: route={r} group={g} ffn={f}")
+
+
+def build_instances(cfg, n: int, seed: int, keep_host: int = 0):
+    import torch
+    import bit_quantized_moe_topk_amd as moe
+    from synth import make_layer
+    insts, hosts = [], []
+    t0 = time.time()
+    for i in range(n):
+        host = make_layer(cfg, seed=seed, layer=i, threads=16)
+        insts.append(LayerInstance(cfg, host, None))
+        if i < keep_host:
+            hosts.append(host)
+        del host
+    torch.cuda.synchronize()
+    log(f"{cfg.name}: generated and uploaded {n} layer instances in {time.time() - t0:.1f}s")
+    L = moe.lib()
+    gws_n = L.moe_group_workspace_size(cfg.T, cfg.k, cfg.E)
+    gws = torch.empty(gws_n, dtype=torch.uint8, device="cuda") if gws_n else None
+    fws_n = insts[0].ex.workspace_size(cfg.T, cfg.k, 0)
+    fws = torch.empty(fws_n, dtype=torch.uint8, device="cuda")
+    lws_n = L.moe_layer_workspace_size(insts[0].ex.handle, cfg.T, cfg.k, 0)
+    lws = torch.empty(lws_n, dtype=torch.uint8, device="cuda")
+    for it in insts:
+        it.bind(gws, fws, lws)
+    return insts, hosts, (gws, fws, lws)
+
+
+def routing_stats(insts) -> list:
+    """Per instance (from the idx the step wrote): experts on the GEMV path
+    (1..4 assignments), on the MFMA path, and the assignments on the MFMA path."""
+    out = []
+    for it in insts:
+        cfg = it.cfg
+        c = np.bincount(it.idx.cpu().numpy().reshape(-1), minlength=cfg.E).astype(np.int64)
+        if cfg.shared:
+            c = np.append(c, cfg.T)
+        gemv = int(((c >= 1) & (c <= 4)).sum())
+        mf = c > 4
+        out.append({"gemv_experts": gemv, "mfma_experts": int(mf.sum()),
+                    "mfma_assignments": int(c[mf].sum()), "touched": int((c > 0).sum())})
+    return out
+
+
+def gpu_hold(ms: float) -> None:
+    """Keep the GPU busy for about `ms` so that launches queued meanwhile run
+    back to back (their HIP events then time the GPU, not the host)."""
+    import torch
+    torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
+
+
+def kernel_profile(insts, L, stream, steps: int, chunk: int = 32) -> dict:
+    import torch
+    import bit_quantized_moe_topk_amd as moe
+    torch.cuda.synchronize()
+    moe.profile_begin(64 * steps + 64)
+    for c0 in range(0, steps, chunk):
+        gpu_hold(25.0)
+        for s in range(c0, min(steps, c0 + chunk)):
+            insts[s % len(insts)].step(L, stream)
+    torch.cuda.synchronize()
+    return moe.profile_end()
+
+
+def run_decode(cfg, args):
+    import torch
+    import bit_quantized_moe_topk_amd as moe
+    L = moe.lib()
+    insts, hosts, keep = build_instances(cfg, args.rotation, args.seed, keep_host=args.cpu_layers)
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for s in range(max(args.warmup, len(insts))):   # every instance runs once untimed
+        insts[s % len(insts)].step(L, stream)
+    torch.cuda.synchronize()
+    stats = routing_stats(insts)
+
+    K = args.steps
+    n = len(insts)
+    graphs = None
+    if not args.eager:
+        # one graph holds a full pass over the rotation; a second one the first
+        # K mod n steps, so exactly K steps run in the timed region
+        def capture(count):
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    cur = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+                    for s in range(count):
+                        insts[s].step(L, cur)
+            torch.cuda.current_stream().wait_stream(side)
+            return g
+        graphs = (capture(n), capture(K % n) if K % n else None)
+        for g in graphs:
+            if g is not None:
+                g.replay()
+        torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    if graphs is not None:
+        for _ in range(K // n):
+            graphs[0].replay()
+        if graphs[1] is not None:
+            graphs[1].replay()
+    else:
+        for s in range(K):
+            insts[s % n].step(L, stream)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / K
+
+    # eager pass with HIP events around every launch: per-kernel durations
+    prof = kernel_profile(insts, L, stream, K)
+    pb = expert_plane_bytes(cfg)
+    step_layers = [stats[s % len(insts)] for s in range(K)]
+    kname = max((k for k in prof if k in ("win_gateup", "gemv_gateup", "win_down", "gemv_down")),
+                key=lambda k: prof[k][1])
+    unit = pb["gateup"] if "gateup" in kname else pb["down"]
+    per_step_units = [st["touched"] if kname.startswith("win") else st["gemv_experts"]
+                      for st in step_layers]
+    k_bytes = sum(per_step_units) * unit
+    n_k, k_ms = prof[kname]
+    touched_bytes = np.mean([st["touched"] for st in stats]) * (pb["gateup"] + pb["down"])
+    kernels_us = {k: round(1e3 * v[1] / max(v[0], 1), 2) for k, v in prof.items()}
+    res = {
+        "tokens_per_s": cfg.T / (ms_per_step / 1e3),
+        "ms_per_step": ms_per_step,
+        "graph": graphs is not None,
+        "kernels_us": kernels_us,
+        "touched_experts_mean": float(np.mean([st["touched"] for st in stats])),
+        "gemv_experts_mean": float(np.mean([st["gemv_experts"] for st in stats])),
+        "layer_weight_bytes_mean": float(touched_bytes),
+        "layer_hbm_gbs": float(touched_bytes / (ms_per_step * 1e-3) / 1e9),
+        "roofline": {
+            "kernel": kname,
+            "bound": "hbm",
+            "achieved": round(k_bytes / (k_ms * 1e-3) / 1e9, 1) if k_ms else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(k_bytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if k_ms else None,
+            "traffic": None,
+            "launches": n_k,
+            "avg_us": round(1e3 * k_ms / max(n_k, 1), 2),
+            "bytes_per_launch": round(k_bytes / max(n_k, 1)),
+            "unit_bytes": unit,
+        },
+    }
+    del graphs
+    return res, hosts, insts
+
+
+def run_prefill(cfg, args):
+    import torch
+    import bit_quantized_moe_topk_amd as moe
+    L = moe.lib()
+    n_layers = args.prefill_layers or cfg.layers
+    insts, _, keep = build_instances(cfg, n_layers, args.seed)
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for it in insts:           # warm-up: the whole stack once
+        it.step(L, stream)
+    torch.cuda.synchronize()
+    stats = routing_stats(insts)
+    K = args.prefill_steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(K):
+        for it in insts:
+            it.step(L, stream)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_stack = ev0.elapsed_time(ev1) / K
+    prof = kernel_profile(insts, L, stream, len(insts))
+    n_gu, gu_ms = prof.get("mfma_gateup", (0, 0.0))
+    flops_gu = sum(2.0 * 2 * cfg.I * cfg.H * st["mfma_assignments"] for st in stats)
+    total_flops = sum(2.0 * 3 * cfg.I * cfg.H * cfg.A for _ in stats)
+    ms_layer = ms_stack / n_layers
+    res = {
+        "workload": f"prefill: {cfg.T}-token chunk through {n_layers} stacked MoE layers "
+                    f"(hidden {cfg.H}, {cfg.E} routed + {cfg.shared} shared experts, top-{cfg.k}, "
+                    f"intermediate {cfg.I}, Q{cfg.qtype}, bf16 activations)",
+        "layers": n_layers,
+        "ms_per_chunk": ms_stack,
+        "ms_per_layer": ms_layer,
+        "tokens_per_s_end_to_end": cfg.T / (ms_stack * 1e-3),
+        "tokens_per_s_per_layer": cfg.T / (ms_layer * 1e-3),
+        "layer_tflops": total_flops / len(stats) / (ms_layer * 1e-3) / 1e12,
+        "kernels_us": {k: round(1e3 * v[1] / max(v[0], 1), 1) for k, v in prof.items()},
+        "roofline": {
+            "kernel": "mfma_gateup",
+            "bound": "mfma",
+            "achieved": round(flops_gu / (gu_ms * 1e-3) / 1e12, 2) if gu_ms else None,
+            "peak": MFMA_PEAK_TFLOPS_F16,
+            "unit": "TFLOP/s",
+            "frac": round(flops_gu / (gu_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS_F16, 4) if gu_ms else None,
+            "traffic": None,
+            "launches": n_gu,
+            "avg_us": round(1e3 * gu_ms / max(n_gu, 1), 1),
+            "flops_per_launch": flops_gu / max(n_gu, 1),
+        },
+    }
+    for it in insts:
+        it.ex.close()
+    del insts, keep
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, hosts, args):
+    """The CPU oracle (fp32 build, OpenMP over tokens) on a bounded decode sample."""
+    import oracle
+    threads = max(1, min(os.cpu_count() or 1, cfg.T))
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        host = hosts[steps % len(hosts)]
+        idx, gates = oracle.route(host["logits"], cfg.k)
+        oracle.group(idx, cfg.E, bool(cfg.shared))
+        oracle.layer_rows(host, idx, gates, prec="f32", threads=threads)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or steps >= 1000:
+            break
+    return {"value": round(steps * cfg.T / el, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} full decode layer steps ({cfg.T} tokens each) over "
+                      f"{len(hosts)} seeded layer instances, fp32 oracle, {el:.1f}s wall; "
+                      f"host has {os.cpu_count()} logical CPUs, the oracle parallelises "
+                      f"over the {cfg.T} tokens only"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--rotation", type=int, default=32,
+                    help="distinct decode layer instances the steps cycle through")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="route and group with two calls instead of moe_route_group")
+    ap.add_argument("--stage-calls", action="store_true",
+                    help="decode steps call route_group + ffn_q instead of moe_layer")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-layers", type=int, default=0, help="0 = all 48")
+    ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-layers", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    global SEPARATE_CALLS, LAYER_CALL
+    SEPARATE_CALLS = args.separate_calls
+    LAYER_CALL = not (args.stage_calls or args.separate_calls)
+    import torch
+    import bit_quantized_moe_topk_amd as moe
+    from synth import CONFIGS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    moe.lib()
+    cfg = CONFIGS[1]
+    dec, hosts, insts = run_decode(cfg, args)
+    log(f"decode: {dec['tokens_per_s']:.0f} tokens/s, {dec['ms_per_step'] * 1e3:.1f} us/step, "
+        f"gemv_gateup {dec['roofline']['achieved']} GB/s")
+    for it in insts:
+        it.ex.close()
+    del insts
+    torch.cuda.empty_cache()
+
+    pre = None
+    if not args.no_prefill:
+        pre = run_prefill(CONFIGS[3], args)
+        log(f"prefill: {pre['tokens_per_s_end_to_end']:.0f} tokens/s end to end, "
+            f"{pre['ms_per_layer']:.3f} ms/layer, mfma_gateup {pre['roofline']['achieved']} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline and hosts:
+        cpu = cpu_baseline(cfg, hosts, args)
+        log(f"cpu oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
+
+    rf = dict(dec["roofline"])
+    line = {
+        "metric": METRIC,
+        "value": round(dec["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode: one MoE layer step over a {cfg.T}-token verify window "
+                        f"(hidden {cfg.H}, {cfg.E} routed + {cfg.shared} shared experts, "
+                        f"top-{cfg.k}, intermediate {cfg.I}, Q{cfg.qtype} weights, bf16 "
+                        f"activations); steps rotate over {args.rotation} seeded layer instances",
+            "tokens_per_step": cfg.T,
+            "launch": "hip graph over the layer rotation" if dec["graph"] else "eager",
+        },
+        "roofline": rf,
+        "cpu_baseline": cpu,
+        "decode_detail": {k: v for k, v in dec.items() if k not in ("roofline",)},
+        "prefill_8k": pre,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

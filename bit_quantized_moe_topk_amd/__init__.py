@@ -55,6 +55,8 @@ def lib() -> C.CDLL:
         L.moe_group_workspace_size.restype = sz
         L.moe_group.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
         L.moe_group.restype = C.c_int
+        L.moe_route_group.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
+        L.moe_route_group.restype = C.c_int
         L.moe_experts_create.argtypes = [C.POINTER(P), i32, i32, i32, i32, i32, P, P, P]
         L.moe_experts_create.restype = C.c_int
         L.moe_experts_destroy.argtypes = [P]
@@ -63,8 +65,38 @@ def lib() -> C.CDLL:
         L.moe_ffn_q_workspace_size.restype = sz
         L.moe_ffn_q.argtypes = [P, i32, i32, P, P, P, i32, P, P, P, P, P, i32, P, sz, P]
         L.moe_ffn_q.restype = C.c_int
+        L.moe_layer_workspace_size.argtypes = [P, i32, i32, i32]
+        L.moe_layer_workspace_size.restype = sz
+        L.moe_layer.argtypes = [P, P, i32, i32, P, i32, P, P, P, i32, P, sz, P]
+        L.moe_layer.restype = C.c_int
+        L.moe_profile_begin.argtypes = [i32]
+        L.moe_profile_begin.restype = C.c_int
+        L.moe_profile_end.argtypes = []
+        L.moe_profile_end.restype = C.c_int
+        L.moe_profile_count.argtypes = []
+        L.moe_profile_count.restype = i32
+        L.moe_profile_get.argtypes = [i32, C.POINTER(C.c_char_p), C.POINTER(i32),
+                                      C.POINTER(C.c_double)]
+        L.moe_profile_get.restype = C.c_int
         _lib = L
     return _lib
+
+
+def profile_begin(max_launches: int = 65536) -> None:
+    """Record HIP events around every library launch from now on."""
+    _check("moe_profile_begin", lib().moe_profile_begin(max_launches))
+
+
+def profile_end() -> dict:
+    """Stop recording; return {kernel name: (launches, total ms)}."""
+    L = lib()
+    _check("moe_profile_end", L.moe_profile_end())
+    out = {}
+    for i in range(L.moe_profile_count()):
+        name, n, ms = C.c_char_p(), C.c_int32(), C.c_double()
+        _check("moe_profile_get", L.moe_profile_get(i, C.byref(name), C.byref(n), C.byref(ms)))
+        out[name.value.decode()] = (n.value, ms.value)
+    return out
 
 
 def status_string(status: int) -> str:
@@ -130,6 +162,28 @@ def group(idx: torch.Tensor, E: int, has_shared: bool) -> Grouping:
     g.perm = g.perm[:A]
     g.slot_of = g.slot_of[:A]
     return g
+
+
+def route_group(logits: torch.Tensor, k: int, has_shared: bool):
+    """Top-k routing and the grouping in one call: (idx, gates, Grouping)."""
+    _need_cuda("logits", logits, torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    A = T * (k + int(bool(has_shared)))
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    g = Grouping(torch.empty(E + 1, dtype=torch.int32, device=dev),
+                 torch.empty(E + 2, dtype=torch.int32, device=dev),
+                 torch.empty(max(A, 1), dtype=torch.int32, device=dev),
+                 torch.empty(max(A, 1), dtype=torch.int32, device=dev))
+    nbytes = lib().moe_group_workspace_size(T, k, E)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check("moe_route_group", lib().moe_route_group(
+        _ptr(logits), T, E, k, int(bool(has_shared)), _ptr(idx), _ptr(gates), _ptr(g.counts),
+        _ptr(g.offsets), _ptr(g.perm), _ptr(g.slot_of), _ptr(ws), nbytes, _stream()))
+    g.perm = g.perm[:A]
+    g.slot_of = g.slot_of[:A]
+    return idx, gates, g
 
 
 class Experts:
@@ -209,5 +263,29 @@ def ffn_q(x: torch.Tensor, ex: Experts, idx: torch.Tensor, gates: torch.Tensor,
     return y
 
 
-__all__ = ["route_topk", "group", "Grouping", "Experts", "ffn_q", "lib", "status_string",
+def layer(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fast",
+          workspace: torch.Tensor | None = None):
+    """The whole layer (route, group, expert FFN, combine): returns (idx, gates, y)."""
+    mode = _MODES[mode]
+    _need_cuda("logits", logits, torch.float32)
+    _need_cuda("x", x, (torch.float32, torch.bfloat16))
+    T, H = x.shape
+    if H != ex.H or logits.shape[0] != T:
+        raise ValueError("shape mismatch between logits, x and the experts")
+    dev = x.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ydtype = torch.float32 if mode == CHECK_F32 else x.dtype
+    y = torch.empty((T, H), dtype=ydtype, device=dev)
+    nbytes = int(lib().moe_layer_workspace_size(ex.handle, T, k, mode))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    xdt = F32 if x.dtype == torch.float32 else BF16
+    _check("moe_layer", lib().moe_layer(_ptr(logits), _ptr(x), xdt, T, ex.handle, k, _ptr(idx),
+                                        _ptr(gates), _ptr(y), mode, _ptr(workspace),
+                                        workspace.numel(), _stream()))
+    return idx, gates, y
+
+
+__all__ = ["layer", "profile_begin", "profile_end", "route_topk", "route_group", "group", "Grouping", "Experts", "ffn_q", "lib", "status_string",
            "MoeError", "Q2", "Q3", "F32", "BF16", "FAST", "CHECK_F32", "MAX_E", "LIB_PATH"]

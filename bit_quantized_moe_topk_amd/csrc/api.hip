@@ -5,10 +5,6 @@
 #include "../../include/moe.h"
 #include "common.h"
 
-namespace moe {
-bool gemv_supported(int H, int I);
-}
-
 using moe::Experts;
 
 struct moe_experts {
@@ -25,8 +21,12 @@ inline int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_H
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Byte layout of the moe_ffn_q workspace.
+//   grouping (used when the caller passes none) | h [A][I] | o [A][H]
+// h: fp32 in check mode, 16-bit in fast mode. o: gate-scaled expert outputs
+// per assignment, fp32 in check mode and for few tokens, bf16 otherwise.
 struct FfnLayout {
-  size_t counts, offsets, perm, slot_of, group, sched, h, o, total;
+  size_t counts, offsets, perm, slot_of, group, h, o, total;
+  bool o_f32;
 };
 
 FfnLayout ffn_layout(const Experts& ex, int T, int k, int mode) {
@@ -38,9 +38,9 @@ FfnLayout ffn_layout(const Experts& ex, int T, int k, int mode) {
   L.perm = off;    off = align_up(off + sizeof(int32_t) * A);
   L.slot_of = off; off = align_up(off + sizeof(int32_t) * A);
   L.group = off;   off = align_up(off + moe::group_scratch_bytes(T, k, ex.E));
-  L.sched = off;   off = align_up(off + sizeof(int32_t) * moe::sched_words(ex.E_tot, (int)A));
   L.h = off;       off = align_up(off + (mode == MOE_CHECK_F32 ? 4 : 2) * A * (size_t)ex.I);
-  L.o = off;       off = align_up(off + sizeof(float) * A * (size_t)ex.H);
+  L.o_f32 = mode == MOE_CHECK_F32 || T <= moe::kF32SlotMaxTokens;
+  L.o = off;       off = align_up(off + (L.o_f32 ? 4 : 2) * A * (size_t)ex.H);
   L.total = off;
   return L;
 }
@@ -89,6 +89,25 @@ int moe_group(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t has_s
   if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE;
   return status_of(moe::launch_group(idx, T, k, E, has_shared, counts, offsets, perm, slot_of, ws,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int moe_route_group(const float* logits, int32_t T, int32_t E, int32_t k, int32_t has_shared,
+                    int32_t* idx, float* gates, int32_t* counts, int32_t* offsets, int32_t* perm,
+                    int32_t* slot_of, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || (has_shared != 0 && has_shared != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_E) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * E > 0x7FFFFFFFLL || (long long)T * (k + has_shared) > 0x7FFFFFFFLL)
+    return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !idx || !gates || !perm || !slot_of)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::group_scratch_bytes(T, k, E);
+  if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) return status_of(moe::launch_group(idx, T, k, E, has_shared, counts, offsets, perm,
+                                                 slot_of, ws, s));
+  return status_of(moe::launch_route_group(logits, T, E, k, has_shared, idx, gates, counts, offsets,
+                                           perm, slot_of, ws, s));
 }
 
 int moe_experts_create(moe_experts** out, int32_t qtype, int32_t E, int32_t has_shared, int32_t H,
@@ -154,9 +173,7 @@ int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, c
   a.idx = idx;
   a.gates = gates;
   a.y = y;
-  a.sched = reinterpret_cast<int*>(at(ws, L.sched));
   a.h = at(ws, L.h);
-  a.o = reinterpret_cast<float*>(at(ws, L.o));
   if (given == 4) {
     a.counts = counts;
     a.offsets = offsets;
@@ -174,18 +191,82 @@ int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, c
     a.perm = p;
     a.slot_of = so;
   }
+  a.out_f32 = mode == MOE_CHECK_F32 || xdtype == MOE_F32;
+  if (L.o_f32) a.o = reinterpret_cast<float*>(at(ws, L.o));
+  else a.ob = reinterpret_cast<uint16_t*>(at(ws, L.o));
   hipError_t e;
   if (mode == MOE_CHECK_F32) {
-    e = moe::launch_sched(d, a, 0, s);
-    if (e == hipSuccess) e = moe::launch_ffn_check(d, a, s);
-    if (e == hipSuccess) e = moe::launch_combine(d, a, 1, s);
+    e = moe::launch_ffn_check(d, a, s);
   } else {
-    const int gemv_max = moe::gemv_supported(d.H, d.I) ? moe::kGemvMaxTokens : 0;
-    e = moe::launch_sched(d, a, gemv_max, s);
-    if (e == hipSuccess) e = moe::launch_ffn_fast(d, a, s);
-    if (e == hipSuccess) e = moe::launch_combine(d, a, xdtype == MOE_F32, s);
+    a.gmax = moe::gemv_supported(d.H, d.I) ? moe::kGemvMaxTokens : 0;
+    e = moe::launch_ffn_fast(d, a, s);
   }
+  if (e == hipSuccess) e = moe::launch_combine(d, a, s);
   return status_of(e);
+}
+
+// ---- whole layer -----------------------------------------------------------
+
+namespace {
+struct LayerLayout {
+  bool window;
+  size_t counts, offsets, perm, slot_of, group, ffn, total;
+};
+
+LayerLayout layer_layout(const Experts& d, int T, int k, int mode) {
+  LayerLayout L{};
+  L.window = mode == MOE_FAST && moe::window_supported(d, T, k);
+  if (L.window) {
+    L.total = align_up(moe::window_workspace_bytes(d, T, k));
+    return L;
+  }
+  const size_t A = (size_t)T * (k + d.has_shared);
+  size_t off = 0;
+  L.counts = off;  off = align_up(off + sizeof(int32_t) * (d.E + 1));
+  L.offsets = off; off = align_up(off + sizeof(int32_t) * (d.E + 2));
+  L.perm = off;    off = align_up(off + sizeof(int32_t) * (A ? A : 1));
+  L.slot_of = off; off = align_up(off + sizeof(int32_t) * (A ? A : 1));
+  L.group = off;   off = align_up(off + moe::group_scratch_bytes(T, k, d.E));
+  L.ffn = off;     off = align_up(off + ffn_layout(d, T, k, mode).total);
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t moe_layer_workspace_size(const moe_experts* ex, int32_t T, int32_t k, int32_t mode) {
+  if (!ex || T < 0 || k < 1 || k > ex->d.E) return 0;
+  if (mode != MOE_FAST && mode != MOE_CHECK_F32) return 0;
+  return layer_layout(ex->d, T, k, mode).total;
+}
+
+int moe_layer(const float* logits, const void* x, int32_t xdtype, int32_t T, const moe_experts* ex,
+              int32_t k, int32_t* idx, float* gates, void* y, int32_t mode, void* ws, size_t ws_bytes,
+              void* stream) {
+  if (!ex || T < 0 || k < 1 || k > ex->d.E) return MOE_ERR_INVALID_ARG;
+  if (xdtype != MOE_F32 && xdtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_FAST && mode != MOE_CHECK_F32) return MOE_ERR_INVALID_ARG;
+  const Experts& d = ex->d;
+  const long long A = (long long)T * (k + d.has_shared);
+  if ((long long)T * d.E > 0x7FFFFFFFLL || A > 0x7FFFFFFFLL || A * d.H > (1LL << 40))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !x || !idx || !gates || !y || !aligned16(x) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  const LayerLayout L = layer_layout(d, T, k, mode);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L.window)
+    return status_of(moe::launch_window(logits, T, k, d, x, xdtype, idx, gates, y,
+                                        xdtype == MOE_F32, ws, s));
+  int32_t* c = reinterpret_cast<int32_t*>(at(ws, L.counts));
+  int32_t* o = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+  int32_t* p = reinterpret_cast<int32_t*>(at(ws, L.perm));
+  int32_t* so = reinterpret_cast<int32_t*>(at(ws, L.slot_of));
+  int st = moe_route_group(logits, T, d.E, k, d.has_shared, idx, gates, c, o, p, so,
+                           at(ws, L.group), moe::group_scratch_bytes(T, k, d.E), stream);
+  if (st != MOE_OK) return st;
+  return moe_ffn_q(x, xdtype, T, ex, idx, gates, k, c, o, p, so, y, mode, at(ws, L.ffn),
+                   ws_bytes - L.ffn, stream);
 }
 
 }  // extern "C"

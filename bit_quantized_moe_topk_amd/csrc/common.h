@@ -8,6 +8,8 @@
 
 namespace moe {
 
+constexpr int MOE_MAX_E_DEV = 2048;  // routed experts per layer (MOE_MAX_E)
+
 // Description of one layer's packed experts (device pointers, shapes).
 struct Experts {
   int qtype;      // 2 or 3
@@ -34,24 +36,23 @@ __host__ __device__ inline size_t blk_down(const Experts& x, int e) {
 // Experts with 1..kGemvMaxTokens assignments take the GEMV kernels (weights
 // streamed once, codes kept exact); the rest take the MFMA tile kernels.
 constexpr int kGemvMaxTokens = 4;
-constexpr int kTileM = 64;  // tokens per MFMA tile
-
-// Layout of the scheduling area inside the FFN workspace (int32 words).
-//   [0] number of GEMV experts   [1] number of MFMA token tiles
-//   [8 .. 8+E_tot)               GEMV expert list
-//   [8+E_tot .. )                MFMA tile list: (expert << 16 | tile index)
-struct SchedView {
-  int* hdr;
-  int* gemv;
-  int* tiles;
-};
-inline size_t sched_words(int E_tot, int A) { return 8 + (size_t)E_tot + (size_t)A / kTileM + E_tot + 1; }
-__host__ __device__ inline SchedView sched_view(int* base, int E_tot) {
-  return SchedView{base, base + 8, base + 8 + E_tot};
-}
+constexpr int kTileM = 64;  // assignments per MFMA tile
+// Up to this many tokens the per-assignment expert outputs are kept in fp32;
+// above it in bf16 (half the traffic of the combine).
+constexpr int kF32SlotMaxTokens = 256;
 
 // fp16 bit pattern -> float (exact; v_cvt_f32_f16).
 __device__ inline float half_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// Launch profiling hooks (no-ops unless a caller enabled moe_profile_begin).
+void prof_open(const char* name, hipStream_t s);
+void prof_close(hipStream_t s);
+#define MOE_LAUNCH(NAME, STREAM, ...)      \
+  do {                                     \
+    ::moe::prof_open(NAME, STREAM);        \
+    hipLaunchKernelGGL(__VA_ARGS__);       \
+    ::moe::prof_close(STREAM);             \
+  } while (0)
 
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----------
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* gates,
@@ -61,6 +62,9 @@ size_t group_scratch_bytes(int T, int k, int E);
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared, int32_t* counts,
                         int32_t* offsets, int32_t* perm, int32_t* slot_of, void* scratch,
                         hipStream_t s);
+hipError_t launch_route_group(const float* logits, int T, int E, int k, int has_shared, int32_t* idx,
+                              float* gates, int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* slot_of, void* scratch, hipStream_t s);
 
 // FFN: check mode (fp32) and fast mode; both read a grouping and write y.
 struct FfnArgs {
@@ -74,13 +78,21 @@ struct FfnArgs {
   const int32_t* perm;
   const int32_t* slot_of;
   void* y;
-  int* sched;  // scheduling area
-  void* h;     // [A][I] intermediate
-  float* o;    // [A][H] gate-scaled expert outputs
+  int out_f32;     // y is float32
+  int gmax;        // GEMV token limit (0: every expert takes the MFMA tiles)
+  void* h;         // [A][I] intermediate (fp32 check; bf16 GEMV / fp16 MFMA rows fast)
+  float* o;        // [A][H] fp32 gate-scaled expert outputs (check mode; fast, few tokens)
+  uint16_t* ob;    // [A][H] bf16 gate-scaled expert outputs (fast, many tokens)
 };
-hipError_t launch_sched(const Experts& ex, const FfnArgs& a, int gemv_max_tokens, hipStream_t s);
 hipError_t launch_ffn_check(const Experts& ex, const FfnArgs& a, hipStream_t s);
+bool gemv_supported(int H, int I);
+// The two-kernel whole-layer path for a decode verify window (T <= 4).
+bool window_supported(const Experts& ex, int T, int k);
+size_t window_workspace_bytes(const Experts& ex, int T, int k);
+hipError_t launch_window(const float* logits, int T, int k, const Experts& ex, const void* x,
+                         int xdtype, int32_t* idx, float* gates, void* y, int out_f32, void* ws,
+                         hipStream_t s);
 hipError_t launch_ffn_fast(const Experts& ex, const FfnArgs& a, hipStream_t s);
-hipError_t launch_combine(const Experts& ex, const FfnArgs& a, int out_f32, hipStream_t s);
+hipError_t launch_combine(const Experts& ex, const FfnArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -6,6 +6,7 @@
 // Expert = gate, up and down rows ("Strata - the details", "Low-RAM mode
 // without experts.bin"); h = silu(gate . x) * (up . x); o = down . h.
 #include "common.h"
+#include "sched.h"
 
 namespace moe {
 namespace {
@@ -34,24 +35,26 @@ __device__ inline float load_x(const void* x, int xdtype, size_t i) {
 // Tile: kTileM assignments of one expert x kCkRows rows of gate and of up.
 // Thread: token lane tm = tid / 4 (0..63), rows rq*8 .. rq*8+7 (rq = tid % 4).
 __global__ __launch_bounds__(kThreads) void ck_gateup(Experts ex, FfnArgs a) {
+  __shared__ WorkMap wm;
+  workmap_init(wm, a.counts, ex.E_tot, 0);
   __shared__ float xs[kTileM][33];
   __shared__ float wg[kCkRows][33];
   __shared__ float wu[kCkRows][33];
-  const SchedView sv = sched_view(a.sched, ex.E_tot);
-  const int n_tiles = sv.hdr[1];
   const int n_rt = ex.I / kCkRows;
   const int tid = threadIdx.x;
   const int tm = tid >> 2, rq = tid & 3;
   float* h = static_cast<float*>(a.h);
-  for (int item = blockIdx.x; item < n_tiles * n_rt; item += gridDim.x) {
-    const int tile = sv.tiles[item / n_rt];
+  for (int item = blockIdx.x; item < wm.n_tiles * n_rt; item += gridDim.x) {
+    int tl;
+    const int e = workmap_tile(wm, ex.E_tot, item / n_rt, tl);
     const int r0 = (item % n_rt) * kCkRows;
-    const int e = tile >> 16, m0 = (tile & 0xFFFF) * kTileM;
+    const int m0 = tl * kTileM;
     const int M = a.counts[e] - m0;  // assignments left in this expert
     const int slot0 = a.offsets[e] + m0;
     // token of each of the tile's rows (loaded cooperatively below)
     const int my_slot = slot0 + tm;
-    const int my_tok = tm < M ? token_of(a.perm[my_slot], a.T, a.k) : -1;
+    int my_tok = tm < M ? token_of(a.perm[my_slot], a.T, a.k) : -1;
+    if ((unsigned)my_tok >= (unsigned)a.T) my_tok = -1;
     float g[8], u[8];
     for (int i = 0; i < 8; ++i) g[i] = u[i] = 0.f;
     for (int kb = 0; kb < ex.H / 32; ++kb) {
@@ -93,18 +96,19 @@ __global__ __launch_bounds__(kThreads) void ck_gateup(Experts ex, FfnArgs a) {
 
 // Tile: kTileM assignments x kCkRows output rows of down; K = I.
 __global__ __launch_bounds__(kThreads) void ck_down(Experts ex, FfnArgs a) {
+  __shared__ WorkMap wm;
+  workmap_init(wm, a.counts, ex.E_tot, 0);
   __shared__ float hs[kTileM][33];
   __shared__ float wd[kCkRows][33];
-  const SchedView sv = sched_view(a.sched, ex.E_tot);
-  const int n_tiles = sv.hdr[1];
   const int n_rt = ex.H / kCkRows;
   const int tid = threadIdx.x;
   const int tm = tid >> 2, rq = tid & 3;
   const float* h = static_cast<const float*>(a.h);
-  for (int item = blockIdx.x; item < n_tiles * n_rt; item += gridDim.x) {
-    const int tile = sv.tiles[item / n_rt];
+  for (int item = blockIdx.x; item < wm.n_tiles * n_rt; item += gridDim.x) {
+    int tl;
+    const int e = workmap_tile(wm, ex.E_tot, item / n_rt, tl);
     const int r0 = (item % n_rt) * kCkRows;
-    const int e = tile >> 16, m0 = (tile & 0xFFFF) * kTileM;
+    const int m0 = tl * kTileM;
     const int M = a.counts[e] - m0;
     const int my_slot = a.offsets[e] + m0 + tm;
     float acc[8];
@@ -141,9 +145,9 @@ inline int grid_for(int max_items) { return max_items < 4096 ? (max_items > 0 ? 
 hipError_t launch_ffn_check(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   const int A = a.T * (a.k + ex.has_shared);
   const int max_tiles = A / kTileM + ex.E_tot + 1;
-  hipLaunchKernelGGL(ck_gateup, dim3(grid_for(max_tiles * (ex.I / kCkRows))), dim3(kThreads), 0, s,
+  MOE_LAUNCH("ck_gateup", s, ck_gateup, dim3(grid_for(max_tiles * (ex.I / kCkRows))), dim3(kThreads), 0, s,
                      ex, a);
-  hipLaunchKernelGGL(ck_down, dim3(grid_for(max_tiles * (ex.H / kCkRows))), dim3(kThreads), 0, s,
+  MOE_LAUNCH("ck_down", s, ck_down, dim3(grid_for(max_tiles * (ex.H / kCkRows))), dim3(kThreads), 0, s,
                      ex, a);
   return hipGetLastError();
 }

@@ -1,259 +1,214 @@
 // Fast mode of the expert FFN on gfx950.
 //
 // Decode shape (an expert holding 1..4 of the step's assignments): the layer is
-// bound by streaming the packed weights ("Strata - the details", section "Other
-// GPUs": the GPU share of the work scales with memory bandwidth). The GEMV
-// kernels read every touched weight once with coalesced loads and never expand
-// it: the 2-bit (or 3-bit) code becomes an exact bf16 value (128 + q) by
-// setting mantissa bits, v_dot2 multiplies code pairs by bf16 activation pairs
-// in fp32, and the block affine map is applied once per block and token:
-//     sum_k (d q_k + m) x_k = d * (sum_k (128 + q_k) x_k - 128 S) + m * S,
-// S = sum_k x_k over the block.
+// bound by streaming the packed weights ("Strata - the details", "Other GPUs":
+// speed scales with memory bandwidth). The GEMV kernels read every touched
+// weight once and never expand it. A 2-bit code c becomes the exact bf16 value
+// 128 + c*4^s by OR-ing it into the mantissa of 128 (s = the code's offset
+// inside its source field, 0..2), v_dot2 multiplies code pairs by bf16
+// activation pairs pre-scaled by 4^-s, and the block affine map is applied once
+// per block and token:
+//     sum_k (d q_k + m) x_k = d * (D - 128 X) + m * S,
+// D = sum of the dot2 terms, X = sum of the scaled activations, S = sum x.
+// (3-bit codes use s = 0 and OR in the third bit.) Every lane owns one 32-weight
+// block of a row; a wave issues all its block loads before computing, then
+// reduces its partial sums across the row's lanes in one batched transpose.
 //
 // Prefill shape (more assignments per expert): tiles of 64 assignments x 64
-// output rows run on v_mfma_f32_32x32x16_f16. Each K step dequantises a weight
-// tile to fp16 (w = d*q + m, one rounding) into LDS and gathers the tile's
-// activation rows (through the grouping permutation) into LDS as fp16; gate and
-// up tiles share the activation fragment and SwiGLU runs in the epilogue. The
-// pages' prompt path likewise multiplies quantised experts without expanding
-// them to FP16 in memory first ("Faster prompts").
+// output rows on v_mfma_f32_32x32x16_f16. Each K step dequantises a weight tile
+// to fp16 (w = d*q + m, one rounding) into LDS and gathers the tile's activation
+// rows through the grouping permutation into LDS as fp16. Gate and up share the
+// activation fragment and SwiGLU runs in the epilogue. The pages' prompt path
+// likewise multiplies quantised experts without first expanding them to FP16
+// ("Faster prompts").
 //
-// Lane layout of every kernel is stated where it is used.
+// Combine: the down kernels store gate * o per assignment slot (fp32 for few
+// tokens, bf16 for many) and the combine kernel sums each token's slots in a
+// fixed order. (A device-wide atomic sum was slower: same-address atomics from
+// all workgroups serialise, and the result would depend on their order.)
 #include "common.h"
+#include "gemv.h"
+#include "sched.h"
 
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float float16_t __attribute__((ext_vector_type(16)));
-
 constexpr int kThreads = 256;
-constexpr uint32_t kMagic = 0x43004300u;  // bf16 pair (128, 128)
 
-__device__ inline float half_lo(uint32_t v) { return half_bits_to_f32((uint16_t)(v & 0xFFFFu)); }
-__device__ inline float half_hi(uint32_t v) { return half_bits_to_f32((uint16_t)(v >> 16)); }
-__device__ inline float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
-
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-__device__ inline int token_of(int asg, int T, int k) { return asg < T * k ? asg / k : asg - T * k; }
-
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
-// ---------------------------------------------------------------------------
-// Activations of one 32-wide block as 16 bf16 pairs in code-pair order:
-// pair (w*8 + s) = (x[16w + s], x[16w + s + 8]), w in {0,1}, s in 0..7,
-// which is the order in which code pairs are extracted from a code word
-// (codes 16w+s and 16w+s+8 sit 16 bits apart). Also returns S = sum of x.
-struct XBlock {
-  uint32_t p[16];
-  float S;
-};
-
-// v[i] holds bf16 elements 2i (low half) and 2i+1 (high half), i < 16.
-__device__ inline void make_pairs(const uint32_t v[16], XBlock& xb) {
-  float S = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) S += bf16_lo(v[i]) + bf16_hi(v[i]);
-  xb.S = S;
-#pragma unroll
-  for (int w = 0; w < 2; ++w)
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint32_t a = v[8 * w + s / 2], b = v[8 * w + 4 + s / 2];
-      xb.p[8 * w + s] = (s & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-    }
-}
-
-__device__ inline void load_xblock_bf16(const uint16_t* src, XBlock& xb) {
-  uint32_t v[16];
-  const uint4* s4 = reinterpret_cast<const uint4*>(src);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 q = s4[i];
-    v[4 * i] = q.x;
-    v[4 * i + 1] = q.y;
-    v[4 * i + 2] = q.z;
-    v[4 * i + 3] = q.w;
+// Activation block of token slot m of an expert (zero past M).
+template <int Q, bool XF32>
+__device__ inline void load_token_xb(const Experts& ex, const FfnArgs& a, int slot0, int m, int M,
+                                     int b, XB& xb) {
+  if (m < M) {
+    int t = token_of(a.perm[slot0 + m], a.T, a.k);
+    t = (unsigned)t < (unsigned)a.T ? t : 0;
+    const size_t off = (size_t)t * ex.H + 32 * b;
+    if (XF32) load_xb_f32<Q>(static_cast<const float*>(a.x) + off, xb);
+    else load_xb_bf16<Q>(static_cast<const uint16_t*>(a.x) + off, xb);
+  } else {
+    zero_xb(xb);
   }
-  make_pairs(v, xb);
 }
 
-__device__ inline void load_xblock_f32(const float* src, XBlock& xb) {
-  uint32_t v[16];
-  const float4* s4 = reinterpret_cast<const float4*>(src);
+// Decode GEMV, gate + up + SwiGLU, one wave: PRW pair-rows of expert e from
+// pair-row prw0, for its MP >= M token slots. Lane l owns block (l % BPR) of
+// row (l / BPR) of each group of RPI = 64/BPR rows.
+template <int BPR, int MP, int Q, bool XF32>
+__device__ inline void gemv_gateup_wave(const Experts& ex, const FfnArgs& a, int e, int prw0, int M,
+                                        int slot0) {
+  constexpr int RPI = 64 / BPR;
+  constexpr int PRW = RPI > 4 ? RPI : 4;
+  constexpr int P = PRW / RPI;
+  constexpr int NV = 2 * P * MP;
+  const int lane = threadIdx.x & 63;
+  const int b = lane % BPR, rg = lane / BPR;
+  QBlock qg[P], qu[P];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 q = s4[i];
-    v[2 * i] = f32_to_bf16_bits(q.x) | (f32_to_bf16_bits(q.y) << 16);
-    v[2 * i + 1] = f32_to_bf16_bits(q.z) | (f32_to_bf16_bits(q.w) << 16);
+  for (int p = 0; p < P; ++p) {
+    const size_t row = (size_t)prw0 + p * RPI + rg;
+    qg[p] = load_qblock<Q>(ex, blk_gate(ex, e) + row * BPR + b);
+    qu[p] = load_qblock<Q>(ex, blk_up(ex, e) + row * BPR + b);
   }
-  make_pairs(v, xb);
-}
-
-// Packed block: 2 code words (+ the high-bit word for Q3) and the (d, m) word.
-struct QBlock {
-  uint32_t c0, c1, hi, dm;
-};
-
-template <int Q>
-__device__ inline QBlock load_qblock(const Experts& ex, size_t blk) {
-  QBlock b;
-  const uint2 c = *reinterpret_cast<const uint2*>(ex.codes + blk * 8);
-  b.c0 = c.x;
-  b.c1 = c.y;
-  b.dm = *reinterpret_cast<const uint32_t*>(ex.dm + blk * 2);
-  b.hi = Q == 3 ? *reinterpret_cast<const uint32_t*>(ex.hi + blk * 4) : 0u;
-  return b;
-}
-
-// sum_k q_k x_k + 128 S  (the chain starts at -128 S so the result is sum q x)
-template <int Q>
-__device__ inline float block_dot(const QBlock& b, const XBlock& xb) {
-  float D = -128.0f * xb.S;
+  XB xb[MP];
 #pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    const uint32_t cw = w ? b.c1 : b.c0;
-    uint32_t r2 = 0;
-    if (Q == 3) {
-      const uint32_t hw = b.hi >> (16 * w);
-      r2 = ((hw & 0xFFu) | ((hw & 0xFF00u) << 8)) << 2;  // code 16w+s -> bit s+2, +8 -> bit s+18
-    }
+  for (int i = 0; i < MP; ++i) load_token_xb<Q, XF32>(ex, a, slot0, i, M, b, xb[i]);
+  float v[NV];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      uint32_t pr = ((cw >> (2 * s)) & 0x00030003u) | kMagic;
-      if (Q == 3) pr |= (r2 >> s) & 0x00040004u;
-      D = dot2(pr, xb.p[8 * w + s], D);
+  for (int p = 0; p < P; ++p) {
+    float g[MP], u[MP];
+    block_values<Q, MP>(qg[p], xb, g);
+    block_values<Q, MP>(qu[p], xb, u);
+#pragma unroll
+    for (int i = 0; i < MP; ++i) {
+      v[2 * (p * MP + i)] = g[i];
+      v[2 * (p * MP + i) + 1] = u[i];
     }
   }
-  return D;
-}
-
-template <int Q>
-__device__ inline float block_term(const QBlock& b, const XBlock& xb) {
-  return half_lo(b.dm) * block_dot<Q>(b, xb) + half_hi(b.dm) * xb.S;
-}
-
-template <int W>
-__device__ inline float group_sum(float v) {
+  int jbase = 0;
+  LaneReduce<NV, BPR / 2>::run(v, lane, jbase);
+  uint16_t* h = static_cast<uint16_t*>(a.h);
+  if constexpr (NV > BPR) {
 #pragma unroll
-  for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+    for (int j = 0; j < NV / BPR; j += 2) {
+      const int pi = (jbase + j) >> 1, p = pi / MP, m = pi % MP;
+      if (m < M) {
+        const int row = prw0 + p * RPI + rg;
+        h[(size_t)(slot0 + m) * ex.I + row] = (uint16_t)f32_to_bf16_bits(silu_mul(v[j], v[j + 1]));
+      }
+    }
+  } else {
+    constexpr int OFF = BPR / NV;  // lane bit that holds the gate/up index bit
+    const float other = __shfl_xor(v[0], OFF, 64);
+    const int pi = jbase >> 1, p = pi / MP, m = pi % MP;
+    if ((jbase & 1) == 0 && (lane & (OFF - 1)) == 0 && m < M) {
+      const int row = prw0 + p * RPI + rg;
+      h[(size_t)(slot0 + m) * ex.I + row] = (uint16_t)f32_to_bf16_bits(silu_mul(v[0], other));
+    }
+  }
 }
 
-// ---------------------------------------------------------------------------
-// Decode GEMV, gate + up + SwiGLU.
-// Lane l works on block (l % BPR) of row (l / BPR) of a group of 64/BPR rows.
-// A workgroup takes RC consecutive rows of I for one expert; its 4 waves take
-// ROWS_W rows each, in PASSES passes of 64/BPR rows.
+template <int BPR>
+constexpr int gateup_rows() {
+  return 4 * (64 / BPR > 4 ? 64 / BPR : 4);
+}
+template <int BPR>
+constexpr int down_rows() {
+  return 4 * (64 / BPR > 16 ? 64 / BPR : 16);
+}
+
 template <int BPR, int Q, bool XF32>
 __global__ __launch_bounds__(kThreads) void gemv_gateup(Experts ex, FfnArgs a) {
-  constexpr int RPI = 64 / BPR;
-  constexpr int ROWS_W = RPI > 4 ? RPI : 4;
-  constexpr int PASSES = ROWS_W / RPI;
-  constexpr int RC = 4 * ROWS_W;
-  const SchedView sv = sched_view(a.sched, ex.E_tot);
-  const int n_items = sv.hdr[0] * (ex.I / RC);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int blk_in_row = lane % BPR, row_in_grp = lane / BPR;
-  uint16_t* h = static_cast<uint16_t*>(a.h);
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int e = sv.gemv[item / (ex.I / RC)];
-    const int r0 = (item % (ex.I / RC)) * RC + wave * ROWS_W;
-    const int M = a.counts[e];
-    const int slot0 = a.offsets[e];
-    XBlock xb[kGemvMaxTokens];
-#pragma unroll
-    for (int m = 0; m < kGemvMaxTokens; ++m) {
-      if (m < M) {
-        int t = token_of(a.perm[slot0 + m], a.T, a.k);
-        t = (unsigned)t < (unsigned)a.T ? t : 0;
-        const size_t off = (size_t)t * ex.H + 32 * blk_in_row;
-        if (XF32) load_xblock_f32(static_cast<const float*>(a.x) + off, xb[m]);
-        else load_xblock_bf16(static_cast<const uint16_t*>(a.x) + off, xb[m]);
-      }
-    }
-    QBlock qg[PASSES], qu[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = r0 + p * RPI + row_in_grp;
-      qg[p] = load_qblock<Q>(ex, blk_gate(ex, e) + (size_t)row * BPR + blk_in_row);
-      qu[p] = load_qblock<Q>(ex, blk_up(ex, e) + (size_t)row * BPR + blk_in_row);
-    }
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = r0 + p * RPI + row_in_grp;
-#pragma unroll
-      for (int m = 0; m < kGemvMaxTokens; ++m) {
-        if (m < M) {
-          const float g = group_sum<BPR>(block_term<Q>(qg[p], xb[m]));
-          const float u = group_sum<BPR>(block_term<Q>(qu[p], xb[m]));
-          if (blk_in_row == 0)
-            h[(size_t)(slot0 + m) * ex.I + row] = (uint16_t)f32_to_bf16_bits(silu_mul(g, u));
-        }
-      }
-    }
+  __shared__ WorkMap wm;
+  workmap_init(wm, a.counts, ex.E_tot, a.gmax);
+  constexpr int WG_ROWS = gateup_rows<BPR>();
+  const int per_e = ex.I / WG_ROWS;
+  const int wave = threadIdx.x >> 6;
+  for (int item = blockIdx.x; item < wm.n_gemv * per_e; item += gridDim.x) {
+    const int e = workmap_gemv(wm, ex.E_tot, item / per_e);
+    const int M = a.counts[e], slot0 = a.offsets[e];
+    const int prw0 = (item % per_e) * WG_ROWS + wave * (WG_ROWS / 4);
+    if (M == 1) gemv_gateup_wave<BPR, 1, Q, XF32>(ex, a, e, prw0, M, slot0);
+    else if (M == 2) gemv_gateup_wave<BPR, 2, Q, XF32>(ex, a, e, prw0, M, slot0);
+    else gemv_gateup_wave<BPR, 4, Q, XF32>(ex, a, e, prw0, M, slot0);
   }
 }
 
-// Decode GEMV, down projection with the gate folded in: o[slot] = gate * Wd h.
-// Lane layout as above with BPR = I/32; a workgroup takes 64 rows of H.
+// Output of one expert row for one assignment: gate * value, stored per slot
+// (fp32 for few tokens, bf16 for many) for the combine kernel.
+__device__ inline void emit(const Experts& ex, const FfnArgs& a, int slot, int row, float val) {
+  if (a.o) a.o[(size_t)slot * ex.H + row] = val;
+  else a.ob[(size_t)slot * ex.H + row] = (uint16_t)f32_to_bf16_bits(val);
+}
+
+__device__ inline float gate_of(const FfnArgs& a, int slot) {
+  const int asg = a.perm[slot];
+  return asg < a.T * a.k ? a.gates[asg] : 1.0f;
+}
+
+// Decode GEMV, down projection with the gate folded in, one wave: RW rows of H
+// from row r0w for MP >= M token slots.
+template <int BPR, int MP, int Q>
+__device__ inline void gemv_down_wave(const Experts& ex, const FfnArgs& a, int e, int r0w, int M,
+                                      int slot0) {
+  constexpr int RPI = 64 / BPR;
+  constexpr int RW = RPI > 16 ? RPI : 16;
+  constexpr int P = RW / RPI;
+  constexpr int NV = P * MP;
+  const int lane = threadIdx.x & 63;
+  const int b = lane % BPR, rg = lane / BPR;
+  QBlock qd[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const size_t row = (size_t)r0w + p * RPI + rg;
+    qd[p] = load_qblock<Q>(ex, blk_down(ex, e) + row * BPR + b);
+  }
+  const uint16_t* h = static_cast<const uint16_t*>(a.h);
+  XB xb[MP];
+  float gate[MP];
+#pragma unroll
+  for (int i = 0; i < MP; ++i) {
+    if (i < M) {
+      load_xb_bf16<Q>(h + (size_t)(slot0 + i) * ex.I + 32 * b, xb[i]);
+      gate[i] = gate_of(a, slot0 + i);
+    } else {
+      zero_xb(xb[i]);
+      gate[i] = 0.f;
+    }
+  }
+  float v[NV];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    float o[MP];
+    block_values<Q, MP>(qd[p], xb, o);
+#pragma unroll
+    for (int i = 0; i < MP; ++i) v[p * MP + i] = o[i];
+  }
+  int jbase = 0;
+  LaneReduce<NV, BPR / 2>::run(v, lane, jbase);
+  constexpr int NF = NV > BPR ? NV / BPR : 1;
+  constexpr int REP = NV < BPR ? BPR / NV : 1;  // lanes holding the same sums
+  if ((lane & (REP - 1)) != 0) return;
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int idx = jbase + j, p = idx / MP, i = idx % MP;
+    if (i < M) emit(ex, a, slot0 + i, r0w + p * RPI + rg, gate[i] * v[j]);
+  }
+}
+
 template <int BPR, int Q>
 __global__ __launch_bounds__(kThreads) void gemv_down(Experts ex, FfnArgs a) {
-  constexpr int RPI = 64 / BPR;
-  constexpr int ROWS_W = RPI > 16 ? RPI : 16;
-  constexpr int PASSES = ROWS_W / RPI;
-  constexpr int RC = 4 * ROWS_W;
-  const SchedView sv = sched_view(a.sched, ex.E_tot);
-  const int n_items = sv.hdr[0] * (ex.H / RC);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int blk_in_row = lane % BPR, row_in_grp = lane / BPR;
-  const uint16_t* h = static_cast<const uint16_t*>(a.h);
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int e = sv.gemv[item / (ex.H / RC)];
-    const int r0 = (item % (ex.H / RC)) * RC + wave * ROWS_W;
-    const int M = a.counts[e];
-    const int slot0 = a.offsets[e];
-    XBlock xb[kGemvMaxTokens];
-    float gate[kGemvMaxTokens];
-#pragma unroll
-    for (int m = 0; m < kGemvMaxTokens; ++m) {
-      if (m < M) {
-        load_xblock_bf16(h + (size_t)(slot0 + m) * ex.I + 32 * blk_in_row, xb[m]);
-        const int asg = a.perm[slot0 + m];
-        gate[m] = asg < a.T * a.k ? a.gates[asg] : 1.0f;
-      }
-    }
-    QBlock qd[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = r0 + p * RPI + row_in_grp;
-      qd[p] = load_qblock<Q>(ex, blk_down(ex, e) + (size_t)row * BPR + blk_in_row);
-    }
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = r0 + p * RPI + row_in_grp;
-#pragma unroll
-      for (int m = 0; m < kGemvMaxTokens; ++m) {
-        if (m < M) {
-          const float v = group_sum<BPR>(block_term<Q>(qd[p], xb[m]));
-          if (blk_in_row == 0) a.o[(size_t)(slot0 + m) * ex.H + row] = gate[m] * v;
-        }
-      }
-    }
+  __shared__ WorkMap wm;
+  workmap_init(wm, a.counts, ex.E_tot, a.gmax);
+  constexpr int WG_ROWS = down_rows<BPR>();
+  const int per_e = ex.H / WG_ROWS;
+  const int wave = threadIdx.x >> 6;
+  for (int item = blockIdx.x; item < wm.n_gemv * per_e; item += gridDim.x) {
+    const int e = workmap_gemv(wm, ex.E_tot, item / per_e);
+    const int M = a.counts[e], slot0 = a.offsets[e];
+    const int r0w = (item % per_e) * WG_ROWS + wave * (WG_ROWS / 4);
+    if (M == 1) gemv_down_wave<BPR, 1, Q>(ex, a, e, r0w, M, slot0);
+    else if (M == 2) gemv_down_wave<BPR, 2, Q>(ex, a, e, r0w, M, slot0);
+    else gemv_down_wave<BPR, 4, Q>(ex, a, e, r0w, M, slot0);
   }
 }
 
@@ -298,31 +253,30 @@ template <int Q, bool XF32>
 __global__ __launch_bounds__(kThreads) void mfma_gateup(Experts ex, FfnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 xs[kTileM * kLdsRow];
   __shared__ __attribute__((aligned(16))) _Float16 ws[2 * kTN * kLdsRow];
-  const SchedView sv = sched_view(a.sched, ex.E_tot);
+  __shared__ WorkMap wm;
+  workmap_init(wm, a.counts, ex.E_tot, a.gmax);
   const int n_nt = ex.I / kTN;
-  const int n_items = sv.hdr[1] * n_nt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int th = wave & 1, rh = wave >> 1;
   _Float16* hbuf = static_cast<_Float16*>(a.h);
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int tile = sv.tiles[item / n_nt];
+  for (int item = blockIdx.x; item < wm.n_tiles * n_nt; item += gridDim.x) {
+    int tl;
+    const int e = workmap_tile(wm, ex.E_tot, item / n_nt, tl);
     const int n0 = (item % n_nt) * kTN;
-    const int e = tile >> 16, m0 = (tile & 0xFFFF) * kTileM;
+    const int m0 = tl * kTileM;
     const int M = a.counts[e] - m0;
     const int slot0 = a.offsets[e] + m0;
-    // loader roles
-    const int xr = tid >> 2, xq = tid & 3;  // x: row xr, 16 K-elements at 16*xq
+    const int xr = tid >> 2, xq = tid & 3;  // x loader: row xr, 16 K-elements at 16*xq
     int tok = -1;
     if (xr < M) {
       tok = token_of(a.perm[slot0 + xr], a.T, a.k);
       if ((unsigned)tok >= (unsigned)a.T) tok = -1;
     }
-    const int wr = tid >> 1, wb = tid & 1;  // w: weight row wr (0..127), block wb
+    const int wr = tid >> 1, wb = tid & 1;  // weight loader: row wr (0..127), block wb
     const size_t wblk0 = (wr < kTN ? blk_gate(ex, e) : blk_up(ex, e)) +
                          (size_t)(n0 + (wr & (kTN - 1))) * (ex.H / 32) + wb;
     float16_t acc_g = {}, acc_u = {};
     for (int k0 = 0; k0 < ex.H; k0 += kTK) {
-      // global -> registers
       uint32_t xv[8];
       if (tok >= 0) {
         if (XF32) {
@@ -365,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gateup(Experts ex, FfnArgs a) {
         acc_u = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bu, acc_u, 0, 0, 0);
       }
     }
-    // epilogue: acc[i] -> assignment 8*(i/4) + 4*(lane/32) + i%4, row lane%32
+    // acc[i] -> assignment 8*(i/4) + 4*(lane/32) + i%4, row lane%32
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int mm = 32 * th + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
@@ -377,25 +331,26 @@ __global__ __launch_bounds__(kThreads) void mfma_gateup(Experts ex, FfnArgs a) {
   }
 }
 
-// Down projection, o[slot] = gate * Wd h. Tile: 64 assignments x 64 rows of H.
+// Down projection, gate * Wd h. Tile: 64 assignments x 64 rows of H.
 template <int Q>
 __global__ __launch_bounds__(kThreads) void mfma_down(Experts ex, FfnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 xs[kTileM * kLdsRow];
   __shared__ __attribute__((aligned(16))) _Float16 ws[kTN * kLdsRow];
-  const SchedView sv = sched_view(a.sched, ex.E_tot);
+  __shared__ WorkMap wm;
+  workmap_init(wm, a.counts, ex.E_tot, a.gmax);
   const int n_nt = ex.H / kTN;
-  const int n_items = sv.hdr[1] * n_nt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int th = wave & 1, rh = wave >> 1;
   const _Float16* hbuf = static_cast<const _Float16*>(a.h);
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int tile = sv.tiles[item / n_nt];
+  for (int item = blockIdx.x; item < wm.n_tiles * n_nt; item += gridDim.x) {
+    int tl;
+    const int e = workmap_tile(wm, ex.E_tot, item / n_nt, tl);
     const int n0 = (item % n_nt) * kTN;
-    const int e = tile >> 16, m0 = (tile & 0xFFFF) * kTileM;
+    const int m0 = tl * kTileM;
     const int M = a.counts[e] - m0;
     const int slot0 = a.offsets[e] + m0;
     const int xr = tid >> 2, xq = tid & 3;
-    const int wr = (tid >> 1) & (kTN - 1), wb = tid & 1;  // threads >= 128 mirror; only < 128 store
+    const int wr = (tid >> 1) & (kTN - 1), wb = tid & 1;  // threads >= 128 only load x
     const size_t wblk0 = blk_down(ex, e) + (size_t)(n0 + wr) * (ex.I / 32) + wb;
     float16_t acc = {};
     for (int k0 = 0; k0 < ex.I; k0 += kTK) {
@@ -426,12 +381,7 @@ __global__ __launch_bounds__(kThreads) void mfma_down(Experts ex, FfnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int mm = 32 * th + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (mm < M) {
-        const int slot = slot0 + mm;
-        const int asg = a.perm[slot];
-        const float gate = asg < a.T * a.k ? a.gates[asg] : 1.0f;
-        a.o[(size_t)slot * ex.H + n0 + 32 * rh + (lane & 31)] = gate * acc[i];
-      }
+      if (mm < M) emit(ex, a, slot0 + mm, n0 + 32 * rh + (lane & 31), gate_of(a, slot0 + mm) * acc[i]);
     }
   }
 }
@@ -440,38 +390,41 @@ inline int grid_for(long max_items, int cap) {
   return (int)(max_items < cap ? (max_items > 0 ? max_items : 1) : cap);
 }
 
+
 template <int Q, bool XF32>
 hipError_t launch_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   const int A = a.T * (a.k + ex.has_shared);
   const long max_gemv = A < ex.E_tot ? A : ex.E_tot;
   const long max_tiles = A / kTileM + ex.E_tot + 1;
   const int bpr_h = ex.H / 32, bpr_i = ex.I / 32;
-  // decode GEMV (only when the shapes fit the lane layouts; otherwise the
-  // scheduler sends every expert to the MFMA tiles)
-#define GU(B) hipLaunchKernelGGL((gemv_gateup<B, Q, XF32>), dim3(grid_for(max_gemv * (ex.I / (4 * (64 / B > 4 ? 64 / B : 4))), 2048)), dim3(kThreads), 0, s, ex, a)
-#define DN(B) hipLaunchKernelGGL((gemv_down<B, Q>), dim3(grid_for(max_gemv * (ex.H / (4 * (64 / B > 16 ? 64 / B : 16))), 2048)), dim3(kThreads), 0, s, ex, a)
-  switch (bpr_h) {
-    case 4: GU(4); break;
-    case 8: GU(8); break;
-    case 16: GU(16); break;
-    case 32: GU(32); break;
-    case 64: GU(64); break;
-    default: break;
+  const bool gemv = a.gmax > 0;
+  const bool mfma = a.T > a.gmax;  // an expert holds at most T assignments
+#define GU(B)                                                                                      \
+  case B:                                                                                          \
+    MOE_LAUNCH("gemv_gateup", s, (gemv_gateup<B, Q, XF32>),                                        \
+               dim3(grid_for(max_gemv * (ex.I / gateup_rows<B>()), 2048)), dim3(kThreads), 0, s, ex, \
+               a);                                                                                 \
+    break;
+#define DN(B)                                                                                    \
+  case B:                                                                                        \
+    MOE_LAUNCH("gemv_down", s, (gemv_down<B, Q>),                                                \
+               dim3(grid_for(max_gemv * (ex.H / down_rows<B>()), 2048)), dim3(kThreads), 0, s, ex, \
+               a);                                                                               \
+    break;
+  if (gemv) {
+    switch (bpr_h) { GU(4) GU(8) GU(16) GU(32) GU(64) default: return hipErrorInvalidValue; }
   }
-  hipLaunchKernelGGL((mfma_gateup<Q, XF32>), dim3(grid_for(max_tiles * (ex.I / kTN), 4096)),
-                     dim3(kThreads), 0, s, ex, a);
-  switch (bpr_i) {
-    case 4: DN(4); break;
-    case 8: DN(8); break;
-    case 16: DN(16); break;
-    case 32: DN(32); break;
-    case 64: DN(64); break;
-    default: break;
+  if (mfma)
+    MOE_LAUNCH("mfma_gateup", s, (mfma_gateup<Q, XF32>), dim3(grid_for(max_tiles * (ex.I / kTN), 4096)),
+               dim3(kThreads), 0, s, ex, a);
+  if (mfma)
+    MOE_LAUNCH("mfma_down", s, (mfma_down<Q>), dim3(grid_for(max_tiles * (ex.H / kTN), 4096)),
+               dim3(kThreads), 0, s, ex, a);
+  if (gemv) {
+    switch (bpr_i) { DN(4) DN(8) DN(16) DN(32) DN(64) default: return hipErrorInvalidValue; }
   }
 #undef GU
 #undef DN
-  hipLaunchKernelGGL((mfma_down<Q>), dim3(grid_for(max_tiles * (ex.H / kTN), 4096)),
-                     dim3(kThreads), 0, s, ex, a);
   return hipGetLastError();
 }
 

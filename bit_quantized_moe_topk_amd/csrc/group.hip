@@ -13,6 +13,8 @@
 // Order inside an expert is therefore ascending id, identical on every run.
 // Small inputs run all three steps in one workgroup; large ones in 3 launches.
 #include "common.h"
+#include "sched.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -59,35 +61,6 @@ __device__ inline void wave_scatter(const int32_t* __restrict__ idx, int f0, int
   }
 }
 
-// Block-wide exclusive scan of data[0..n) in place; returns the total.
-// blockDim.x must be a multiple of 64 and at most 1024.
-__device__ int block_exclusive_scan(int* data, int n, int* tmp /* LDS, >= 1024 */) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int per = (n + nt - 1) / nt;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += data[i];
-  tmp[tid] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the per-thread sums
-  for (int off = 1; off < nt; off <<= 1) {
-    const int v = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += v;
-    __syncthreads();
-  }
-  int run = tid == 0 ? 0 : tmp[tid - 1];
-  const int total = tmp[nt - 1];
-  __syncthreads();
-  for (int i = lo; i < hi; ++i) {
-    const int v = data[i];
-    data[i] = run;
-    run += v;
-  }
-  __syncthreads();
-  return total;
-}
-
 __device__ inline void write_offsets(const int* base, int nseg, int E, int T, int k, int has_shared,
                                      int32_t* counts, int32_t* offsets) {
   const int AR = T * k;
@@ -111,12 +84,12 @@ __device__ inline void write_shared(int T, int k, int has_shared, int32_t* perm,
   }
 }
 
-// All three steps in one workgroup of 1024 threads (16 waves = 16 segments).
+// All three steps in one workgroup: one wave per segment (nseg <= 16).
 __global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ idx, int T, int k,
                                                     int E, int has_shared, int nseg,
                                                     int32_t* counts, int32_t* offsets,
                                                     int32_t* perm, int32_t* slot_of) {
-  extern __shared__ int lds[];  // [E * nseg] bases, then [1024] scan scratch
+  extern __shared__ int lds[];  // [E * nseg] bases, then [16] wave totals
   int* hist = lds;
   int* tmp = lds + E * nseg;
   const int AR = T * k;
@@ -130,6 +103,35 @@ __global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ 
   write_offsets(hist, nseg, E, T, k, has_shared, counts, offsets);
   __syncthreads();  // the bases are read above before the scatter advances them
   if (seg < nseg) wave_scatter(idx, f0, f1, E, hist + seg, nseg, perm, slot_of);
+  write_shared(T, k, has_shared, perm, slot_of);
+}
+
+// Top-k and grouping in one workgroup for small batches (a decode verify
+// window): every wave selects experts for its tokens into global memory and
+// into LDS, then the workgroup groups the LDS copy as group_fused does.
+template <int PER_LANE>
+__global__ __launch_bounds__(1024) void route_group_small(const float* __restrict__ logits, int T,
+                                                          int E, int k, int has_shared,
+                                                          int32_t* idx, float* gates,
+                                                          int32_t* counts, int32_t* offsets,
+                                                          int32_t* perm, int32_t* slot_of) {
+  extern __shared__ int lds[];  // [T*k] expert ids, [E] bases, [16] wave totals
+  int* lidx = lds;
+  int* hist = lds + T * k;
+  int* wsum = hist + E;
+  const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int t = wv; t < T; t += nw)
+    topk_token<PER_LANE>(logits + (size_t)t * E, E, k, idx + (size_t)t * k, gates + (size_t)t * k,
+                         lidx + t * k);
+  for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const int AR = T * k;
+  if (wv == 0) wave_count(lidx, 0, AR, E, hist, 1);
+  __syncthreads();
+  block_exclusive_scan(hist, E, wsum);
+  write_offsets(hist, 1, E, T, k, has_shared, counts, offsets);
+  __syncthreads();
+  if (wv == 0) wave_scatter(lidx, 0, AR, E, hist, 1, perm, slot_of);
   write_shared(T, k, has_shared, perm, slot_of);
 }
 
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) void group_count(const int32_t* __restrict__ i
 // Step 2: one workgroup scans hist in place and writes counts / offsets.
 __global__ __launch_bounds__(1024) void group_scan(int T, int k, int E, int has_shared, int nseg,
                                                    int* hist, int32_t* counts, int32_t* offsets) {
-  __shared__ int tmp[1024];
+  __shared__ int tmp[16];
   block_exclusive_scan(hist, E * nseg, tmp);
   write_offsets(hist, nseg, E, T, k, has_shared, counts, offsets);
 }
@@ -180,10 +182,25 @@ __global__ __launch_bounds__(256) void group_scatter(const int32_t* __restrict__
 }
 
 inline int nseg_of(int T, int k) { return (T * k + kSeg - 1) / kSeg; }
-// One workgroup when its LDS (bases + scan scratch) stays within 64 KiB.
+// One workgroup when its LDS (bases + wave totals) stays within 64 KiB.
 inline bool use_fused(int T, int k, int E) {
   const int n = nseg_of(T, k);
-  return n <= 16 && (size_t)E * n + 1024 <= 16384;
+  return n <= 16 && (size_t)E * n + 16 <= 16384;
+}
+
+inline bool small_route_group(int T, int k, int E) {
+  return T <= 64 && T * k <= kSeg && (size_t)(T * k + E + 16) * sizeof(int) <= 65536;
+}
+
+template <int P>
+hipError_t launch_rg(const float* logits, int T, int E, int k, int has_shared, int32_t* idx,
+                     float* gates, int32_t* counts, int32_t* offsets, int32_t* perm,
+                     int32_t* slot_of, hipStream_t s) {
+  const int waves = T < 16 ? T : 16;
+  const size_t lds = (size_t)(T * k + E + 16) * sizeof(int);
+  MOE_LAUNCH("route_group", s, route_group_small<P>, dim3(1), dim3(64 * waves), lds, s, logits, T,
+             E, k, has_shared, idx, gates, counts, offsets, perm, slot_of);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -198,21 +215,39 @@ hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared,
                         hipStream_t s) {
   const int nseg = nseg_of(T, k);
   if (use_fused(T, k, E)) {
-    const size_t lds = ((size_t)E * nseg + 1024) * sizeof(int);
-    hipLaunchKernelGGL(group_fused, dim3(1), dim3(1024), lds, s, idx, T, k, E, has_shared, nseg,
+    const size_t lds = ((size_t)E * nseg + 16) * sizeof(int);
+    const int threads = 64 * (nseg > 0 ? nseg : 1);
+    MOE_LAUNCH("group_fused", s, group_fused, dim3(1), dim3(threads), lds, s, idx, T, k, E, has_shared, nseg,
                        counts, offsets, perm, slot_of);
     return hipGetLastError();
   }
   int* hist = static_cast<int*>(scratch);
   const int blocks = (nseg + 3) / 4;
   const size_t lds = (size_t)4 * E * sizeof(int);
-  hipLaunchKernelGGL(group_count, dim3(blocks), dim3(256), lds, s, idx, T, k, E, has_shared, nseg,
+  MOE_LAUNCH("group_count", s, group_count, dim3(blocks), dim3(256), lds, s, idx, T, k, E, has_shared, nseg,
                      hist, perm, slot_of);
-  hipLaunchKernelGGL(group_scan, dim3(1), dim3(1024), 0, s, T, k, E, has_shared, nseg, hist,
+  MOE_LAUNCH("group_scan", s, group_scan, dim3(1), dim3(1024), 0, s, T, k, E, has_shared, nseg, hist,
                      counts, offsets);
-  hipLaunchKernelGGL(group_scatter, dim3(blocks), dim3(256), lds, s, idx, T, k, E, nseg, hist,
+  MOE_LAUNCH("group_scatter", s, group_scatter, dim3(blocks), dim3(256), lds, s, idx, T, k, E, nseg, hist,
                      perm, slot_of);
   return hipGetLastError();
+}
+
+hipError_t launch_route_group(const float* logits, int T, int E, int k, int has_shared, int32_t* idx,
+                              float* gates, int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* slot_of, void* scratch, hipStream_t s) {
+  if (small_route_group(T, k, E)) {
+    const int per = (E + 63) / 64;
+    if (per <= 1) return launch_rg<1>(logits, T, E, k, has_shared, idx, gates, counts, offsets, perm, slot_of, s);
+    if (per <= 2) return launch_rg<2>(logits, T, E, k, has_shared, idx, gates, counts, offsets, perm, slot_of, s);
+    if (per <= 4) return launch_rg<4>(logits, T, E, k, has_shared, idx, gates, counts, offsets, perm, slot_of, s);
+    if (per <= 8) return launch_rg<8>(logits, T, E, k, has_shared, idx, gates, counts, offsets, perm, slot_of, s);
+    if (per <= 16) return launch_rg<16>(logits, T, E, k, has_shared, idx, gates, counts, offsets, perm, slot_of, s);
+    return launch_rg<32>(logits, T, E, k, has_shared, idx, gates, counts, offsets, perm, slot_of, s);
+  }
+  hipError_t e = launch_topk(logits, T, E, k, idx, gates, s);
+  if (e != hipSuccess) return e;
+  return launch_group(idx, T, k, E, has_shared, counts, offsets, perm, slot_of, scratch, s);
 }
 
 }  // namespace moe

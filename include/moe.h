@@ -24,8 +24,9 @@
  *     MOE_ERR_HIP means a kernel launch failed (hipGetLastError); faults inside
  *     a kernel surface at the caller's next synchronisation of the stream.
  *   - Element counts are int32; sizes in bytes are size_t.
- *   - No call keeps global state; calls on different streams may run
- *     concurrently as long as they do not share output or workspace buffers.
+ *   - No compute call keeps global state (the opt-in launch profiler below is
+ *     the one exception); calls on different streams may run concurrently as
+ *     long as they do not share output or workspace buffers.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -107,6 +108,16 @@ int moe_group(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t has_s
               int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *slot_of, void *ws,
               size_t ws_bytes, void *stream);
 
+/* Top-k routing followed by the grouping, in one call: the same results as
+ * moe_route_topk then moe_group (idx, gates, counts, offsets, perm, slot_of as
+ * defined there). Small batches (T <= 64 and T*k <= 1024, the decode verify
+ * windows) run as one workgroup in a single launch; larger ones run the two
+ * steps' kernels back to back. ws: at least moe_group_workspace_size(T, k, E)
+ * bytes. T == 0 writes the empty grouping (counts, offsets) only. */
+int moe_route_group(const float *logits, int32_t T, int32_t E, int32_t k, int32_t has_shared,
+                    int32_t *idx, float *gates, int32_t *counts, int32_t *offsets, int32_t *perm,
+                    int32_t *slot_of, void *ws, size_t ws_bytes, void *stream);
+
 /* ---- experts ------------------------------------------------------------ */
 
 /* An immutable description of one layer's packed experts. The handle is a small
@@ -123,8 +134,10 @@ int moe_group(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t has_s
  *          32-bit word is bit 2 of code j. Pass NULL for Q2.
  *   dm   : NB * 2 uint16 per expert: fp16 bits of d, then of m, per block.
  *   Weight value: w = d*q + m.
- * Plane bases must be 16-byte aligned. Requires H, I multiples of 256 (the
- * decode kernels' row chunk), 1 <= E <= MOE_MAX_E. */
+ * Plane bases must be 16-byte aligned. Requires H, I multiples of 64 (the
+ * matrix-core tile), 1 <= E <= MOE_MAX_E. The decode GEMV kernels cover
+ * H/32 and I/32 in {4, 8, 16, 32, 64}; other shapes run every expert on the
+ * matrix-core tiles. */
 typedef struct moe_experts moe_experts;
 
 int moe_experts_create(moe_experts **out, int32_t qtype, int32_t E, int32_t has_shared,
@@ -157,6 +170,44 @@ int moe_ffn_q(const void *x, int32_t xdtype, int32_t T, const moe_experts *ex,
               const int32_t *idx, const float *gates, int32_t k, const int32_t *counts,
               const int32_t *offsets, const int32_t *perm, const int32_t *slot_of, void *y,
               int32_t mode, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- whole layer ---------------------------------------------------------- */
+
+/* Workspace bytes moe_layer needs (device scratch). */
+size_t moe_layer_workspace_size(const moe_experts *ex, int32_t T, int32_t k, int32_t mode);
+
+/* The whole routed MoE layer in one call: top-k routing of `logits` ([T][E]
+ * f32), the grouping, the expert FFN and the combine, writing idx and gates
+ * ([T][k]) and y ([T][H]). Results match moe_route_group followed by
+ * moe_ffn_q within the FFN tolerance (idx and gates identically). A decode
+ * verify window (fast mode, T <= 4, k <= 64, H/32 and I/32 in {4..64}) runs as
+ * two kernels: the first routes the window in every workgroup and computes
+ * gate/up for all active experts, the second computes the down projection and
+ * sums the combine in registers, so its y is reproducible run to run. Other
+ * calls run moe_route_group then moe_ffn_q inside the workspace.
+ * ws: at least moe_layer_workspace_size(ex, T, k, mode) bytes. */
+int moe_layer(const float *logits, const void *x, int32_t xdtype, int32_t T, const moe_experts *ex,
+              int32_t k, int32_t *idx, float *gates, void *y, int32_t mode, void *ws,
+              size_t ws_bytes, void *stream);
+
+/* ---- launch profiling ------------------------------------------------------ */
+
+/* A measurement aid for the caller's own timing (per-kernel GPU durations).
+ * moe_profile_begin: from now on every kernel the library launches is
+ *   bracketed by two HIP events recorded on its launch stream, for up to
+ *   max_launches launches (later launches are not recorded). Clears earlier
+ *   records. Creates the events on first use (host-side objects, no device
+ *   memory).
+ * moe_profile_end: stops recording, waits for the recorded events and sums the
+ *   elapsed time per kernel name.
+ * moe_profile_count / moe_profile_get: the summary, one entry per kernel name:
+ *   name (static string owned by the library), launches, total milliseconds.
+ * The profiling state is process-global and not thread-safe; it is off unless
+ * moe_profile_begin is called. */
+int moe_profile_begin(int32_t max_launches);
+int moe_profile_end(void);
+int32_t moe_profile_count(void);
+int moe_profile_get(int32_t i, const char **name, int32_t *launches, double *total_ms);
 
 /* A static, human-readable description of a status code (host string). */
 const char *moe_status_string(int32_t status);

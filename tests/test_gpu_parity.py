@@ -107,6 +107,58 @@ def test_group_edges():
     check_group(rng.integers(0, 3, size=(1700, 2)).astype(np.int32), 3, True, "E=3 ragged")
 
 
+@pytest.mark.parametrize("cid,T", [(0, 8), (1, 4), (4, 64), (1, 1), (2, 1024), (0, 3)])
+def test_route_group_fused_bit_exact(cid, T):
+    """The one-call route + group (single workgroup for small batches) equals
+    the oracle's top-k followed by its grouping."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfg = CONFIGS[cid].with_(T=T)
+    lg = make_logits(CONFIGS[cid], seed=3)[:T].copy()
+    log(f"[route_group] cfg{cid} T={T}")
+    idx, gates, g = moe.route_group(torch.from_numpy(lg).cuda(), cfg.k, bool(cfg.shared))
+    torch.cuda.synchronize()
+    idx_o, g_o = oracle.route(lg, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_o)
+    assert np.max(np.abs(gates.cpu().numpy() - g_o)) <= 1e-6
+    ref = oracle.group(idx_o, cfg.E, bool(cfg.shared))
+    got = (g.counts.cpu().numpy(), g.offsets.cpu().numpy(), g.perm.cpu().numpy(),
+           g.slot_of.cpu().numpy())
+    for name, a, b in zip(("counts", "offsets", "perm", "slot_of"), got, ref):
+        assert np.array_equal(a, b), name
+
+
+@pytest.mark.parametrize("cid,T,mode", [(1, 4, "fast"), (1, 1, "fast"), (1, 3, "fast"),
+                                         (4, 4, "fast"), (4, 2, "fast"), (0, 4, "fast"),
+                                         (0, 8, "fast"), (4, 64, "fast"), (1, 4, "check")])
+def test_layer_call(cid, T, mode):
+    """moe_layer (whole layer in one call; the two-kernel window path for T <= 4
+    in fast mode) against the oracle's route, grouping and layer."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    base = CONFIGS[cid]
+    lay = make_layer(base, seed=21)
+    cfg = base.with_(T=T)
+    lay = dict(lay, cfg=cfg, x=lay["x"][:T].copy(), logits=lay["logits"][:T].copy())
+    dev = upload(lay)
+    ex = experts_of(lay, dev)
+    log(f"[layer call] cfg{cid} T={T} mode={mode}")
+    idx, gates, y = moe.layer(dev["logits"], dev["x"], ex, cfg.k, mode=mode)
+    torch.cuda.synchronize()
+    idx_o, g_o = oracle.route(lay["logits"], cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_o)
+    assert np.max(np.abs(gates.cpu().numpy() - g_o)) <= 1e-6
+    ref = oracle_rows(lay, idx_o, g_o)
+    err = rel_l2_rows(y_to_f64(y), ref)
+    log(f"[layer call] cfg{cid} T={T} {mode}: max rel-L2 {err.max():.3e}")
+    assert err.max() <= (TOL_CHECK if mode == "check" else TOL_FAST)
+    y2 = moe.layer(dev["logits"], dev["x"], ex, cfg.k, mode=mode)[2]
+    torch.cuda.synchronize()
+    if mode == "fast" and T <= 4:
+        assert torch.equal(y, y2), "window path must be reproducible run to run"
+    ex.close()
+
+
 def run_ffn(lay, dev, idx_np, gates_np, mode, use_gpu_grouping=False):
     torch = torch_cuda()
     import bit_quantized_moe_topk_amd as moe
