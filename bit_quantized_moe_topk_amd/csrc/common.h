@@ -42,6 +42,12 @@ constexpr int kTileM = 64;  // assignments per MFMA tile
 constexpr int kF32SlotMaxTokens = 256;
 
 // fp16 bit pattern -> float (exact; v_cvt_f32_f16).
+// Bit mask of the lanes below this one in its 64-wide wavefront.
+__device__ inline uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
 __device__ inline float half_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
 // Launch profiling hooks (no-ops unless a caller enabled moe_profile_begin).

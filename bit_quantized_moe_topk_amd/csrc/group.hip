@@ -116,13 +116,14 @@ __global__ __launch_bounds__(1024) void route_group_small(const float* __restric
                                                           int32_t* counts, int32_t* offsets,
                                                           int32_t* perm, int32_t* slot_of) {
   extern __shared__ int lds[];  // [T*k] expert ids, [E] bases, [16] wave totals
+  __shared__ TopkScratch sc[16];
   int* lidx = lds;
   int* hist = lds + T * k;
   int* wsum = hist + E;
   const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int t = wv; t < T; t += nw)
     topk_token<PER_LANE>(logits + (size_t)t * E, E, k, idx + (size_t)t * k, gates + (size_t)t * k,
-                         lidx + t * k);
+                         &sc[wv], lidx + t * k);
   for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
   __syncthreads();
   const int AR = T * k;
@@ -189,7 +190,8 @@ inline bool use_fused(int T, int k, int E) {
 }
 
 inline bool small_route_group(int T, int k, int E) {
-  return T <= 64 && T * k <= kSeg && (size_t)(T * k + E + 16) * sizeof(int) <= 65536;
+  return T <= 64 && T * k <= kSeg &&
+         (size_t)(T * k + E + 16) * sizeof(int) + 16 * sizeof(TopkScratch) <= 65536;
 }
 
 template <int P>

@@ -10,9 +10,11 @@ template <int PER_LANE>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ gates) {
+  __shared__ TopkScratch sc[4];
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token<PER_LANE>(logits + (size_t)t * E, E, k, idx + (size_t)t * k, gates + (size_t)t * k);
+  topk_token<PER_LANE>(logits + (size_t)t * E, E, k, idx + (size_t)t * k, gates + (size_t)t * k,
+                       &sc[threadIdx.x >> 6]);
 }
 
 template <int P>

@@ -15,11 +15,6 @@
 
 namespace moe {
 
-__device__ inline uint64_t lanemask_lt() {
-  const int lane = threadIdx.x & 63;
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
-}
-
 __device__ inline int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll

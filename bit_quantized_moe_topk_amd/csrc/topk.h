@@ -51,22 +51,106 @@ __device__ inline uint32_t wave_reduce(uint32_t v) {
   return op(op(r0, r1), op(r2, r3));
 }
 
+// Sum over the 64 lanes in a fixed order, returned in every lane (DPP within
+// each 16-lane row, then the four row sums in lane order).
+__device__ inline float wave_sum(float v) {
+  v += __uint_as_float(dpp(__float_as_uint(v), 0xB1));
+  v += __uint_as_float(dpp(__float_as_uint(v), 0x4E));
+  v += __uint_as_float(dpp(__float_as_uint(v), 0x141));
+  v += __uint_as_float(dpp(__float_as_uint(v), 0x140));
+  const float r0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+  const float r1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
+  const float r2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32));
+  const float r3 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// LDS scratch of one wave for topk_token.
+struct alignas(16) TopkScratch {
+  uint32_t head[64];  // every lane's best code
+  uint64_t cand[64];  // compacted candidates: code << 32 | (~expert)
+};
+
 // Selects the k best experts of logits row l (E entries) into idx_t[0..k) in
 // rank order and their gates into g_t[0..k); also into lds_idx when not null.
-// Every lane of the wave calls it. A round takes one DPP max of the lanes' best
-// codes; a ballot finds the lanes holding it, and only when several lanes tie
-// does a DPP min pick the lowest expert index among them. The softmax runs
-// once after the k rounds (lane j holds the j-th selected logit).
+// Every lane of the wave calls it; sc is this wave's own LDS scratch.
+//
+// Threshold pass (k <= 64): the k-th largest of the 64 lane maxima, tau, is at
+// most the k-th largest code overall (k distinct experts reach it), so every
+// selected expert has a code >= tau, and few others do. Those candidates are
+// compacted into LDS; each ranks itself by counting the candidates that beat
+// it (larger code, or equal code and lower index), and rank r < k lands in
+// slot r. When more than 64 codes reach tau (heavy ties), or k > 64, rounds
+// take over: each finds the largest remaining code with a DPP max and the
+// lowest index holding it, and retires it.
 template <int PER_LANE>
 __device__ inline void topk_token(const float* __restrict__ l, int E, int k, int32_t* idx_t,
-                                  float* g_t, int32_t* lds_idx = nullptr) {
+                                  float* g_t, TopkScratch* sc, int32_t* lds_idx = nullptr) {
   const int lane = threadIdx.x & 63;
+  // All loads issue back to back (clamped address, no branch), so their
+  // latencies overlap; padding slots get code 0 afterwards.
+  float raw[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) raw[i] = l[min(lane + 64 * i, E - 1)];
   uint32_t key[PER_LANE];
 #pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? orderable(l[e]) : 0u;
+  for (int i = 0; i < PER_LANE; ++i) key[i] = lane + 64 * i < E ? orderable(raw[i]) : 0u;
+
+  if (k <= 64) {
+    uint32_t head = key[0];
+#pragma unroll
+    for (int i = 1; i < PER_LANE; ++i) head = key[i] > head ? key[i] : head;
+    sc->head[lane] = head;
+    sc->cand[lane] = 0ull;  // padding for the unrolled rank loop: beats nothing
+    __builtin_amdgcn_wave_barrier();
+    int gt = 0;
+    const uint4* h4 = reinterpret_cast<const uint4*>(sc->head);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint4 h = h4[j];
+      gt += (h.x > head) + (h.y > head) + (h.z > head) + (h.w > head);
+    }
+    const uint32_t tau = wave_reduce<false>(gt < k ? head : 0xFFFFFFFFu);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) n += __popcll(__ballot(key[i] >= tau));
+    if (n <= 64) {
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i) {
+        const bool c = key[i] >= tau;
+        const uint64_t m = __ballot(c);
+        if (c)
+          sc->cand[base + __popcll(m & lanemask_lt())] =
+              ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(lane + 64 * i);
+        base += __popcll(m);
+      }
+      __builtin_amdgcn_wave_barrier();
+      const uint64_t mine = sc->cand[lane];
+      int rank = 0;
+      const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(sc->cand);
+      for (int c = 0; c < n; c += 4) {
+        const ulonglong2 a = c2[c >> 1], b = c2[(c >> 1) + 1];
+        rank += (a.x > mine) + (a.y > mine) + (b.x > mine) + (b.y > mine);
+      }
+      const bool sel = lane < n && rank < k;
+      const int e = (int)~(uint32_t)mine;
+      const uint32_t code = (uint32_t)(mine >> 32);
+      const uint64_t first = __ballot(lane < n && rank == 0);
+      const float top =
+          from_orderable(__builtin_amdgcn_readlane(code, __ffsll((unsigned long long)first) - 1));
+      const float ej = sel ? expf(from_orderable(code) - top) : 0.f;
+      const float sum = wave_sum(ej);
+      if (sel) {
+        idx_t[rank] = e;
+        if (lds_idx) lds_idx[rank] = e;
+        g_t[rank] = ej / sum;
+      }
+      __builtin_amdgcn_wave_barrier();  // scratch free for the wave's next call
+      return;
+    }
   }
+
   uint32_t my_v = 0u;  // code of the selected logit of rank `lane` (and lane + 64*r)
   for (int j = 0; j < k; ++j) {
     uint32_t bv = key[0];

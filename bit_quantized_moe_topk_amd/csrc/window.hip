@@ -66,14 +66,15 @@ __device__ inline void block_values_masked(const QBlock& b, const XB (&xb)[kWinT
 }
 
 // Top-k of one token row with the lane count chosen by E (E <= MOE_MAX_E).
-__device__ inline void topk_any(const float* l, int E, int k, int32_t* idx_t, float* g_t) {
+__device__ inline void topk_any(const float* l, int E, int k, int32_t* idx_t, float* g_t,
+                                TopkScratch* sc) {
   const int per = (E + 63) / 64;
-  if (per <= 1) topk_token<1>(l, E, k, idx_t, g_t);
-  else if (per <= 2) topk_token<2>(l, E, k, idx_t, g_t);
-  else if (per <= 4) topk_token<4>(l, E, k, idx_t, g_t);
-  else if (per <= 8) topk_token<8>(l, E, k, idx_t, g_t);
-  else if (per <= 16) topk_token<16>(l, E, k, idx_t, g_t);
-  else topk_token<32>(l, E, k, idx_t, g_t);
+  if (per <= 1) topk_token<1>(l, E, k, idx_t, g_t, sc);
+  else if (per <= 2) topk_token<2>(l, E, k, idx_t, g_t, sc);
+  else if (per <= 4) topk_token<4>(l, E, k, idx_t, g_t, sc);
+  else if (per <= 8) topk_token<8>(l, E, k, idx_t, g_t, sc);
+  else if (per <= 16) topk_token<16>(l, E, k, idx_t, g_t, sc);
+  else topk_token<32>(l, E, k, idx_t, g_t, sc);
 }
 
 template <int BPR>
@@ -99,13 +100,15 @@ __global__ __launch_bounds__(kWinThreads) void win_gateup(const float* __restric
   __shared__ int tmask[MOE_MAX_E_DEV + 1];
   __shared__ int wsum[16];
   __shared__ WinList wl;
+  __shared__ TopkScratch tks[kWinT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = ex.E, E_tot = ex.E_tot;
   const int b = lane % BPR, rg = lane / BPR;
 
   // routing: wave t selects token t's experts (before the activation loads:
   // loads complete in order, so the logits must not queue behind them)
-  if (wave < T) topk_any(logits + (size_t)wave * E, E, k, lidx + wave * k, lgate + wave * k);
+  if (wave < T)
+    topk_any(logits + (size_t)wave * E, E, k, lidx + wave * k, lgate + wave * k, &tks[wave]);
   XB xb[kWinT];
 #pragma unroll
   for (int t = 0; t < kWinT; ++t) {
