@@ -25,7 +25,7 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // h: fp32 in check mode, 16-bit in fast mode. o: gate-scaled expert outputs
 // per assignment, fp32 in check mode and for few tokens, bf16 otherwise.
 struct FfnLayout {
-  size_t counts, offsets, perm, slot_of, group, h, o, total;
+  size_t counts, offsets, perm, slot_of, group, h, x16, o, total;
   bool o_f32;
 };
 
@@ -39,6 +39,7 @@ FfnLayout ffn_layout(const Experts& ex, int T, int k, int mode) {
   L.slot_of = off; off = align_up(off + sizeof(int32_t) * A);
   L.group = off;   off = align_up(off + moe::group_scratch_bytes(T, k, ex.E));
   L.h = off;       off = align_up(off + (mode == MOE_CHECK_F32 ? 4 : 2) * A * (size_t)ex.I);
+  L.x16 = off;     off = align_up(off + (mode == MOE_CHECK_F32 ? 0 : 2) * (size_t)T * ex.H);
   L.o_f32 = mode == MOE_CHECK_F32 || T <= moe::kF32SlotMaxTokens;
   L.o = off;       off = align_up(off + (L.o_f32 ? 4 : 2) * A * (size_t)ex.H);
   L.total = off;
@@ -117,7 +118,7 @@ int moe_experts_create(moe_experts** out, int32_t qtype, int32_t E, int32_t has_
   if (qtype != MOE_Q2 && qtype != MOE_Q3) return MOE_ERR_INVALID_ARG;
   if (E < 1 || (has_shared != 0 && has_shared != 1) || H < 64 || I < 64) return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_E) return MOE_ERR_UNSUPPORTED;
-  if (H % 64 || I % 64) return MOE_ERR_UNSUPPORTED;
+  if (!moe::mfma_supported(H, I)) return MOE_ERR_UNSUPPORTED;
   if (!codes || !dm || (qtype == MOE_Q3) != (hi != nullptr)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(codes) || !aligned16(dm) || (hi && !aligned16(hi))) return MOE_ERR_INVALID_ARG;
   moe_experts* ex = new (std::nothrow) moe_experts;
@@ -174,6 +175,7 @@ int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, c
   a.gates = gates;
   a.y = y;
   a.h = at(ws, L.h);
+  a.x16 = reinterpret_cast<uint16_t*>(at(ws, L.x16));
   if (given == 4) {
     a.counts = counts;
     a.offsets = offsets;

@@ -36,7 +36,7 @@ __host__ __device__ inline size_t blk_down(const Experts& x, int e) {
 // Experts with 1..kGemvMaxTokens assignments take the GEMV kernels (weights
 // streamed once, codes kept exact); the rest take the MFMA tile kernels.
 constexpr int kGemvMaxTokens = 4;
-constexpr int kTileM = 64;  // assignments per MFMA tile
+constexpr int kTileM = 64;  // assignments per tile of the fp32 check kernels
 // Up to this many tokens the per-assignment expert outputs are kept in fp32;
 // above it in bf16 (half the traffic of the combine).
 constexpr int kF32SlotMaxTokens = 256;
@@ -87,6 +87,7 @@ struct FfnArgs {
   int out_f32;     // y is float32
   int gmax;        // GEMV token limit (0: every expert takes the MFMA tiles)
   void* h;         // [A][I] intermediate (fp32 check; bf16 GEMV / fp16 MFMA rows fast)
+  uint16_t* x16;   // [T][H] fp16 copy of x (fast mode, MFMA tiles)
   float* o;        // [A][H] fp32 gate-scaled expert outputs (check mode; fast, few tokens)
   uint16_t* ob;    // [A][H] bf16 gate-scaled expert outputs (fast, many tokens)
 };
@@ -99,6 +100,9 @@ hipError_t launch_window(const float* logits, int T, int k, const Experts& ex, c
                          int xdtype, int32_t* idx, float* gates, void* y, int out_f32, void* ws,
                          hipStream_t s);
 hipError_t launch_ffn_fast(const Experts& ex, const FfnArgs& a, hipStream_t s);
+// MFMA tiles of fast mode (experts with more than gmax assignments); writes x16.
+bool mfma_supported(int H, int I);
+hipError_t launch_mfma(const Experts& ex, const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(const Experts& ex, const FfnArgs& a, hipStream_t s);
 
 }  // namespace moe

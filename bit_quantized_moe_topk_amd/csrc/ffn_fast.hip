@@ -135,16 +135,6 @@ __global__ __launch_bounds__(kThreads) void gemv_gateup(Experts ex, FfnArgs a) {
 
 // Output of one expert row for one assignment: gate * value, stored per slot
 // (fp32 for few tokens, bf16 for many) for the combine kernel.
-__device__ inline void emit(const Experts& ex, const FfnArgs& a, int slot, int row, float val) {
-  if (a.o) a.o[(size_t)slot * ex.H + row] = val;
-  else a.ob[(size_t)slot * ex.H + row] = (uint16_t)f32_to_bf16_bits(val);
-}
-
-__device__ inline float gate_of(const FfnArgs& a, int slot) {
-  const int asg = a.perm[slot];
-  return asg < a.T * a.k ? a.gates[asg] : 1.0f;
-}
-
 // Decode GEMV, down projection with the gate folded in, one wave: RW rows of H
 // from row r0w for MP >= M token slots.
 template <int BPR, int MP, int Q>
@@ -212,180 +202,6 @@ __global__ __launch_bounds__(kThreads) void gemv_down(Experts ex, FfnArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// MFMA tiles.
-constexpr int kTN = 64;      // output rows per tile
-constexpr int kTK = 64;      // K per step (two blocks)
-constexpr int kLdsRow = 72;  // fp16 elements per LDS row (64 + 8 pad: 144 B stride)
-
-__device__ inline uint32_t pack_half2(float lo, float hi) {
-  const half2_t v = {(_Float16)lo, (_Float16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Dequantise one 32-weight block to fp16 and store it at dst (LDS, 64 bytes).
-template <int Q>
-__device__ inline void deq_block_to_lds(const QBlock& b, _Float16* dst) {
-  const float d = half_lo(b.dm), m = half_hi(b.dm);
-  uint32_t out[16];
-#pragma unroll
-  for (int j = 0; j < 32; j += 2) {
-    const uint32_t cw = j < 16 ? b.c0 : b.c1;
-    int q0 = (cw >> (2 * (j & 15))) & 3, q1 = (cw >> (2 * ((j + 1) & 15))) & 3;
-    if (Q == 3) {
-      q0 |= ((b.hi >> j) & 1) << 2;
-      q1 |= ((b.hi >> (j + 1)) & 1) << 2;
-    }
-    out[j / 2] = pack_half2(fmaf(d, (float)q0, m), fmaf(d, (float)q1, m));
-  }
-  uint4* d4 = reinterpret_cast<uint4*>(dst);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) d4[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-}
-
-__device__ inline half8_t lds_frag(const _Float16* base) {
-  return *reinterpret_cast<const half8_t*>(base);
-}
-
-// Gate + up + SwiGLU. Workgroup tile: 64 assignments x 64 rows of I (gate and
-// up: 128 weight rows). Wave w: assignments 32*(w&1).., rows 32*(w>>1)..
-template <int Q, bool XF32>
-__global__ __launch_bounds__(kThreads) void mfma_gateup(Experts ex, FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 xs[kTileM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) _Float16 ws[2 * kTN * kLdsRow];
-  __shared__ WorkMap wm;
-  workmap_init(wm, a.counts, ex.E_tot, a.gmax);
-  const int n_nt = ex.I / kTN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int th = wave & 1, rh = wave >> 1;
-  _Float16* hbuf = static_cast<_Float16*>(a.h);
-  for (int item = blockIdx.x; item < wm.n_tiles * n_nt; item += gridDim.x) {
-    int tl;
-    const int e = workmap_tile(wm, ex.E_tot, item / n_nt, tl);
-    const int n0 = (item % n_nt) * kTN;
-    const int m0 = tl * kTileM;
-    const int M = a.counts[e] - m0;
-    const int slot0 = a.offsets[e] + m0;
-    const int xr = tid >> 2, xq = tid & 3;  // x loader: row xr, 16 K-elements at 16*xq
-    int tok = -1;
-    if (xr < M) {
-      tok = token_of(a.perm[slot0 + xr], a.T, a.k);
-      if ((unsigned)tok >= (unsigned)a.T) tok = -1;
-    }
-    const int wr = tid >> 1, wb = tid & 1;  // weight loader: row wr (0..127), block wb
-    const size_t wblk0 = (wr < kTN ? blk_gate(ex, e) : blk_up(ex, e)) +
-                         (size_t)(n0 + (wr & (kTN - 1))) * (ex.H / 32) + wb;
-    float16_t acc_g = {}, acc_u = {};
-    for (int k0 = 0; k0 < ex.H; k0 += kTK) {
-      uint32_t xv[8];
-      if (tok >= 0) {
-        if (XF32) {
-          const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) +
-                                                              (size_t)tok * ex.H + k0 + 16 * xq);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 f = src[i];
-            xv[2 * i] = pack_half2(f.x, f.y);
-            xv[2 * i + 1] = pack_half2(f.z, f.w);
-          }
-        } else {
-          const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) +
-                                                            (size_t)tok * ex.H + k0 + 16 * xq);
-          const uint4 q0 = src[0], q1 = src[1];
-          const uint32_t r[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) xv[i] = pack_half2(bf16_lo(r[i]), bf16_hi(r[i]));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xv[i] = 0u;
-      }
-      const QBlock qb = load_qblock<Q>(ex, wblk0 + k0 / 32);
-      __syncthreads();  // previous step's fragments consumed
-      {
-        uint4* dst = reinterpret_cast<uint4*>(xs + xr * kLdsRow + 16 * xq);
-        dst[0] = make_uint4(xv[0], xv[1], xv[2], xv[3]);
-        dst[1] = make_uint4(xv[4], xv[5], xv[6], xv[7]);
-      }
-      deq_block_to_lds<Q>(qb, ws + wr * kLdsRow + 32 * wb);
-      __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < kTK; kk += 16) {
-        const int kc = kk + 8 * (lane >> 5);
-        const half8_t af = lds_frag(xs + (32 * th + (lane & 31)) * kLdsRow + kc);
-        const half8_t bg = lds_frag(ws + (32 * rh + (lane & 31)) * kLdsRow + kc);
-        const half8_t bu = lds_frag(ws + (kTN + 32 * rh + (lane & 31)) * kLdsRow + kc);
-        acc_g = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bg, acc_g, 0, 0, 0);
-        acc_u = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bu, acc_u, 0, 0, 0);
-      }
-    }
-    // acc[i] -> assignment 8*(i/4) + 4*(lane/32) + i%4, row lane%32
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mm = 32 * th + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (mm < M) {
-        const int row = n0 + 32 * rh + (lane & 31);
-        hbuf[(size_t)(slot0 + mm) * ex.I + row] = (_Float16)silu_mul(acc_g[i], acc_u[i]);
-      }
-    }
-  }
-}
-
-// Down projection, gate * Wd h. Tile: 64 assignments x 64 rows of H.
-template <int Q>
-__global__ __launch_bounds__(kThreads) void mfma_down(Experts ex, FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 xs[kTileM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) _Float16 ws[kTN * kLdsRow];
-  __shared__ WorkMap wm;
-  workmap_init(wm, a.counts, ex.E_tot, a.gmax);
-  const int n_nt = ex.H / kTN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int th = wave & 1, rh = wave >> 1;
-  const _Float16* hbuf = static_cast<const _Float16*>(a.h);
-  for (int item = blockIdx.x; item < wm.n_tiles * n_nt; item += gridDim.x) {
-    int tl;
-    const int e = workmap_tile(wm, ex.E_tot, item / n_nt, tl);
-    const int n0 = (item % n_nt) * kTN;
-    const int m0 = tl * kTileM;
-    const int M = a.counts[e] - m0;
-    const int slot0 = a.offsets[e] + m0;
-    const int xr = tid >> 2, xq = tid & 3;
-    const int wr = (tid >> 1) & (kTN - 1), wb = tid & 1;  // threads >= 128 only load x
-    const size_t wblk0 = blk_down(ex, e) + (size_t)(n0 + wr) * (ex.I / 32) + wb;
-    float16_t acc = {};
-    for (int k0 = 0; k0 < ex.I; k0 += kTK) {
-      uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
-      if (xr < M) {
-        const uint4* src = reinterpret_cast<const uint4*>(hbuf + (size_t)(slot0 + xr) * ex.I + k0 + 16 * xq);
-        x0 = src[0];
-        x1 = src[1];
-      }
-      QBlock qb;
-      if (tid < 2 * kTN) qb = load_qblock<Q>(ex, wblk0 + k0 / 32);
-      __syncthreads();
-      {
-        uint4* dst = reinterpret_cast<uint4*>(xs + xr * kLdsRow + 16 * xq);
-        dst[0] = x0;
-        dst[1] = x1;
-      }
-      if (tid < 2 * kTN) deq_block_to_lds<Q>(qb, ws + wr * kLdsRow + 32 * wb);
-      __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < kTK; kk += 16) {
-        const int kc = kk + 8 * (lane >> 5);
-        const half8_t af = lds_frag(xs + (32 * th + (lane & 31)) * kLdsRow + kc);
-        const half8_t bf = lds_frag(ws + (32 * rh + (lane & 31)) * kLdsRow + kc);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, acc, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mm = 32 * th + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (mm < M) emit(ex, a, slot0 + mm, n0 + 32 * rh + (lane & 31), gate_of(a, slot0 + mm) * acc[i]);
-    }
-  }
-}
-
 inline int grid_for(long max_items, int cap) {
   return (int)(max_items < cap ? (max_items > 0 ? max_items : 1) : cap);
 }
@@ -395,7 +211,6 @@ template <int Q, bool XF32>
 hipError_t launch_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   const int A = a.T * (a.k + ex.has_shared);
   const long max_gemv = A < ex.E_tot ? A : ex.E_tot;
-  const long max_tiles = A / kTileM + ex.E_tot + 1;
   const int bpr_h = ex.H / 32, bpr_i = ex.I / 32;
   const bool gemv = a.gmax > 0;
   const bool mfma = a.T > a.gmax;  // an expert holds at most T assignments
@@ -414,12 +229,10 @@ hipError_t launch_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   if (gemv) {
     switch (bpr_h) { GU(4) GU(8) GU(16) GU(32) GU(64) default: return hipErrorInvalidValue; }
   }
-  if (mfma)
-    MOE_LAUNCH("mfma_gateup", s, (mfma_gateup<Q, XF32>), dim3(grid_for(max_tiles * (ex.I / kTN), 4096)),
-               dim3(kThreads), 0, s, ex, a);
-  if (mfma)
-    MOE_LAUNCH("mfma_down", s, (mfma_down<Q>), dim3(grid_for(max_tiles * (ex.H / kTN), 4096)),
-               dim3(kThreads), 0, s, ex, a);
+  if (mfma) {
+    const hipError_t e = launch_mfma(ex, a, s);
+    if (e != hipSuccess) return e;
+  }
   if (gemv) {
     switch (bpr_i) { DN(4) DN(8) DN(16) DN(32) DN(64) default: return hipErrorInvalidValue; }
   }

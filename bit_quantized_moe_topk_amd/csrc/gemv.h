@@ -187,4 +187,21 @@ struct LaneReduce {
   }
 };
 
+// fp32 pair -> packed fp16 pair (round to nearest even).
+__device__ inline uint32_t pack_half2(float lo, float hi) {
+  const half2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Gate-scaled expert output of one assignment slot and output row.
+__device__ inline void emit(const Experts& ex, const FfnArgs& a, int slot, int row, float val) {
+  if (a.o) a.o[(size_t)slot * ex.H + row] = val;
+  else a.ob[(size_t)slot * ex.H + row] = (uint16_t)f32_to_bf16_bits(val);
+}
+
+__device__ inline float gate_of(const FfnArgs& a, int slot) {
+  const int asg = a.perm[slot];
+  return asg < a.T * a.k ? a.gates[asg] : 1.0f;
+}
+
 }  // namespace moe

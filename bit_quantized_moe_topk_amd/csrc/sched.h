@@ -4,7 +4,7 @@
 // the grouping's per-expert counts into LDS once, turns them into two prefix
 // sums, and maps each of its item numbers to work by binary search:
 //   GEMV experts: 1 .. gmax assignments, one unit per expert;
-//   MFMA tiles  : experts with more than gmax assignments, ceil(M / kTileM)
+//   MFMA tiles  : experts with more than gmax assignments, ceil(M / tile_m)
 //                 token tiles each.
 // Only experts that a token picked get work, as in the pages' prefill, which
 // multiplies only the routed experts ("Strata - the details", "Faster
@@ -62,11 +62,11 @@ struct WorkMap {
 };
 
 __device__ inline void workmap_init(WorkMap& wm, const int32_t* __restrict__ counts, int E_tot,
-                                    int gmax) {
+                                    int gmax, int tile_m = kTileM) {
   for (int e = threadIdx.x; e < E_tot; e += blockDim.x) {
     const int M = counts[e];
     wm.gbase[e] = (M >= 1 && M <= gmax) ? 1 : 0;
-    wm.tbase[e] = M > gmax ? (M + kTileM - 1) / kTileM : 0;
+    wm.tbase[e] = M > gmax ? (M + tile_m - 1) / tile_m : 0;
   }
   __syncthreads();
   const int ng = block_exclusive_scan(wm.gbase, E_tot, wm.wsum);

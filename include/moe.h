@@ -134,9 +134,11 @@ int moe_route_group(const float *logits, int32_t T, int32_t E, int32_t k, int32_
  *          32-bit word is bit 2 of code j. Pass NULL for Q2.
  *   dm   : NB * 2 uint16 per expert: fp16 bits of d, then of m, per block.
  *   Weight value: w = d*q + m.
- * Plane bases must be 16-byte aligned. Requires H, I multiples of 64 (the
- * matrix-core tile), 1 <= E <= MOE_MAX_E. The decode GEMV kernels cover
- * H/32 and I/32 in {4, 8, 16, 32, 64}; other shapes run every expert on the
+ * Plane bases must be 16-byte aligned. Requires H a multiple of 256 and I a
+ * multiple of 128 (the matrix-core tile: 256 output rows of the down
+ * projection, 128 rows each of gate and up), 1 <= E <= MOE_MAX_E; other
+ * shapes return MOE_ERR_UNSUPPORTED. The decode GEMV kernels cover H/32 and
+ * I/32 in {4, 8, 16, 32, 64}; other shapes run every expert on the
  * matrix-core tiles. */
 typedef struct moe_experts moe_experts;
 
