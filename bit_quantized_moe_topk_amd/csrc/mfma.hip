@@ -5,18 +5,21 @@
 // tile and SwiGLU runs in the epilogue; the down projection folds the routing
 // gate into its epilogue. The pages' prompt path likewise multiplies quantised
 // experts in large chunks without first expanding them to FP16 in memory
-// ("Strata - the details", "Faster prompts"). Here each weight tile is
-// expanded only in LDS, once per workgroup tile, and fed to
-// v_mfma_f32_32x32x16_f16.
+// ("Strata - the details", "Faster prompts"). Here weights are expanded only
+// in registers, right before v_mfma_f32_32x32x16_f16 consumes them.
 //
-// Workgroup tile: kBM = 128 assignments x kBN = 256 weight rows (gate/up: 128
-// rows of I from each of gate and up; down: 256 rows of H), K in stages of 64
-// (two quantisation blocks). Eight waves split by role, two per SIMD:
-//   waves 0..3 (MFMA): each a 64 x 128 sub-tile, 8 MFMAs per 16 of K;
-//   waves 4..7 (load): gather the next stage's activation rows through the
-//     grouping permutation, load and dequantise the next stage's weight rows
-//     (w = d*q + m, one fp16 rounding), and write both to the other LDS buffer.
-// One barrier per stage hands a buffer from the loaders to the MFMA waves.
+// Workgroup tile: kBM = 128 assignments x NW * 64 weight rows, K in stages of
+// 64 (two quantisation blocks), NW = 8 waves (4 for narrow matrices), two
+// per SIMD. Each wave owns 64 weight rows for all 128 assignments: it loads
+// its own weight blocks and dequantises them straight into MFMA operand
+// registers (w = d*q + m, one fp16 rounding), so weights never touch LDS. The
+// activation tile is gathered through the grouping permutation by all waves
+// into double-buffered LDS and read by every wave.
+// K order: stage s of S = K/64 holds blocks s (lane half 0) and S + s (lane
+// half 1); within a 16-wide MFMA step kk, lane half h covers weights
+// 8 kk .. 8 kk + 7 of its block. So each lane dequantises one whole block per
+// weight row per stage, and its blocks for stages s, s + 1 are adjacent in
+// memory (one 16-byte code load per two stages).
 //
 // The grid is persistent. Work items are (expert tile, N tile) with the N
 // tiles of one expert tile adjacent; consecutive items go to workgroups of one
@@ -29,18 +32,8 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 128;          // assignments per tile
-constexpr int kBN = 256;          // weight rows per tile
 constexpr int kBK = 64;           // K per stage
 constexpr int kRow = 72;          // LDS row stride in halves (64 + 8 pad: 144 B)
-constexpr int kMThreads = 512;    // 4 MFMA waves + 4 loader waves
-constexpr int kLoadT = 256;       // loader threads
-constexpr int kDepth = 4;         // stages a loader has in flight (even)
-
-struct TileLds {
-  _Float16 x[2][kBM * kRow];
-  _Float16 w[2][kBN * kRow];
-};
-
 // --- dequantisation -------------------------------------------------------
 // Code pair -> fp16 pair: OR the codes into the mantissa of 1024 (exact
 // 1024 + q), subtract 1024 (exact), then one fused d*q + m.
@@ -50,113 +43,142 @@ __device__ inline uint32_t deq_pair(uint32_t t, half2_t d2, half2_t m2) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, d2, m2));
 }
 
-// 16 two-bit codes (code j at bits 2j of c) -> 8 fp16 pairs in natural order.
-// Byte j of c holds codes 4j..4j+3; byte j of c >> 2 holds 4j+1..4j+3. A byte
-// permute puts byte j of each in the two halves; masks pick codes (4j, 4j+1)
-// from bits 0-1 and (4j+2, 4j+3) from bits 4-5. hq: the third code bits
-// (Q3), bit j = code j's bit 2.
-template <int Q>
-__device__ inline void deq_word(uint32_t c, uint32_t hq, half2_t d2, half2_t m2, uint32_t* out) {
-  const uint32_t s = c >> 2;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t r = __builtin_amdgcn_perm(s, c, 0x0C000C00u | ((4u + j) << 16) | (uint32_t)j);
-    uint32_t t0 = r & 0x00030003u, t1 = (r >> 4) & 0x00030003u;
-    if (Q == 3) {
-      const uint32_t h = hq >> (4 * j);
-      t0 |= ((h & 1u) << 2) | ((h & 2u) << 17);
-      t1 |= (h & 4u) | ((h & 8u) << 15);
-    }
-    out[2 * j] = deq_pair(t0, d2, m2);
-    out[2 * j + 1] = deq_pair(t1, d2, m2);
-  }
-}
+__device__ inline half8_t frag(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
 
-// Two consecutive blocks of one weight row (64 weights) -> 64 fp16 in LDS.
-template <int Q>
-__device__ inline void deq_stage(uint4 c, uint2 hi, uint2 dm, _Float16* dst) {
-  uint4* d4 = reinterpret_cast<uint4*>(dst);
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const uint32_t dmb = b ? dm.y : dm.x;
-    const half2_t d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dmb, dmb, 0x01000100u));
-    const half2_t m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dmb, dmb, 0x03020302u));
-    const uint32_t c0 = b ? c.z : c.x, c1 = b ? c.w : c.y;
-    const uint32_t h = Q == 3 ? (b ? hi.y : hi.x) : 0u;
-    uint32_t o[16];
-    deq_word<Q>(c0, h, d2, m2, o);
-    deq_word<Q>(c1, h >> 16, d2, m2, o + 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      d4[4 * b + i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-  }
-}
-
-// --- loader role ------------------------------------------------------------
-// Per stage a loader thread fetches 4 activation chunks (rows xrow + 32 i,
-// 8 halves at column 8 * xq) and one weight row's two blocks.
-struct Stage {
-  uint4 x[4];
-  uint4 c;
-  uint2 hi, dm;
+// Two consecutive quantisation blocks of one weight row (the blocks a lane
+// needs for two consecutive stages): codes, third bits (Q3), d and m.
+struct WPair {
+  uint4 c;   // block 0: c.x, c.y; block 1: c.z, c.w
+  uint2 hi;  // Q3 third bits of blocks 0, 1
+  uint2 dm;  // fp16 d | m << 16 of blocks 0, 1
 };
 
 template <int Q>
-__device__ inline void load_stage(const Experts& ex, const uint16_t* __restrict__ a16, int lda,
-                                  const int (&arow)[4], int xq, size_t wblk, int k0, Stage& st) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (arow[i] >= 0)
-      st.x[i] = *reinterpret_cast<const uint4*>(a16 + (size_t)arow[i] * lda + k0 + 8 * xq);
-    else
-      st.x[i] = make_uint4(0, 0, 0, 0);
-  }
-  const size_t blk = wblk + k0 / 32;
-  st.c = *reinterpret_cast<const uint4*>(ex.codes + blk * 8);
-  st.dm = *reinterpret_cast<const uint2*>(ex.dm + blk * 2);
-  st.hi = Q == 3 ? *reinterpret_cast<const uint2*>(ex.hi + blk * 4) : make_uint2(0, 0);
+__device__ inline WPair load_wpair(const Experts& ex, size_t blk) {
+  WPair w;
+  w.c = *reinterpret_cast<const uint4*>(ex.codes + blk * 8);
+  w.dm = *reinterpret_cast<const uint2*>(ex.dm + blk * 2);
+  w.hi = Q == 3 ? *reinterpret_cast<const uint2*>(ex.hi + blk * 4) : make_uint2(0, 0);
+  return w;
 }
+
+// MFMA K order inside each group of four weights: positions 0, 1, 2, 3 hold
+// weights 0, 2, 1, 3. Both operands follow it: the fp16 activation copy and the
+// SwiGLU output are stored that way, so each products' sum is unchanged.
+//
+// Q2 operands: byte j of e = c & 0x33333333 holds codes 4j (low nibble) and
+// 4j + 2 (high nibble), and byte j of o = (c >> 2) & 0x33333333 holds codes
+// 4j + 1 and 4j + 3, each as an FP4 E2M1 value q / 2. One scaled conversion
+// (scale 2) turns a byte into the exact fp16 pair (q, q'), then one fused
+// d*q + m rounds once.
+//
+// Q3 operands: a byte permute puts byte j of c and of c >> 2 in the two halves
+// of a word; masks pick codes (4j, 4j + 1) from bits 0-1 and (4j + 2, 4j + 3)
+// from bits 4-5, OR in the third bits, and OR-ing into the mantissa of 1024
+// gives 1024 + q exactly; subtracting 1024 and one fused d*q + m follow, and a
+// final permute brings the pairs into the K order above.
+struct WStage {
+  uint32_t w0, w1, w2, w3;  // Q2: e, o of code words 0, 1; Q3: codes 0, 1, third bits
+  half2_t d2, m2;
+};
 
 template <int Q>
-__device__ inline void store_stage(const Stage& st, int tl, _Float16* xs, _Float16* ws) {
-  const int xrow = tl >> 3, xq = tl & 7;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(xs + (xrow + 32 * i) * kRow + 8 * xq) = st.x[i];
-  deq_stage<Q>(st.c, st.hi, st.dm, ws + tl * kRow);
+__device__ inline WStage wstage(const WPair& w, int b) {
+  WStage st;
+  const uint32_t c0 = b ? w.c.z : w.c.x, c1 = b ? w.c.w : w.c.y;
+  if (Q == 2) {
+    st.w0 = c0 & 0x33333333u;
+    st.w1 = (c0 >> 2) & 0x33333333u;
+    st.w2 = c1 & 0x33333333u;
+    st.w3 = (c1 >> 2) & 0x33333333u;
+  } else {
+    st.w0 = c0;
+    st.w1 = c1;
+    st.w2 = b ? w.hi.y : w.hi.x;
+    st.w3 = 0u;
+  }
+  const uint32_t dm = b ? w.dm.y : w.dm.x;
+  st.d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
+  st.m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
+  return st;
 }
 
-// --- MFMA role --------------------------------------------------------------
-__device__ inline half8_t frag(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
+// Byte j of w as two FP4 E2M1 values, times 2, in fp16 (j is a constant after
+// unrolling; the instruction takes it as an immediate).
+__device__ inline half2_t fp4x2_to_f16(uint32_t w, int j) {
+  switch (j) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 3);
+  }
+}
 
-// One stage for an MFMA wave: weight rows brow[j] + lane%32 (the MFMA's row
-// operand) times activation rows 64 mh + 32 i + lane%32 (its column operand);
-// the 32-row half i = 1 is skipped when it lies at or past M.
-__device__ inline void mma_stage(const _Float16* xs, const _Float16* ws, int mh, bool live1,
-                                 const int (&brow)[4], float16_t (&acc)[2][4]) {
-  const int lane = threadIdx.x & 63;
+// Weights 8 kk .. 8 kk + 7 of the stage's block as an MFMA operand.
+template <int Q>
+__device__ inline half8_t wfrag(const WStage& w, int kk) {
+  uint32_t o[4];
+  if (Q == 2) {
+    const uint32_t e = kk < 2 ? w.w0 : w.w2, od = kk < 2 ? w.w1 : w.w3;
 #pragma unroll
-  for (int kk = 0; kk < kBK; kk += 16) {
-    const int kc = kk + 8 * (lane >> 5);
-    half8_t b[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = frag(ws + (brow[j] + (lane & 31)) * kRow + kc);
-    const half8_t a0 = frag(xs + (64 * mh + (lane & 31)) * kRow + kc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a0, acc[0][j], 0, 0, 0);
-    if (live1) {
-      const half8_t a1 = frag(xs + (64 * mh + 32 + (lane & 31)) * kRow + kc);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a1, acc[1][j], 0, 0, 0);
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * (kk & 1) + u;
+      const half2_t qa = fp4x2_to_f16(e, j), qb = fp4x2_to_f16(od, j);
+      o[2 * u] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qa, w.d2, w.m2));
+      o[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qb, w.d2, w.m2));
     }
+  } else {
+    const uint32_t cw = kk < 2 ? w.w0 : w.w1, hq = kk < 2 ? w.w2 : w.w2 >> 16;
+    const uint32_t s = cw >> 2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t j = 2 * (kk & 1) + u;  // byte of cw: codes 4j .. 4j + 3
+      const uint32_t r = __builtin_amdgcn_perm(s, cw, 0x0C000C00u | ((4u + j) << 16) | j);
+      uint32_t t0 = r & 0x00030003u, t1 = (r >> 4) & 0x00030003u;
+      const uint32_t hb = hq >> (4 * j);
+      t0 |= ((hb & 1u) << 2) | ((hb & 2u) << 17);
+      t1 |= (hb & 4u) | ((hb & 8u) << 15);
+      const uint32_t p01 = deq_pair(t0, w.d2, w.m2), p23 = deq_pair(t1, w.d2, w.m2);
+      o[2 * u] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);      // weights 0, 2
+      o[2 * u + 1] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);  // weights 1, 3
+    }
+  }
+  return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// One stage of an MFMA wave over NI 32-row activation groups: activation
+// fragments are read one MFMA step ahead and each step's weight operands are
+// dequantised while the previous step's MFMAs run.
+template <int NI, int Q>
+__device__ inline void stage_mma(const _Float16* xb, const WStage (&w)[2],
+                                 float16_t (&acc)[4][2]) {
+  const int lane = threadIdx.x & 63;
+  const _Float16* ap = xb + (lane & 31) * kRow + 32 * (lane >> 5);
+  half8_t af[2][NI], bf[2][2];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) af[0][i] = frag(ap + 32 * i * kRow);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) bf[0][j] = wfrag<Q>(w[j], 0);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int c = kk & 1, n = c ^ 1;
+    if (kk < 3) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) af[n][i] = frag(ap + 32 * i * kRow + 8 * (kk + 1));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[n][j] = wfrag<Q>(w[j], kk + 1);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[c][j], af[c][i], acc[i][j], 0, 0, 0);
   }
 }
 
 // Logical item of this workgroup in round r: consecutive items share an XCD
 // (workgroup g runs on XCD g % 8) when the grid is a multiple of 8.
-__device__ inline long item_of(long r) {
+__device__ inline int item_of(int r) {
   const int g = blockIdx.x, G = gridDim.x;
   if (G % 8) return r * G + g;
   return r * G + (g % 8) * (G / 8) + g / 8;
@@ -166,140 +188,197 @@ struct TileInfo {
   int e, nt, M, slot0;
 };
 
+// Wave-uniform description of work item `item` (values read from LDS are
+// moved to scalar registers).
 __device__ inline TileInfo tile_info(const WorkMap& wm, const int* offs, int E_tot, int n_nt,
-                                     long item) {
+                                     int item) {
   int tl;
   TileInfo t;
-  t.e = workmap_tile(wm, E_tot, (int)(item / n_nt), tl);
-  t.nt = (int)(item % n_nt);
+  const int e = workmap_tile(wm, E_tot, item / n_nt, tl);
+  t.e = __builtin_amdgcn_readfirstlane(e);
+  t.nt = item % n_nt;
   const int m0 = tl * kBM;
-  t.M = min(kBM, offs[t.e + 1] - offs[t.e] - m0);
-  t.slot0 = offs[t.e] + m0;
+  t.M = __builtin_amdgcn_readfirstlane(min(kBM, offs[e + 1] - offs[e] - m0));
+  t.slot0 = __builtin_amdgcn_readfirstlane(offs[e] + m0);
   return t;
 }
 
-// DOWN = false: gate/up + SwiGLU -> h (fp16, grouped order, [A][I]).
+// Output rows of one workgroup tile: gate/up: 32 NW rows of I from each of
+// gate and up; down: 64 NW rows of H.
+template <bool DOWN, int NW>
+constexpr int tile_rows() { return DOWN ? 64 * NW : 32 * NW; }
+
+// DOWN = false: gate/up + SwiGLU -> h (fp16, grouped order, [A][I], each
+//               group of four rows of I in the MFMA K order).
 // DOWN = true : gate * (W_d h) -> per-slot outputs.
 //
-// Loader waves run a flat sequence of (tile, stage) loads kDepth stages ahead
-// of the LDS stores (kDepth register sets; stage i lands in LDS buffer i & 1);
-// the grouping permutation entries of the next tile are fetched a tile ahead.
-template <int Q, bool DOWN>
-__global__ __launch_bounds__(kMThreads) void mfma_tiles(Experts ex, FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) TileLds L;
+// NW waves, each owning 64 weight rows (gate/up: 32 gate + 32 up rows, so
+// SwiGLU is local) for all kBM activation rows of the tile. Every wave also
+// loads a share of the activation tile. Loads follow the stage sequence of all
+// of the workgroup's tiles through two cursors, so they run on across tile
+// boundaries: activations two stages ahead of their LDS stores (stage g lives
+// in LDS buffer g & 1), weight blocks one stage pair ahead. One barrier per
+// stage.
+template <int Q, bool DOWN, int NW>
+__global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
+  constexpr int NT = 64 * NW;                 // threads
+  constexpr int CH = kBM * (kBK / 8) / NT;    // 16-byte activation chunks per thread per stage
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][kBM * kRow];
   __shared__ WorkMap wm;
   __shared__ int offs[MOE_MAX_E_DEV + 2];
-  for (int e = threadIdx.x; e <= ex.E_tot; e += blockDim.x) offs[e] = a.offsets[e];
+  for (int e = threadIdx.x; e <= ex.E_tot; e += NT) offs[e] = a.offsets[e];
   workmap_init(wm, a.counts, ex.E_tot, a.gmax, kBM);
   const int K = DOWN ? ex.I : ex.H;
-  const int n_nt = DOWN ? ex.H / kBN : ex.I / (kBN / 2);
-  const long n_items = (long)wm.n_tiles * n_nt;
+  const int n_nt = (DOWN ? ex.H : ex.I) / tile_rows<DOWN, NW>();
+  const int n_items = wm.n_tiles * n_nt;
   const int S = K / kBK;  // even: H % 256 == 0, I % 128 == 0
-  const long first = item_of(0);
-  const int n_my = first < n_items ? (int)((n_items - first + gridDim.x - 1) / gridDim.x) : 0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int first = item_of(0);
+  const int n_my = first < n_items ? (n_items - first + gridDim.x - 1) / gridDim.x : 0;
+  if (n_my == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const uint16_t* a16 = DOWN ? static_cast<const uint16_t*>(a.h) : a.x16;
 
-  if (tid >= kMThreads - kLoadT) {
-    // ---- loader ----
-    const int tl = tid - (kMThreads - kLoadT), xr = tl >> 3, xq = tl & 7;
-    const uint16_t* a16 = DOWN ? static_cast<const uint16_t*>(a.h) : a.x16;
-    int arow[4], nxt[4];
-    size_t wblk = 0;
-    TileInfo tn{};
-    auto prep = [&](int r) {  // tile r's info and permutation entries, not yet waited on
-      tn = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
+  // ---- activation cursor: chunk tid + NT u = row (c >> 3), LDS column 8 (c & 7) ----
+  // LDS column 8 q of stage s holds K column 32 (s + S (q / 4)) + 8 (q % 4).
+  const uint4* xptr[CH];  // next stage's source chunk (null: row past M)
+  int anext[CH];
+  int xt = 0, xsg = 0;    // tile round and stage of the next activation load
+  auto xprep = [&](int r) {  // tile r's rows: permutation entries, not yet waited on
+    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = xr + 32 * i;
-        nxt[i] = m >= tn.M ? -1 : (DOWN ? tn.slot0 + m : a.perm[tn.slot0 + m]);
-      }
-    };
-    auto fin = [&]() {  // make the prepared tile the one being loaded
+    for (int u = 0; u < CH; ++u) {
+      const int m = (tid + NT * u) >> 3;
+      anext[u] = m >= t.M ? -1 : (DOWN ? t.slot0 + m : a.perm[t.slot0 + m]);
+    }
+  };
+  auto xfin = [&]() {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int r = nxt[i];
-        if (!DOWN && r >= 0) {
-          r = token_of(r, a.T, a.k);
-          r = (unsigned)r < (unsigned)a.T ? r : -1;
-        }
-        arow[i] = r;
+    for (int u = 0; u < CH; ++u) {
+      int r = anext[u];
+      if (!DOWN && r >= 0) {
+        r = token_of(r, a.T, a.k);
+        r = (unsigned)r < (unsigned)a.T ? r : -1;
       }
+      const int q = (tid + NT * u) & 7;
+      xptr[u] = r < 0 ? nullptr
+                      : reinterpret_cast<const uint4*>(a16 + (size_t)r * K + 32 * S * (q >> 2) + 8 * (q & 3));
+    }
+  };
+  auto xload = [&](uint4 (&v)[CH]) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      // rows past M (null source) stay zero and are never loaded
+      v[u] = xptr[u] ? *xptr[u] : make_uint4(0, 0, 0, 0);
+      if (xptr[u]) xptr[u] += 4;  // 32 halves: the next stage
+    }
+    if (++xsg == S) {
+      xsg = 0;
+      if (++xt < n_my) {
+        xfin();
+        if (xt + 1 < n_my) xprep(xt + 1);
+      }
+    }
+  };
+  auto xstore = [&](const uint4 (&v)[CH], _Float16* buf) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int c = tid + NT * u;
+      *reinterpret_cast<uint4*>(buf + (c >> 3) * kRow + 8 * (c & 7)) = v[u];
+    }
+  };
+
+  // ---- weight cursor: rows wrow(j) + lane % 32, blocks h S + stage ----
+  int wt = 0, wp = 0;  // tile round and stage pair of the next weight load
+  const uint4* wc[2];  // next pair's codes, d/m and third bits per row j
+  const uint2 *wd[2], *wh[2];
+  auto wsetup = [&](int r) {
+    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      size_t blk;
       if (DOWN) {
-        wblk = blk_down(ex, tn.e) + (size_t)(tn.nt * kBN + tl) * (ex.I / 32);
+        const int row = t.nt * tile_rows<DOWN, NW>() + 64 * wave + 32 * j + (lane & 31);
+        blk = blk_down(ex, t.e) + (size_t)row * (ex.I / 32) + h * S;
       } else {
-        const int row = tn.nt * (kBN / 2) + (tl & (kBN / 2 - 1));
-        wblk = (tl < kBN / 2 ? blk_gate(ex, tn.e) : blk_up(ex, tn.e)) + (size_t)row * (ex.H / 32);
+        const int row = t.nt * tile_rows<DOWN, NW>() + 32 * wave + (lane & 31);
+        blk = (j ? blk_up(ex, t.e) : blk_gate(ex, t.e)) + (size_t)row * (ex.H / 32) + h * S;
       }
-    };
-    int lr = 0, ls = 0;  // tile round and stage of the next load
-    if (n_my > 0) {
-      prep(0);
-      fin();
-      if (n_my > 1) prep(1);
+      wc[j] = reinterpret_cast<const uint4*>(ex.codes + blk * 8);
+      wd[j] = reinterpret_cast<const uint2*>(ex.dm + blk * 2);
+      wh[j] = Q == 3 ? reinterpret_cast<const uint2*>(ex.hi + blk * 4) : nullptr;
     }
-    auto next_load = [&](Stage& st) {
-      load_stage<Q>(ex, a16, K, arow, xq, wblk, ls * kBK, st);
-      if (++ls == S) {
-        ls = 0;
-        if (++lr < n_my) {
-          fin();
-          if (lr + 1 < n_my) prep(lr + 1);
-        }
-      }
-    };
-    const int total = n_my * S;
-    Stage st[kDepth];
+  };
+  auto wload = [&](WPair (&w)[2]) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d)
-      if (d < total) next_load(st[d]);
-    for (int i = 0; i < total; i += kDepth) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        if (i + d < total) {
-          store_stage<Q>(st[d], tl, L.x[d & 1], L.w[d & 1]);
-          if (i + d + kDepth < total) next_load(st[d]);
-          __syncthreads();
-        }
-      }
+    for (int j = 0; j < 2; ++j) {
+      w[j].c = *wc[j]++;
+      w[j].dm = *wd[j]++;
+      w[j].hi = Q == 3 ? *wh[j]++ : make_uint2(0, 0);
     }
-    return;
-  }
+    if (++wp == S / 2) {
+      wp = 0;
+      if (++wt < n_my) wsetup(wt);
+    }
+  };
 
-  // ---- MFMA waves ----
-  const int mh = wave & 1, nq = wave >> 1;
-  int brow[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    brow[j] = DOWN ? 128 * nq + 32 * j : (j < 2 ? 64 * nq + 32 * j : 128 + 64 * nq + 32 * (j - 2));
+  const int total = n_my * S;
+  xprep(0);
+  xfin();
+  if (n_my > 1) xprep(1);
+  wsetup(0);
+  uint4 xa[CH], xb[CH];  // activation stages in flight: even stages in xa, odd in xb
+  WPair wq[2];           // the current stage pair's weight blocks
+  xload(xa);
+  xload(xb);             // total >= 2
+  wload(wq);
+  xstore(xa, xs[0]);
+  if (total > 2) xload(xa);
+  __syncthreads();
+
+  int g = 0;  // global stage index
   for (int r = 0; r < n_my; ++r) {
     const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
-    float16_t acc[2][4];
+    const int wrow0 = t.nt * tile_rows<DOWN, NW>() + (DOWN ? 64 : 32) * wave;
+    float16_t acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = float16_t{};
-    const bool live = 64 * mh < t.M, live1 = 64 * mh + 32 < t.M;
-    for (int s = 0; s < S; s += 2) {
+      for (int j = 0; j < 2; ++j) acc[i][j] = float16_t{};
+    for (int s = 0; s < S; s += 2, g += 2) {
+      // even stage g: LDS buffer 0, weight block 0 of the pair
+      WStage w[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) w[j] = wstage<Q>(wq[j], 0);
+      xstore(xb, xs[1]);             // stage g + 1 (total is even)
+      if (g + 3 < total) xload(xb);  // stage g + 3
+      stage_mma<4, Q>(xs[0], w, acc);
       __syncthreads();
-      if (live) mma_stage(L.x[0], L.w[0], mh, live1, brow, acc);
-      __syncthreads();
-      if (live) mma_stage(L.x[1], L.w[1], mh, live1, brow, acc);
+      // odd stage g + 1: LDS buffer 1, weight block 1
+#pragma unroll
+      for (int j = 0; j < 2; ++j) w[j] = wstage<Q>(wq[j], 1);
+      if (g + 2 < total) {
+        wload(wq);                   // stage pair g + 2, g + 3
+        xstore(xa, xs[0]);           // stage g + 2
+      }
+      if (g + 4 < total) xload(xa);  // stage g + 4
+      stage_mma<4, Q>(xs[1], w, acc);
+      if (s + 2 < S) __syncthreads();
     }
-    if (!live) continue;
-    // acc[i][j][v]: weight row brow[j] + 8 (v / 4) + 4 (lane / 32) + v % 4,
-    //               activation row 64 mh + 32 i + lane % 32
+    // ---- epilogue ----
+    // acc[i][j][v]: weight row wrow0 (+ 32 j for down) + 8 (v / 4) + 4 h + v % 4,
+    //               activation row 32 i + lane % 32
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int mm = 64 * mh + 32 * i + (lane & 31);
+    for (int i = 0; i < 4; ++i) {
+      const int mm = 32 * i + (lane & 31);
       if (mm >= t.M) continue;
       const int slot = t.slot0 + mm;
       if (DOWN) {
         const float gt = gate_of(a, slot);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const size_t off = (size_t)slot * ex.H + t.nt * kBN + brow[j] + 8 * q + 4 * (lane >> 5);
+            const size_t off = (size_t)slot * ex.H + wrow0 + 32 * j + 8 * q + 4 * h;
             const float v0 = gt * acc[i][j][4 * q], v1 = gt * acc[i][j][4 * q + 1];
             const float v2 = gt * acc[i][j][4 * q + 2], v3 = gt * acc[i][j][4 * q + 3];
             if (a.o) {
@@ -312,24 +391,23 @@ __global__ __launch_bounds__(kMThreads) void mfma_tiles(Experts ex, FfnArgs a) {
           }
         }
       } else {
-        _Float16* h = static_cast<_Float16*>(a.h) + (size_t)slot * ex.I + t.nt * (kBN / 2);
+        _Float16* hrow = static_cast<_Float16*>(a.h) + (size_t)slot * ex.I + wrow0;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = silu_mul(acc[i][j][4 * q + u], acc[i][j + 2][4 * q + u]);
-            *reinterpret_cast<uint2*>(h + brow[j] + 8 * q + 4 * (lane >> 5)) =
-                make_uint2(pack_half2(v[0], v[1]), pack_half2(v[2], v[3]));
-          }
+          for (int u = 0; u < 4; ++u) v[u] = silu_mul(acc[i][0][4 * q + u], acc[i][1][4 * q + u]);
+          *reinterpret_cast<uint2*>(hrow + 8 * q + 4 * h) =  // K order 0, 2, 1, 3
+              make_uint2(pack_half2(v[0], v[2]), pack_half2(v[1], v[3]));
         }
       }
     }
+    __syncthreads();
   }
 }
 
-// x -> fp16 copy, the activation operand of the gate/up tiles.
+// x -> fp16 copy, the activation operand of the gate/up tiles, in the MFMA K
+// order (each group of four stored as 0, 2, 1, 3).
 template <bool XF32>
 __global__ __launch_bounds__(256) void x_to_f16(const void* __restrict__ x, long n8,
                                                 uint16_t* __restrict__ x16) {
@@ -338,15 +416,16 @@ __global__ __launch_bounds__(256) void x_to_f16(const void* __restrict__ x, long
     if (XF32) {
       const float4* src = static_cast<const float4*>(x) + 2 * i;
       const float4 f0 = src[0], f1 = src[1];
-      o[0] = pack_half2(f0.x, f0.y);
-      o[1] = pack_half2(f0.z, f0.w);
-      o[2] = pack_half2(f1.x, f1.y);
-      o[3] = pack_half2(f1.z, f1.w);
+      o[0] = pack_half2(f0.x, f0.z);
+      o[1] = pack_half2(f0.y, f0.w);
+      o[2] = pack_half2(f1.x, f1.z);
+      o[3] = pack_half2(f1.y, f1.w);
     } else {
       const uint4 v = static_cast<const uint4*>(x)[i];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = pack_half2(bf16_lo(w[j]), bf16_hi(w[j]));
+      o[0] = pack_half2(bf16_lo(v.x), bf16_lo(v.y));
+      o[1] = pack_half2(bf16_hi(v.x), bf16_hi(v.y));
+      o[2] = pack_half2(bf16_lo(v.z), bf16_lo(v.w));
+      o[3] = pack_half2(bf16_hi(v.z), bf16_hi(v.w));
     }
     reinterpret_cast<uint4*>(x16)[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
@@ -360,23 +439,39 @@ hipError_t launch_q(const Experts& ex, const FfnArgs& a, int grid, hipStream_t s
     MOE_LAUNCH("x_to_f16", s, x_to_f16<true>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
   else
     MOE_LAUNCH("x_to_f16", s, x_to_f16<false>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
-  MOE_LAUNCH("mfma_gateup", s, (mfma_tiles<Q, false>), dim3(grid), dim3(kMThreads), 0, s, ex, a);
-  MOE_LAUNCH("mfma_down", s, (mfma_tiles<Q, true>), dim3(grid), dim3(kMThreads), 0, s, ex, a);
+  if (ex.I % tile_rows<false, 8>() == 0)
+    MOE_LAUNCH("mfma_gateup", s, (mfma_tiles<Q, false, 8>), dim3(grid), dim3(512), 0, s, ex, a);
+  else
+    MOE_LAUNCH("mfma_gateup", s, (mfma_tiles<Q, false, 4>), dim3(grid), dim3(256), 0, s, ex, a);
+  if (ex.H % tile_rows<true, 8>() == 0)
+    MOE_LAUNCH("mfma_down", s, (mfma_tiles<Q, true, 8>), dim3(grid), dim3(512), 0, s, ex, a);
+  else
+    MOE_LAUNCH("mfma_down", s, (mfma_tiles<Q, true, 4>), dim3(grid), dim3(256), 0, s, ex, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool mfma_supported(int H, int I) { return H % kBN == 0 && I % (kBN / 2) == 0; }
+bool mfma_supported(int H, int I) {
+  return H % tile_rows<true, 4>() == 0 && I % tile_rows<false, 4>() == 0;
+}
 
 hipError_t launch_mfma(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   const long A = (long)a.T * (a.k + ex.has_shared);
   const long max_tiles = A / kBM + ex.E_tot + 1;
-  const long max_items = max_tiles * (ex.H / kBN > ex.I / (kBN / 2) ? ex.H / kBN : ex.I / (kBN / 2));
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int grid = (int)(max_items < cus ? max_items : cus);
+  const long max_items = max_tiles * (ex.H / tile_rows<true, 4>() > ex.I / tile_rows<false, 4>()
+                                          ? ex.H / tile_rows<true, 4>()
+                                          : ex.I / tile_rows<false, 4>());
+  static int cus[64] = {0};  // compute units per device, read once
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  const int grid = (int)(max_items < cus[dev] ? max_items : cus[dev]);
   return ex.qtype == 3 ? launch_q<3>(ex, a, grid, s) : launch_q<2>(ex, a, grid, s);
 }
 
