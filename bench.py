@@ -280,6 +280,12 @@ def run_prefill(cfg, args):
     n_layers = args.prefill_layers or cfg.layers
     insts, _, keep = build_instances(cfg, n_layers, args.seed)
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if not args.no_tiled:  # weight copy in the matrix-core tile order, built at load time
+        t0 = time.time()
+        for it in insts:
+            it.ex.attach_tiled()
+        torch.cuda.synchronize()
+        log(f"prefill: tiled weight copies for {n_layers} layers in {time.time() - t0:.1f}s")
     for it in insts:           # warm-up: the whole stack once
         it.step(L, stream)
     torch.cuda.synchronize()
@@ -303,6 +309,7 @@ def run_prefill(cfg, args):
                     f"(hidden {cfg.H}, {cfg.E} routed + {cfg.shared} shared experts, top-{cfg.k}, "
                     f"intermediate {cfg.I}, Q{cfg.qtype}, bf16 activations)",
         "layers": n_layers,
+        "weights": "canonical planes" if args.no_tiled else "canonical planes + tiled copy",
         "ms_per_chunk": ms_stack,
         "ms_per_layer": ms_layer,
         "tokens_per_s_end_to_end": cfg.T / (ms_stack * 1e-3),
@@ -368,6 +375,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-layers", type=int, default=0, help="0 = all 48")
     ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--no-tiled", action="store_true",
+                    help="prefill on the canonical weight planes only (no tiled copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-layers", type=int, default=8)

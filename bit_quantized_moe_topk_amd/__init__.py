@@ -61,6 +61,10 @@ def lib() -> C.CDLL:
         L.moe_experts_create.restype = C.c_int
         L.moe_experts_destroy.argtypes = [P]
         L.moe_experts_destroy.restype = C.c_int
+        L.moe_experts_tiled_size.argtypes = [P]
+        L.moe_experts_tiled_size.restype = sz
+        L.moe_experts_attach_tiled.argtypes = [P, P, sz, P]
+        L.moe_experts_attach_tiled.restype = C.c_int
         L.moe_ffn_q_workspace_size.argtypes = [P, i32, i32, i32]
         L.moe_ffn_q_workspace_size.restype = sz
         L.moe_ffn_q.argtypes = [P, i32, i32, P, P, P, i32, P, P, P, P, P, i32, P, sz, P]
@@ -212,6 +216,21 @@ class Experts:
     @property
     def handle(self) -> C.c_void_p:
         return self._h
+
+    def attach_tiled(self) -> None:
+        """Build the tiled weight copy that the prefill matrix-core tiles read
+        (a device buffer as large as the planes, kept by this object)."""
+        import torch
+        nbytes = int(lib().moe_experts_tiled_size(self._h))
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=self._planes[0].device)
+        stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        _check("moe_experts_attach_tiled",
+               lib().moe_experts_attach_tiled(self._h, _ptr(buf), nbytes, stream))
+        self._tiled = buf
+
+    def detach_tiled(self) -> None:
+        _check("moe_experts_attach_tiled", lib().moe_experts_attach_tiled(self._h, None, 0, None))
+        self._tiled = None
 
     def workspace_size(self, T: int, k: int, mode: int = FAST) -> int:
         return int(lib().moe_ffn_q_workspace_size(self._h, T, k, mode))

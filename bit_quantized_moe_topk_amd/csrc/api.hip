@@ -121,7 +121,7 @@ int moe_experts_create(moe_experts** out, int32_t qtype, int32_t E, int32_t has_
   if (!moe::mfma_supported(H, I)) return MOE_ERR_UNSUPPORTED;
   if (!codes || !dm || (qtype == MOE_Q3) != (hi != nullptr)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(codes) || !aligned16(dm) || (hi && !aligned16(hi))) return MOE_ERR_INVALID_ARG;
-  moe_experts* ex = new (std::nothrow) moe_experts;
+  moe_experts* ex = new (std::nothrow) moe_experts();
   if (!ex) return MOE_ERR_INVALID_ARG;
   ex->d.qtype = qtype;
   ex->d.E = E;
@@ -139,6 +139,34 @@ int moe_experts_create(moe_experts** out, int32_t qtype, int32_t E, int32_t has_
 
 int moe_experts_destroy(moe_experts* ex) {
   delete ex;
+  return MOE_OK;
+}
+
+size_t moe_experts_tiled_size(const moe_experts* ex) {
+  if (!ex) return 0;
+  const moe::Experts& d = ex->d;
+  return (size_t)d.E_tot * d.nb * (8 + 4 + (d.qtype == MOE_Q3 ? 4 : 0));
+}
+
+int moe_experts_attach_tiled(moe_experts* ex, void* buf, size_t bytes, void* stream) {
+  if (!ex) return MOE_ERR_INVALID_ARG;
+  moe::Experts& d = ex->d;
+  if (!buf) {
+    d.t_codes = nullptr;
+    d.t_dm = nullptr;
+    d.t_hi = nullptr;
+    return MOE_OK;
+  }
+  if (!aligned16(buf) || bytes < moe_experts_tiled_size(ex)) return MOE_ERR_INVALID_ARG;
+  const size_t nblk = (size_t)d.E_tot * d.nb;
+  uint8_t* base = static_cast<uint8_t*>(buf);
+  moe::Experts t = d;
+  t.t_codes = base;
+  t.t_dm = reinterpret_cast<const uint16_t*>(base + nblk * 8);
+  t.t_hi = d.qtype == MOE_Q3 ? base + nblk * 12 : nullptr;
+  const hipError_t e = moe::launch_tile_weights(t, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  d = t;
   return MOE_OK;
 }
 

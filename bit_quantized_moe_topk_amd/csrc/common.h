@@ -21,7 +21,17 @@ struct Experts {
   const uint8_t* codes;  // [E_tot][nb][8]
   const uint8_t* hi;     // [E_tot][nb][4] (Q3) or nullptr
   const uint16_t* dm;    // [E_tot][nb][2] fp16 bits (d, m)
+  // Optional tiled copy for the matrix-core tiles (null when not attached):
+  // per (expert, matrix, 32-row group, block quad) a record of 64 lanes.
+  const uint8_t* t_codes;  // [E_tot][3][R][64][16]
+  const uint16_t* t_dm;    // [E_tot][3][R][64][4]
+  const uint8_t* t_hi;     // [E_tot][3][R][64][8] (Q3)
 };
+
+// Records per matrix of the tiled copy (32 rows x 4 blocks each).
+__host__ __device__ inline size_t tiled_records(const Experts& x) {
+  return (size_t)x.H * x.I / 4096;
+}
 
 // First block of each matrix inside an expert.
 __host__ __device__ inline size_t blk_gate(const Experts& x, int e) { return (size_t)e * x.nb; }
@@ -103,6 +113,8 @@ hipError_t launch_ffn_fast(const Experts& ex, const FfnArgs& a, hipStream_t s);
 // MFMA tiles of fast mode (experts with more than gmax assignments); writes x16.
 bool mfma_supported(int H, int I);
 hipError_t launch_mfma(const Experts& ex, const FfnArgs& a, hipStream_t s);
+// Writes the tiled copy of ex's planes (t_codes, t_dm, t_hi must be set).
+hipError_t launch_tile_weights(const Experts& ex, hipStream_t s);
 hipError_t launch_combine(const Experts& ex, const FfnArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -24,6 +24,8 @@
 // The grid is persistent. Work items are (expert tile, N tile) with the N
 // tiles of one expert tile adjacent; consecutive items go to workgroups of one
 // XCD, so the activation rows they share stay in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "gemv.h"
 #include "sched.h"
@@ -219,7 +221,7 @@ constexpr int tile_rows() { return DOWN ? 64 * NW : 32 * NW; }
 // boundaries: activations two stages ahead of their LDS stores (stage g lives
 // in LDS buffer g & 1), weight blocks one stage pair ahead. One barrier per
 // stage.
-template <int Q, bool DOWN, int NW>
+template <int Q, bool DOWN, int NW, bool TILED>
 __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   constexpr int NT = 64 * NW;                 // threads
   constexpr int CH = kBM * (kBK / 8) / NT;    // 16-byte activation chunks per thread per stage
@@ -240,7 +242,8 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
 
   // ---- activation cursor: chunk tid + NT u = row (c >> 3), LDS column 8 (c & 7) ----
   // LDS column 8 q of stage s holds K column 32 (s + S (q / 4)) + 8 (q % 4).
-  const uint4* xptr[CH];  // next stage's source chunk (null: row past M)
+  const uint4* x4 = reinterpret_cast<const uint4*>(a16);
+  uint32_t xoff[CH];      // next stage's source chunk in 16-byte units (~0u: row past M)
   int anext[CH];
   int xt = 0, xsg = 0;    // tile round and stage of the next activation load
   auto xprep = [&](int r) {  // tile r's rows: permutation entries, not yet waited on
@@ -260,16 +263,16 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
         r = (unsigned)r < (unsigned)a.T ? r : -1;
       }
       const int q = (tid + NT * u) & 7;
-      xptr[u] = r < 0 ? nullptr
-                      : reinterpret_cast<const uint4*>(a16 + (size_t)r * K + 32 * S * (q >> 2) + 8 * (q & 3));
+      const int col = TILED ? 8 * q : 32 * S * (q >> 2) + 8 * (q & 3);
+      xoff[u] = r < 0 ? ~0u : (uint32_t)(((size_t)r * K + col) / 8);
     }
   };
   auto xload = [&](uint4 (&v)[CH]) {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      // rows past M (null source) stay zero and are never loaded
-      v[u] = xptr[u] ? *xptr[u] : make_uint4(0, 0, 0, 0);
-      if (xptr[u]) xptr[u] += 4;  // 32 halves: the next stage
+      // rows past M stay zero and are never loaded
+      v[u] = xoff[u] != ~0u ? x4[xoff[u]] : make_uint4(0, 0, 0, 0);
+      if (xoff[u] != ~0u) xoff[u] += TILED ? 8 : 4;  // the next stage
     }
     if (++xsg == S) {
       xsg = 0;
@@ -287,33 +290,37 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
     }
   };
 
-  // ---- weight cursor: rows wrow(j) + lane % 32, blocks h S + stage ----
+  // ---- weight cursor: rows wrow(j) + lane % 32 ----
+  // canonical planes: blocks h S + stage; tiled copy: one 64-lane record per
+  // (32-row group, stage pair), blocks 4p + h and 4p + 2 + h.
   int wt = 0, wp = 0;  // tile round and stage pair of the next weight load
-  const uint4* wc[2];  // next pair's codes, d/m and third bits per row j
-  const uint2 *wd[2], *wh[2];
+  uint32_t wb[2];      // next pair's index in 16-byte code / 8-byte d,m units, per row j
+  const uint4* c4 = reinterpret_cast<const uint4*>(TILED ? ex.t_codes : ex.codes);
+  const uint2* dm2 = reinterpret_cast<const uint2*>(TILED ? ex.t_dm : ex.dm);
+  const uint2* hi2 = reinterpret_cast<const uint2*>(TILED ? ex.t_hi : ex.hi);
   auto wsetup = [&](int r) {
     const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      size_t blk;
-      if (DOWN) {
-        const int row = t.nt * tile_rows<DOWN, NW>() + 64 * wave + 32 * j + (lane & 31);
-        blk = blk_down(ex, t.e) + (size_t)row * (ex.I / 32) + h * S;
+      const int row0 = t.nt * tile_rows<DOWN, NW>() + (DOWN ? 64 * wave + 32 * j : 32 * wave);
+      const int mat = DOWN ? 2 : j;  // gate, up, down
+      if (TILED) {
+        const size_t rec = ((size_t)t.e * 3 + mat) * tiled_records(ex) + (size_t)(row0 / 32) * (S / 2);
+        wb[j] = (uint32_t)(rec * 64 + lane);
       } else {
-        const int row = t.nt * tile_rows<DOWN, NW>() + 32 * wave + (lane & 31);
-        blk = (j ? blk_up(ex, t.e) : blk_gate(ex, t.e)) + (size_t)row * (ex.H / 32) + h * S;
+        const size_t base = DOWN ? blk_down(ex, t.e) : (j ? blk_up(ex, t.e) : blk_gate(ex, t.e));
+        const size_t blk = base + (size_t)(row0 + (lane & 31)) * (K / 32) + h * S;
+        wb[j] = (uint32_t)(blk / 2);  // blk is even
       }
-      wc[j] = reinterpret_cast<const uint4*>(ex.codes + blk * 8);
-      wd[j] = reinterpret_cast<const uint2*>(ex.dm + blk * 2);
-      wh[j] = Q == 3 ? reinterpret_cast<const uint2*>(ex.hi + blk * 4) : nullptr;
     }
   };
   auto wload = [&](WPair (&w)[2]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      w[j].c = *wc[j]++;
-      w[j].dm = *wd[j]++;
-      w[j].hi = Q == 3 ? *wh[j]++ : make_uint2(0, 0);
+      w[j].c = c4[wb[j]];
+      w[j].dm = dm2[wb[j]];
+      w[j].hi = Q == 3 ? hi2[wb[j]] : make_uint2(0, 0);
+      wb[j] += TILED ? 64 : 1;
     }
     if (++wp == S / 2) {
       wp = 0;
@@ -336,8 +343,10 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   __syncthreads();
 
   int g = 0;  // global stage index
-  for (int r = 0; r < n_my; ++r) {
-    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
+  // One tile whose assignments fill LIVE 32-row activation groups; MFMAs of
+  // the empty groups are left out.
+  auto tile = [&](auto live_c, const TileInfo& t) {
+    constexpr int LIVE = decltype(live_c)::value;
     const int wrow0 = t.nt * tile_rows<DOWN, NW>() + (DOWN ? 64 : 32) * wave;
     float16_t acc[4][2];
 #pragma unroll
@@ -351,7 +360,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
       for (int j = 0; j < 2; ++j) w[j] = wstage<Q>(wq[j], 0);
       xstore(xb, xs[1]);             // stage g + 1 (total is even)
       if (g + 3 < total) xload(xb);  // stage g + 3
-      stage_mma<4, Q>(xs[0], w, acc);
+      stage_mma<LIVE, Q>(xs[0], w, acc);
       __syncthreads();
       // odd stage g + 1: LDS buffer 1, weight block 1
 #pragma unroll
@@ -361,14 +370,14 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
         xstore(xa, xs[0]);           // stage g + 2
       }
       if (g + 4 < total) xload(xa);  // stage g + 4
-      stage_mma<4, Q>(xs[1], w, acc);
+      stage_mma<LIVE, Q>(xs[1], w, acc);
       if (s + 2 < S) __syncthreads();
     }
     // ---- epilogue ----
     // acc[i][j][v]: weight row wrow0 (+ 32 j for down) + 8 (v / 4) + 4 h + v % 4,
     //               activation row 32 i + lane % 32
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < LIVE; ++i) {
       const int mm = 32 * i + (lane & 31);
       if (mm >= t.M) continue;
       const int slot = t.slot0 + mm;
@@ -403,6 +412,14 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
       }
     }
     __syncthreads();
+  };
+  for (int r = 0; r < n_my; ++r) {
+    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
+    // wave-uniform; Q3 keeps one variant (its third-bit plane leaves no
+    // registers for more)
+    if (Q == 2 && t.M <= 32) tile(std::integral_constant<int, 1>{}, t);
+    else if (Q == 2 && t.M <= 64) tile(std::integral_constant<int, 2>{}, t);
+    else tile(std::integral_constant<int, 4>{}, t);
   }
 }
 
@@ -431,6 +448,33 @@ __global__ __launch_bounds__(256) void x_to_f16(const void* __restrict__ x, long
   }
 }
 
+// Writes the tiled copy: one thread per (expert, matrix, record, lane).
+__global__ __launch_bounds__(256) void tile_weights(Experts ex, long n) {
+  const size_t R = tiled_records(ex);
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    const int lane = (int)(i & 63);
+    const size_t rec_all = (size_t)i >> 6;
+    const size_t rec = rec_all % R;
+    const int mat = (int)((rec_all / R) % 3);
+    const int e = (int)(rec_all / (R * 3));
+    const int K = mat == 2 ? ex.I : ex.H;
+    const size_t P = K / 128;  // block quads per row
+    const size_t g = rec / P, p = rec % P;
+    const size_t row = 32 * g + (lane & 31);
+    const size_t base = mat == 0 ? blk_gate(ex, e) : mat == 1 ? blk_up(ex, e) : blk_down(ex, e);
+    const size_t b0 = base + row * (K / 32) + 4 * p + (lane >> 5), b1 = b0 + 2;
+    const uint2* c = reinterpret_cast<const uint2*>(ex.codes);
+    const uint32_t* dm = reinterpret_cast<const uint32_t*>(ex.dm);
+    const uint2 c0 = c[b0], c1 = c[b1];
+    reinterpret_cast<uint4*>(const_cast<uint8_t*>(ex.t_codes))[i] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+    reinterpret_cast<uint2*>(const_cast<uint16_t*>(ex.t_dm))[i] = make_uint2(dm[b0], dm[b1]);
+    if (ex.qtype == 3) {
+      const uint32_t* hi = reinterpret_cast<const uint32_t*>(ex.hi);
+      reinterpret_cast<uint2*>(const_cast<uint8_t*>(ex.t_hi))[i] = make_uint2(hi[b0], hi[b1]);
+    }
+  }
+}
+
 template <int Q>
 hipError_t launch_q(const Experts& ex, const FfnArgs& a, int grid, hipStream_t s) {
   const long n8 = (long)a.T * ex.H / 8;
@@ -439,18 +483,32 @@ hipError_t launch_q(const Experts& ex, const FfnArgs& a, int grid, hipStream_t s
     MOE_LAUNCH("x_to_f16", s, x_to_f16<true>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
   else
     MOE_LAUNCH("x_to_f16", s, x_to_f16<false>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
-  if (ex.I % tile_rows<false, 8>() == 0)
-    MOE_LAUNCH("mfma_gateup", s, (mfma_tiles<Q, false, 8>), dim3(grid), dim3(512), 0, s, ex, a);
-  else
-    MOE_LAUNCH("mfma_gateup", s, (mfma_tiles<Q, false, 4>), dim3(grid), dim3(256), 0, s, ex, a);
-  if (ex.H % tile_rows<true, 8>() == 0)
-    MOE_LAUNCH("mfma_down", s, (mfma_tiles<Q, true, 8>), dim3(grid), dim3(512), 0, s, ex, a);
-  else
-    MOE_LAUNCH("mfma_down", s, (mfma_tiles<Q, true, 4>), dim3(grid), dim3(256), 0, s, ex, a);
+  const bool g8 = ex.I % tile_rows<false, 8>() == 0, d8 = ex.H % tile_rows<true, 8>() == 0;
+#define MOE_TILES(NAME, DOWN, NW)                                                              \
+  do {                                                                                         \
+    if (ex.t_codes)                                                                            \
+      MOE_LAUNCH(NAME, s, (mfma_tiles<Q, DOWN, NW, true>), dim3(grid), dim3(64 * NW), 0, s, ex, \
+                 a);                                                                           \
+    else                                                                                       \
+      MOE_LAUNCH(NAME, s, (mfma_tiles<Q, DOWN, NW, false>), dim3(grid), dim3(64 * NW), 0, s,   \
+                 ex, a);                                                                       \
+  } while (0)
+  if (g8) MOE_TILES("mfma_gateup", false, 8);
+  else MOE_TILES("mfma_gateup", false, 4);
+  if (d8) MOE_TILES("mfma_down", true, 8);
+  else MOE_TILES("mfma_down", true, 4);
+#undef MOE_TILES
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_tile_weights(const Experts& ex, hipStream_t s) {
+  const long n = (long)ex.E_tot * 3 * (long)tiled_records(ex) * 64;
+  const int grid = (int)(n / 256 + 1 < 8192 ? n / 256 + 1 : 8192);
+  MOE_LAUNCH("tile_weights", s, tile_weights, dim3(grid), dim3(256), 0, s, ex, n);
+  return hipGetLastError();
+}
 
 bool mfma_supported(int H, int I) {
   return H % tile_rows<true, 4>() == 0 && I % tile_rows<false, 4>() == 0;

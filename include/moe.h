@@ -147,6 +147,34 @@ int moe_experts_create(moe_experts **out, int32_t qtype, int32_t E, int32_t has_
                        const void *dm);
 int moe_experts_destroy(moe_experts *ex);
 
+/* Optional second copy of the weights, in the order in which the prefill
+ * matrix-core tiles read them, so that every wave's weight loads are
+ * contiguous (the canonical planes give one 16-byte piece per weight row).
+ * The pages' prompt path likewise runs on quantised expert data in kernel-
+ * friendly form ("Strata - the details", "Faster prompts"); the arrangement
+ * here is this library's own.
+ *
+ * moe_experts_tiled_size: bytes of the copy (the same as the codes, hi and dm
+ *   planes together), or 0 for a null handle.
+ * moe_experts_attach_tiled: enqueues on `stream` a device kernel that writes
+ *   the copy into buf (device memory owned by the caller, at least
+ *   moe_experts_tiled_size bytes, 16-byte aligned) from the canonical planes,
+ *   and records buf in the handle; from then on moe_ffn_q and moe_layer run
+ *   their matrix-core tiles on it (same results up to fp32 summation order).
+ *   buf == NULL detaches. The caller keeps buf alive and unchanged until it
+ *   detaches or destroys the handle, and must not call this while other calls
+ *   on the handle are in flight on other streams.
+ * Layout of the copy: codes [E_tot][3 matrices][R][64 lanes][16 bytes], then
+ *   dm [E_tot][3][R][64][4 uint16], then (Q3) hi [E_tot][3][R][64][8 bytes],
+ *   R = H*I/4096 records per matrix: for 32-row group g (rows 32g..32g+31 of
+ *   the matrix) and block quad p (blocks 4p..4p+3 of each row), record
+ *   g * (K/128) + p (K = the matrix's row length) holds for lane l the blocks
+ *   4p + l/32 and 4p + 2 + l/32 of row 32g + l%32.
+ * Errors: MOE_ERR_INVALID_ARG for a null handle, a misaligned buf or
+ *   bytes below the size; MOE_ERR_HIP if the kernel launch fails. */
+size_t moe_experts_tiled_size(const moe_experts *ex);
+int moe_experts_attach_tiled(moe_experts *ex, void *buf, size_t bytes, void *stream);
+
 /* ---- expert FFN and combine ---------------------------------------------- */
 
 /* Workspace bytes moe_ffn_q needs for T tokens, k experts per token, `mode`,

@@ -112,3 +112,22 @@ def test_ffn_validation_and_workspace():
         assert call(args(T=0, x=None, idx=None, gates=None, y=None, ws=None, nb=0)) == moe.OK
     finally:
         L.moe_experts_destroy(h)
+
+
+def test_tiled_copy_validation():
+    L = moe.lib()
+    assert L.moe_experts_tiled_size(None) == 0
+    assert L.moe_experts_attach_tiled(None, FAKE, 1 << 30, None) == moe.ERR_INVALID_ARG
+    for qtype, per_block in ((2, 12), (3, 16)):
+        st, h = make_handle(qtype=qtype, E=16, shared=1, H=256, I=128,
+                            hi=FAKE if qtype == 3 else None)
+        assert st == moe.OK
+        try:
+            need = L.moe_experts_tiled_size(h)
+            assert need == 17 * (3 * 256 * 128 // 32) * per_block
+            assert L.moe_experts_attach_tiled(h, FAKE, need - 1, None) == moe.ERR_INVALID_ARG
+            assert L.moe_experts_attach_tiled(h, C.c_void_p(0x10008), need,
+                                              None) == moe.ERR_INVALID_ARG  # misaligned
+            assert L.moe_experts_attach_tiled(h, None, 0, None) == moe.OK     # detach
+        finally:
+            L.moe_experts_destroy(h)

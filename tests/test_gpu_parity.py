@@ -159,11 +159,13 @@ def test_layer_call(cid, T, mode):
     ex.close()
 
 
-def run_ffn(lay, dev, idx_np, gates_np, mode, use_gpu_grouping=False):
+def run_ffn(lay, dev, idx_np, gates_np, mode, use_gpu_grouping=False, tiled=False):
     torch = torch_cuda()
     import bit_quantized_moe_topk_amd as moe
     cfg = lay["cfg"]
     ex = experts_of(lay, dev)
+    if tiled:
+        ex.attach_tiled()
     idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).cuda()
     gates = torch.from_numpy(np.ascontiguousarray(gates_np, dtype=np.float32)).cuda()
     grp = moe.group(idx, cfg.E, bool(cfg.shared)) if use_gpu_grouping else None
@@ -187,6 +189,24 @@ def test_ffn_parity(cid, mode, tol):
     log(f"[ffn] cfg{cid} {mode}: max rel-L2 {err.max():.3e}  p99 {np.percentile(err, 99):.3e}  "
         f"mean {err.mean():.3e}")
     assert err.max() <= tol
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_ffn_parity_tiled_weights(cid):
+    """Matrix-core tiles reading the tiled weight copy: oracle tolerance, and
+    agreement with the canonical-plane path up to fp32 summation order."""
+    lay, dev = layer_for(cid)
+    cfg = lay["cfg"]
+    idx, gates = oracle.route(lay["logits"], cfg.k)
+    log(f"[ffn] cfg{cid} tiled weights T={cfg.T}")
+    y_t = run_ffn(lay, dev, idx, gates, "fast", use_gpu_grouping=True, tiled=True)
+    y_c = run_ffn(lay, dev, idx, gates, "fast", use_gpu_grouping=True, tiled=False)
+    ref = oracle_rows(lay, idx, gates)
+    err = rel_l2_rows(y_t, ref)
+    log(f"[ffn] cfg{cid} tiled: max rel-L2 {err.max():.3e}; vs canonical "
+        f"{rel_l2_rows(y_t, y_c).max():.3e}")
+    assert err.max() <= TOL_FAST
+    assert rel_l2_rows(y_t, y_c).max() <= 5e-3
 
 
 @pytest.mark.parametrize("cid", [0, 1, 4])
@@ -218,11 +238,12 @@ def test_prefill_8k_sampled_rows(layer):
     idx, gates = oracle.route(lay["logits"], cfg.k)
     rows = np.random.default_rng(layer).choice(cfg.T, 256, replace=False).astype(np.int32)
     ref = oracle_rows(lay, idx, gates, rows=rows)
-    for mode, tol in (("fast", TOL_FAST), ("check", TOL_CHECK)):
-        log(f"[ffn] cfg3 layer {layer} mode={mode}")
-        y = run_ffn(lay, dev, idx, gates, mode, use_gpu_grouping=True)
+    for mode, tol, tiled in (("fast", TOL_FAST, False), ("fast", TOL_FAST, True),
+                             ("check", TOL_CHECK, False)):
+        log(f"[ffn] cfg3 layer {layer} mode={mode} tiled={tiled}")
+        y = run_ffn(lay, dev, idx, gates, mode, use_gpu_grouping=True, tiled=tiled)
         err = rel_l2_rows(y[rows], ref)
-        log(f"[ffn] cfg3 layer {layer} {mode}: max rel-L2 {err.max():.3e}")
+        log(f"[ffn] cfg3 layer {layer} {mode} tiled={tiled}: max rel-L2 {err.max():.3e}")
         assert err.max() <= tol
 
 
