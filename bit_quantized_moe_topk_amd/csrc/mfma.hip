@@ -36,6 +36,9 @@ namespace {
 constexpr int kBM = 128;          // assignments per tile
 constexpr int kBK = 64;           // K per stage
 constexpr int kRow = 72;          // LDS row stride in halves (64 + 8 pad: 144 B)
+// Epilogue staging per wave (16-bit outputs): down, 64 assignments x 64 rows
+// (stride 72); gate/up, 128 assignments x 32 rows (stride 40).
+constexpr int kStage = 128 * 40;
 // --- dequantisation -------------------------------------------------------
 // Code pair -> fp16 pair: OR the codes into the mantissa of 1024 (exact
 // 1024 + q), subtract 1024 (exact), then one fused d*q + m.
@@ -226,6 +229,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   constexpr int NT = 64 * NW;                 // threads
   constexpr int CH = kBM * (kBK / 8) / NT;    // 16-byte activation chunks per thread per stage
   __shared__ __attribute__((aligned(16))) _Float16 xs[2][kBM * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ostage[NW][kStage];  // epilogue, per wave
   __shared__ WorkMap wm;
   __shared__ int offs[MOE_MAX_E_DEV + 2];
   for (int e = threadIdx.x; e <= ex.E_tot; e += NT) offs[e] = a.offsets[e];
@@ -348,6 +352,12 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   auto tile = [&](auto live_c, const TileInfo& t) {
     constexpr int LIVE = decltype(live_c)::value;
     const int wrow0 = t.nt * tile_rows<DOWN, NW>() + (DOWN ? 64 : 32) * wave;
+    float gpre[LIVE];  // routing gates of this lane's assignments, fetched early
+#pragma unroll
+    for (int i = 0; i < LIVE; ++i) {
+      const int mm = 32 * i + (lane & 31);
+      gpre[i] = DOWN && mm < t.M ? gate_of(a, t.slot0 + mm) : 0.f;
+    }
     float16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -375,41 +385,80 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
     }
     // ---- epilogue ----
     // acc[i][j][v]: weight row wrow0 (+ 32 j for down) + 8 (v / 4) + 4 h + v % 4,
-    //               activation row 32 i + lane % 32
+    //               activation row 32 i + lane % 32.
+    // 16-bit outputs go through this wave's LDS staging area so that each
+    // assignment's row segment is written with full 16-byte stores.
+    uint16_t* stg = ostage[wave];
+    if (DOWN && a.o) {
 #pragma unroll
-    for (int i = 0; i < LIVE; ++i) {
-      const int mm = 32 * i + (lane & 31);
-      if (mm >= t.M) continue;
-      const int slot = t.slot0 + mm;
-      if (DOWN) {
-        const float gt = gate_of(a, slot);
+      for (int i = 0; i < LIVE; ++i) {
+        const int mm = 32 * i + (lane & 31);
+        if (mm >= t.M) continue;
+        const size_t orow = (size_t)(t.slot0 + mm) * ex.H + wrow0;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const size_t off = (size_t)slot * ex.H + wrow0 + 32 * j + 8 * q + 4 * h;
-            const float v0 = gt * acc[i][j][4 * q], v1 = gt * acc[i][j][4 * q + 1];
-            const float v2 = gt * acc[i][j][4 * q + 2], v3 = gt * acc[i][j][4 * q + 3];
-            if (a.o) {
-              *reinterpret_cast<float4*>(a.o + off) = make_float4(v0, v1, v2, v3);
-            } else {
-              *reinterpret_cast<uint2*>(a.ob + off) =
-                  make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
-                             f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(a.o + orow + 32 * j + 8 * q + 4 * h) =
+                make_float4(gpre[i] * acc[i][j][4 * q], gpre[i] * acc[i][j][4 * q + 1],
+                            gpre[i] * acc[i][j][4 * q + 2], gpre[i] * acc[i][j][4 * q + 3]);
+      }
+    } else if (DOWN) {
+      // two passes of 64 assignments x 64 rows (bf16, row stride 72)
+#pragma unroll
+      for (int ip = 0; ip < (LIVE + 1) / 2; ++ip) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * ip + ii;
+          if (i >= LIVE) break;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float g = gpre[i];
+              const uint32_t b0 = f32_to_bf16_bits(g * acc[i][j][4 * q]);
+              const uint32_t b1 = f32_to_bf16_bits(g * acc[i][j][4 * q + 1]);
+              const uint32_t b2 = f32_to_bf16_bits(g * acc[i][j][4 * q + 2]);
+              const uint32_t b3 = f32_to_bf16_bits(g * acc[i][j][4 * q + 3]);
+              *reinterpret_cast<uint2*>(stg + (32 * ii + (lane & 31)) * 72 + 32 * j + 8 * q + 4 * h) =
+                  make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
             }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {  // 8 assignments x 8 chunks of 16 bytes per step
+          const int tk = (lane >> 3) + 8 * it, mm = 64 * ip + tk;
+          if (mm < t.M) {
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + tk * 72 + 8 * (lane & 7));
+            *reinterpret_cast<uint4*>(a.ob + (size_t)(t.slot0 + mm) * ex.H + wrow0 + 8 * (lane & 7)) = v;
           }
         }
-      } else {
-        _Float16* hrow = static_cast<_Float16*>(a.h) + (size_t)slot * ex.I + wrow0;
+        __builtin_amdgcn_wave_barrier();
+      }
+    } else {
+      // 128 assignments x 32 rows of h (fp16, row stride 40)
+#pragma unroll
+      for (int i = 0; i < LIVE; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float v[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) v[u] = silu_mul(acc[i][0][4 * q + u], acc[i][1][4 * q + u]);
-          *reinterpret_cast<uint2*>(hrow + 8 * q + 4 * h) =  // K order 0, 2, 1, 3
-              make_uint2(pack_half2(v[0], v[2]), pack_half2(v[1], v[3]));
+          *reinterpret_cast<uint2*>(stg + (32 * i + (lane & 31)) * 40 + 8 * q + 4 * h) =
+              make_uint2(pack_half2(v[0], v[2]), pack_half2(v[1], v[3]));  // K order 0, 2, 1, 3
         }
       }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < 2 * LIVE; ++it) {  // 16 assignments x 4 chunks of 16 bytes per step
+        const int mm = (lane >> 2) + 16 * it;
+        if (mm < t.M) {
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + mm * 40 + 8 * (lane & 3));
+          *reinterpret_cast<uint4*>(static_cast<_Float16*>(a.h) + (size_t)(t.slot0 + mm) * ex.I +
+                                    wrow0 + 8 * (lane & 3)) = v;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
   };
