@@ -170,6 +170,37 @@ def gpu_hold(ms: float) -> None:
     torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
 
 
+def kernel_source_hash() -> str:
+    """Digest of the HIP sources (a byte-counter summary is valid only for them)."""
+    import hashlib
+    d = os.path.join(ROOT, "bit_quantized_moe_topk_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 byte-counter summary, or
+    None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel source hash") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic bytes per launch"].replace(",", ""))
+    except (KeyError, ValueError):
+        return None
+
+
 def kernel_profile(insts, L, stream, steps: int, chunk: int = 32) -> dict:
     import torch
     import bit_quantized_moe_topk_amd as moe
@@ -262,7 +293,7 @@ def run_decode(cfg, args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(k_bytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if k_ms else None,
-            "traffic": None,
+            "traffic": measured_traffic(kname, "decode"),
             "launches": n_k,
             "avg_us": round(1e3 * k_ms / max(n_k, 1), 2),
             "bytes_per_launch": round(k_bytes / max(n_k, 1)),
@@ -323,7 +354,7 @@ def run_prefill(cfg, args):
             "peak": MFMA_PEAK_TFLOPS_F16,
             "unit": "TFLOP/s",
             "frac": round(flops_gu / (gu_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS_F16, 4) if gu_ms else None,
-            "traffic": None,
+            "traffic": measured_traffic("mfma_gateup", "prefill_8k"),
             "launches": n_gu,
             "avg_us": round(1e3 * gu_ms / max(n_gu, 1), 1),
             "flops_per_launch": flops_gu / max(n_gu, 1),
@@ -378,6 +409,9 @@ def main() -> int:
     ap.add_argument("--no-tiled", action="store_true",
                     help="prefill on the canonical weight planes only (no tiled copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="first copy a buffer of this many MiB 5 times (a kernel of known "
+                         "traffic for scaling hardware byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-layers", type=int, default=8)
     args = ap.parse_args()
@@ -397,6 +431,15 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     moe.lib()
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 copies of {args.copy_calibration_mb} MiB")
+        del src, dst
     cfg = CONFIGS[1]
     dec, hosts, insts = run_decode(cfg, args)
     log(f"decode: {dec['tokens_per_s']:.0f} tokens/s, {dec['ms_per_step'] * 1e3:.1f} us/step, "

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -60,14 +61,21 @@ __device__ inline uint64_t lanemask_lt() {
 
 __device__ inline float half_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
-// Launch profiling hooks (no-ops unless a caller enabled moe_profile_begin).
-void prof_open(const char* name, hipStream_t s);
-void prof_close(hipStream_t s);
-#define MOE_LAUNCH(NAME, STREAM, ...)      \
-  do {                                     \
-    ::moe::prof_open(NAME, STREAM);        \
-    hipLaunchKernelGGL(__VA_ARGS__);       \
-    ::moe::prof_close(STREAM);             \
+// Launch profiling hooks (inactive unless a caller enabled moe_profile_begin).
+// While active, prof_open hands out an event pair that the launch attaches to
+// the kernel's own dispatch (hipExtLaunchKernelGGL), so the pair brackets the
+// kernel's execution on the device, not the queueing around it.
+bool prof_open(const char* name, hipEvent_t* start, hipEvent_t* stop);
+void prof_close();
+#define MOE_LAUNCH(NAME, STREAM, KERNEL, GRID, BLOCK, LDS, S, ...)                           \
+  do {                                                                                     \
+    hipEvent_t moe_ev_a_ = nullptr, moe_ev_b_ = nullptr;                                   \
+    if (::moe::prof_open(NAME, &moe_ev_a_, &moe_ev_b_)) {                                  \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, S, moe_ev_a_, moe_ev_b_, 0, __VA_ARGS__); \
+      ::moe::prof_close();                                                                 \
+    } else {                                                                               \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, S, __VA_ARGS__);                        \
+    }                                                                                      \
   } while (0)
 
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----------

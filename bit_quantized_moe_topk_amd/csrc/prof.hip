@@ -1,7 +1,7 @@
-// Launch profiling: while enabled, every kernel the library launches is
-// bracketed by two HIP events recorded on the launch stream, so a caller can
-// read per-kernel GPU durations of the launches it made (moe_profile_* in
-// include/moe.h). Process-global and not thread-safe by design: it is a
+// Launch profiling: while enabled, every kernel the library launches carries
+// two HIP events attached to its dispatch (start and end of its execution on
+// the launch stream), so a caller can read per-kernel GPU durations of the
+// launches it made (moe_profile_* in include/moe.h). Process-global and not thread-safe by design: it is a
 // measurement aid, off unless a caller turns it on.
 #include <string.h>
 
@@ -35,20 +35,21 @@ Rec g_cur;
 
 }  // namespace
 
-void prof_open(const char* name, hipStream_t s) {
+bool prof_open(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   g_open = false;
-  if (!g_on || g_used + 2 > g_pool.size()) return;
+  if (!g_on || g_used + 2 > g_pool.size()) return false;
   g_cur.name = name;
   g_cur.a = g_pool[g_used];
   g_cur.b = g_pool[g_used + 1];
-  if (hipEventRecord(g_cur.a, s) != hipSuccess) return;
+  *start = g_cur.a;
+  *stop = g_cur.b;
   g_open = true;
+  return true;
 }
 
-void prof_close(hipStream_t s) {
+void prof_close() {
   if (!g_open) return;
   g_open = false;
-  if (hipEventRecord(g_cur.b, s) != hipSuccess) return;
   g_used += 2;
   g_recs.push_back(g_cur);
 }
@@ -91,6 +92,7 @@ int moe_profile_end(void) {
 }
 
 int32_t moe_profile_count(void) { return (int32_t)moe::g_sum.size(); }
+
 
 int moe_profile_get(int32_t i, const char** name, int32_t* launches, double* total_ms) {
   using namespace moe;

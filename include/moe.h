@@ -223,11 +223,11 @@ int moe_layer(const float *logits, const void *x, int32_t xdtype, int32_t T, con
 /* ---- launch profiling ------------------------------------------------------ */
 
 /* A measurement aid for the caller's own timing (per-kernel GPU durations).
- * moe_profile_begin: from now on every kernel the library launches is
- *   bracketed by two HIP events recorded on its launch stream, for up to
- *   max_launches launches (later launches are not recorded). Clears earlier
- *   records. Creates the events on first use (host-side objects, no device
- *   memory).
+ * moe_profile_begin: from now on every kernel the library launches carries
+ *   two HIP events attached to its dispatch on its launch stream, which record
+ *   the start and end of the kernel's execution, for up to max_launches
+ *   launches (later launches are not recorded). Clears earlier records.
+ *   Creates the events on first use (host-side objects, no device memory).
  * moe_profile_end: stops recording, waits for the recorded events and sums the
  *   elapsed time per kernel name.
  * moe_profile_count / moe_profile_get: the summary, one entry per kernel name:
