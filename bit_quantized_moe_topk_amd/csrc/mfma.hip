@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "deq16.h"
 #include "gemv.h"
 #include "sched.h"
 
@@ -39,15 +40,6 @@ constexpr int kRow = 72;          // LDS row stride in halves (64 + 8 pad: 144 B
 // Epilogue staging per wave (16-bit outputs): down, 64 assignments x 64 rows
 // (stride 72); gate/up, 128 assignments x 32 rows (stride 40).
 constexpr int kStage = 128 * 40;
-// --- dequantisation -------------------------------------------------------
-// Code pair -> fp16 pair: OR the codes into the mantissa of 1024 (exact
-// 1024 + q), subtract 1024 (exact), then one fused d*q + m.
-__device__ inline uint32_t deq_pair(uint32_t t, half2_t d2, half2_t m2) {
-  const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  const half2_t q = __builtin_bit_cast(half2_t, t | 0x64006400u) - k1024;
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, d2, m2));
-}
-
 __device__ inline half8_t frag(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
 
 // Two consecutive quantisation blocks of one weight row (the blocks a lane
@@ -67,88 +59,10 @@ __device__ inline WPair load_wpair(const Experts& ex, size_t blk) {
   return w;
 }
 
-// MFMA K order inside each group of four weights: positions 0, 1, 2, 3 hold
-// weights 0, 2, 1, 3. Both operands follow it: the fp16 activation copy and the
-// SwiGLU output are stored that way, so each products' sum is unchanged.
-//
-// Q2 operands: byte j of e = c & 0x33333333 holds codes 4j (low nibble) and
-// 4j + 2 (high nibble), and byte j of o = (c >> 2) & 0x33333333 holds codes
-// 4j + 1 and 4j + 3, each as an FP4 E2M1 value q / 2. One scaled conversion
-// (scale 2) turns a byte into the exact fp16 pair (q, q'), then one fused
-// d*q + m rounds once.
-//
-// Q3 operands: a byte permute puts byte j of c and of c >> 2 in the two halves
-// of a word; masks pick codes (4j, 4j + 1) from bits 0-1 and (4j + 2, 4j + 3)
-// from bits 4-5, OR in the third bits, and OR-ing into the mantissa of 1024
-// gives 1024 + q exactly; subtracting 1024 and one fused d*q + m follow, and a
-// final permute brings the pairs into the K order above.
-struct WStage {
-  uint32_t w0, w1, w2, w3;  // Q2: e, o of code words 0, 1; Q3: codes 0, 1, third bits
-  half2_t d2, m2;
-};
-
 template <int Q>
 __device__ inline WStage wstage(const WPair& w, int b) {
-  WStage st;
-  const uint32_t c0 = b ? w.c.z : w.c.x, c1 = b ? w.c.w : w.c.y;
-  if (Q == 2) {
-    st.w0 = c0 & 0x33333333u;
-    st.w1 = (c0 >> 2) & 0x33333333u;
-    st.w2 = c1 & 0x33333333u;
-    st.w3 = (c1 >> 2) & 0x33333333u;
-  } else {
-    st.w0 = c0;
-    st.w1 = c1;
-    st.w2 = b ? w.hi.y : w.hi.x;
-    st.w3 = 0u;
-  }
-  const uint32_t dm = b ? w.dm.y : w.dm.x;
-  st.d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
-  st.m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
-  return st;
-}
-
-// Byte j of w as two FP4 E2M1 values, times 2, in fp16 (j is a constant after
-// unrolling; the instruction takes it as an immediate).
-__device__ inline half2_t fp4x2_to_f16(uint32_t w, int j) {
-  switch (j) {
-    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 0);
-    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 1);
-    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 2);
-    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 3);
-  }
-}
-
-// Weights 8 kk .. 8 kk + 7 of the stage's block as an MFMA operand.
-template <int Q>
-__device__ inline half8_t wfrag(const WStage& w, int kk) {
-  uint32_t o[4];
-  if (Q == 2) {
-    const uint32_t e = kk < 2 ? w.w0 : w.w2, od = kk < 2 ? w.w1 : w.w3;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = 2 * (kk & 1) + u;
-      const half2_t qa = fp4x2_to_f16(e, j), qb = fp4x2_to_f16(od, j);
-      o[2 * u] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qa, w.d2, w.m2));
-      o[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qb, w.d2, w.m2));
-    }
-  } else {
-    const uint32_t cw = kk < 2 ? w.w0 : w.w1, hq = kk < 2 ? w.w2 : w.w2 >> 16;
-    const uint32_t s = cw >> 2;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t j = 2 * (kk & 1) + u;  // byte of cw: codes 4j .. 4j + 3
-      const uint32_t r = __builtin_amdgcn_perm(s, cw, 0x0C000C00u | ((4u + j) << 16) | j);
-      uint32_t t0 = r & 0x00030003u, t1 = (r >> 4) & 0x00030003u;
-      const uint32_t hb = hq >> (4 * j);
-      t0 |= ((hb & 1u) << 2) | ((hb & 2u) << 17);
-      t1 |= (hb & 4u) | ((hb & 8u) << 15);
-      const uint32_t p01 = deq_pair(t0, w.d2, w.m2), p23 = deq_pair(t1, w.d2, w.m2);
-      o[2 * u] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);      // weights 0, 2
-      o[2 * u + 1] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);  // weights 1, 3
-    }
-  }
-  return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  return wstage_block<Q>(b ? w.c.z : w.c.x, b ? w.c.w : w.c.y, b ? w.hi.y : w.hi.x,
+                         b ? w.dm.y : w.dm.x);
 }
 
 // One stage of an MFMA wave over NI 32-row activation groups: activation

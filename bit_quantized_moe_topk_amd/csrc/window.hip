@@ -16,6 +16,7 @@
 //     reproducible run to run.
 // Activations enter as bf16 and the codes stay exact (gemv.h).
 #include "common.h"
+#include "deq16.h"
 #include "gemv.h"
 #include "sched.h"
 #include "topk.h"
@@ -89,67 +90,160 @@ constexpr int win_dn_rows() {  // rows of H per down workgroup: two row groups
 }
 constexpr int kWinBatch = 4;   // experts whose weights a wave has in flight at once
 
+// LDS state of the window's routing, built by every workgroup.
+struct WinRoute {
+  int lidx[kWinT * kWinMaxK];
+  float lgate[kWinT * kWinMaxK];
+  int flag[MOE_MAX_E_DEV + 1];
+  int tmask[MOE_MAX_E_DEV + 1];
+  int wsum[16];
+  uint32_t bits[64];  // routed-expert bitmap (experts < 2,048)
+  int pref[64];       // set bits before each bitmap word
+  WinList wl;
+  TopkScratch tks[kWinT];
+};
+
+// Routing, part 1: wave t selects token t's experts into LDS. Called before
+// the activation loads: loads complete in order, so the logits must not queue
+// behind them.
+__device__ inline void win_topk(WinRoute& R, const float* __restrict__ logits, int T, int E, int k) {
+  const int wave = threadIdx.x >> 6;
+  if (wave < T)
+    topk_any(logits + (size_t)wave * E, E, k, R.lidx + wave * k, R.lgate + wave * k, &R.tks[wave]);
+}
+
+__device__ inline void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Routing, part 2: the active-expert list (ascending expert, shared last) with
+// each expert's token mask and gates; workgroup 0 also publishes idx, gates
+// and the list. Returns the number of active experts.
+//
+// Up to 64 assignments (every 4-token window with k <= 16) take one wave: the
+// assignments set bits of an expert bitmap, a scan over its 64 words gives
+// every expert its rank (the number of routed experts below it), and each
+// assignment writes its expert, token bit and gate at that rank.
+__device__ inline int win_list(WinRoute& R, const Experts& ex, int T, int k, int32_t* idx_out,
+                               float* gates_out, WinList* gmeta) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int E = ex.E, E_tot = ex.E_tot;
+  const int A = T * k;
+  if (A <= 64) {
+    __syncthreads();  // the top-k waves' lidx, lgate
+    if (tid < 64) {
+      const int lane = tid;
+      R.bits[lane] = 0u;
+      wave_sync_lds();
+      int e = 0, t = 0;
+      float g = 0.f;
+      if (lane < A) {
+        e = R.lidx[lane];
+        g = R.lgate[lane];
+        t = lane / k;
+        atomicOr(&R.bits[e >> 5], 1u << (e & 31));
+      }
+      wave_sync_lds();
+      const uint32_t w = R.bits[lane];
+      const int incl = wave_inclusive_scan(__popc(w));
+      R.pref[lane] = incl - __popc(w);
+      const int n_routed = __builtin_amdgcn_readlane(incl, 63);
+      const int n_act = n_routed + ex.has_shared;
+      for (int p = lane; p < n_act; p += 64) {
+        R.wl.act_mask[p] = 0;
+#pragma unroll
+        for (int u = 0; u < kWinT; ++u) R.wl.act_gate[p][u] = 0.f;
+      }
+      wave_sync_lds();
+      if (lane < A) {
+        const int rank = R.pref[e >> 5] + __popc(R.bits[e >> 5] & ((1u << (e & 31)) - 1u));
+        R.wl.act_e[rank] = e;  // the same value from every assignment of e
+        atomicOr(&R.wl.act_mask[rank], 1 << t);
+        R.wl.act_gate[rank][t] = g;
+      }
+      if (ex.has_shared && lane < T) {
+        if (lane == 0) {
+          R.wl.act_e[n_routed] = E;
+          R.wl.act_mask[n_routed] = (1 << T) - 1;
+        }
+        R.wl.act_gate[n_routed][lane] = 1.0f;
+      }
+      if (lane == 0) R.wl.n_act = n_act;
+    }
+    __syncthreads();
+    const int n_act = R.wl.n_act;
+    if (blockIdx.x == 0) {
+      for (int a = tid; a < A; a += NT) {
+        idx_out[a] = R.lidx[a];
+        gates_out[a] = R.lgate[a];
+      }
+      if (tid == 0) gmeta->n_act = n_act;
+      for (int p = tid; p < n_act; p += NT) {
+        gmeta->act_e[p] = R.wl.act_e[p];
+        gmeta->act_mask[p] = R.wl.act_mask[p];
+#pragma unroll
+        for (int u = 0; u < kWinT; ++u) gmeta->act_gate[p][u] = R.wl.act_gate[p][u];
+      }
+    }
+    return n_act;
+  }
+  for (int e = tid; e < E_tot; e += NT) R.tmask[e] = 0;
+  __syncthreads();
+  for (int a = tid; a < T * k; a += NT) atomicOr(&R.tmask[R.lidx[a]], 1 << (a / k));
+  if (ex.has_shared && tid == 0) R.tmask[E] = (1 << T) - 1;
+  __syncthreads();
+  for (int e = tid; e < E_tot; e += NT) R.flag[e] = R.tmask[e] != 0;
+  __syncthreads();
+  const int n_act = block_exclusive_scan(R.flag, E_tot, R.wsum);
+  for (int e = tid; e < E_tot; e += NT) {
+    if (R.tmask[e]) {
+      const int p = R.flag[e];
+      R.wl.act_e[p] = e;
+      R.wl.act_mask[p] = R.tmask[e];
+#pragma unroll
+      for (int t = 0; t < kWinT; ++t) R.wl.act_gate[p][t] = 0.f;
+    }
+  }
+  if (tid == 0) R.wl.n_act = n_act;
+  __syncthreads();
+  for (int a = tid; a < T * k; a += NT) R.wl.act_gate[R.flag[R.lidx[a]]][a / k] = R.lgate[a];
+  if (ex.has_shared && tid < T) R.wl.act_gate[R.flag[E]][tid] = 1.0f;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int a = tid; a < T * k; a += NT) {
+      idx_out[a] = R.lidx[a];
+      gates_out[a] = R.lgate[a];
+    }
+    if (tid == 0) gmeta->n_act = n_act;
+    for (int p = tid; p < n_act; p += NT) {
+      gmeta->act_e[p] = R.wl.act_e[p];
+      gmeta->act_mask[p] = R.wl.act_mask[p];
+#pragma unroll
+      for (int t = 0; t < kWinT; ++t) gmeta->act_gate[p][t] = R.wl.act_gate[p][t];
+    }
+  }
+  return n_act;
+}
+
 template <int BPR, int Q, bool XF32>
 __global__ __launch_bounds__(kWinThreads) void win_gateup(const float* __restrict__ logits, int T,
                                                           int k, Experts ex, const void* x,
                                                           int32_t* idx_out, float* gates_out,
                                                           WinList* gmeta, uint16_t* hwin) {
-  __shared__ int lidx[kWinT * kWinMaxK];
-  __shared__ float lgate[kWinT * kWinMaxK];
-  __shared__ int flag[MOE_MAX_E_DEV + 1];
-  __shared__ int tmask[MOE_MAX_E_DEV + 1];
-  __shared__ int wsum[16];
-  __shared__ WinList wl;
-  __shared__ TopkScratch tks[kWinT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = ex.E, E_tot = ex.E_tot;
+  __shared__ WinRoute R;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = lane % BPR, rg = lane / BPR;
+  WinList& wl = R.wl;
 
-  // routing: wave t selects token t's experts (before the activation loads:
-  // loads complete in order, so the logits must not queue behind them)
-  if (wave < T)
-    topk_any(logits + (size_t)wave * E, E, k, lidx + wave * k, lgate + wave * k, &tks[wave]);
+  win_topk(R, logits, T, ex.E, k);
   XB xb[kWinT];
 #pragma unroll
   for (int t = 0; t < kWinT; ++t) {
     if (t < T) load_x_row<Q, XF32>(x, ex.H, t, b, xb[t]);
     else zero_xb(xb[t]);
   }
-  for (int e = tid; e < E_tot; e += kWinThreads) tmask[e] = 0;
-  __syncthreads();
-  for (int a = tid; a < T * k; a += kWinThreads) atomicOr(&tmask[lidx[a]], 1 << (a / k));
-  if (ex.has_shared && tid == 0) tmask[E] = (1 << T) - 1;
-  __syncthreads();
-  for (int e = tid; e < E_tot; e += kWinThreads) flag[e] = tmask[e] != 0;
-  __syncthreads();
-  const int n_act = block_exclusive_scan(flag, E_tot, wsum);
-  for (int e = tid; e < E_tot; e += kWinThreads) {
-    if (tmask[e]) {
-      const int p = flag[e];
-      wl.act_e[p] = e;
-      wl.act_mask[p] = tmask[e];
-#pragma unroll
-      for (int t = 0; t < kWinT; ++t) wl.act_gate[p][t] = 0.f;
-    }
-  }
-  if (tid == 0) wl.n_act = n_act;
-  __syncthreads();
-  for (int a = tid; a < T * k; a += kWinThreads) wl.act_gate[flag[lidx[a]]][a / k] = lgate[a];
-  if (ex.has_shared && tid < T) wl.act_gate[flag[E]][tid] = 1.0f;
-  __syncthreads();
-  if (blockIdx.x == 0) {
-    for (int a = tid; a < T * k; a += kWinThreads) {
-      idx_out[a] = lidx[a];
-      gates_out[a] = lgate[a];
-    }
-    if (tid == 0) gmeta->n_act = n_act;
-    for (int p = tid; p < n_act; p += kWinThreads) {
-      gmeta->act_e[p] = wl.act_e[p];
-      gmeta->act_mask[p] = wl.act_mask[p];
-#pragma unroll
-      for (int t = 0; t < kWinT; ++t) gmeta->act_gate[p][t] = wl.act_gate[p][t];
-    }
-  }
+  const int n_act = win_list(R, ex, T, k, idx_out, gates_out, gmeta);
 
   // gate/up + SwiGLU for this workgroup's pair-rows; wave w takes the active
   // experts w, w + 8, ..., kWinBatch at a time with all their loads in flight
@@ -209,6 +303,157 @@ __global__ __launch_bounds__(kWinThreads) void win_gateup(const float* __restric
               (uint16_t)f32_to_bf16_bits(silu_mul(v[0], other));
       }
     }
+  }
+}
+
+// Gate/up + SwiGLU of the window on the matrix cores (H a multiple of 1,024,
+// at most 4,096). Workgroup (g, s) owns rows 16g .. 16g + 15 of I (gate and
+// up) for the active experts s, s + 8, ...; its 8 waves split H into 8 slices.
+// A wave computes, per expert, a 16-row x 16-token tile of gate and of up with
+// v_mfma_f32_16x16x32_f16 (weights as rows, tokens past T zero): lane group c
+// (lane / 16) feeds 8 weights of block (slice start + NBL c + b) per step, so
+// each lane streams NBL contiguous blocks of its row, and dequantises them in
+// registers (deq16.h). The slices' partial tiles are summed in LDS in slice
+// order (deterministic), then SwiGLU and the h store for routed tokens.
+constexpr int kMmaSlices = 8;   // expert slices: workgroups per 16-row group
+constexpr int kMmaBatch = 4;    // experts per round
+constexpr int kMmaMaxH = 4096;
+
+template <int NBL>
+struct WRow {  // NBL consecutive blocks of one row
+  uint32_t c[2 * NBL], hi[NBL], dm[NBL];
+};
+
+template <int Q, int NBL>
+__device__ inline WRow<NBL> load_wrow(const Experts& ex, size_t blk) {
+  WRow<NBL> w;
+  if (NBL == 1) {
+    const uint2 c = *reinterpret_cast<const uint2*>(ex.codes + blk * 8);
+    w.c[0] = c.x;
+    w.c[1] = c.y;
+    w.dm[0] = *reinterpret_cast<const uint32_t*>(ex.dm + blk * 2);
+    if (Q == 3) w.hi[0] = *reinterpret_cast<const uint32_t*>(ex.hi + blk * 4);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBL; i += 2) {
+      const uint4 c = *reinterpret_cast<const uint4*>(ex.codes + (blk + i) * 8);
+      w.c[2 * i] = c.x;
+      w.c[2 * i + 1] = c.y;
+      w.c[2 * i + 2] = c.z;
+      w.c[2 * i + 3] = c.w;
+      const uint2 dm = *reinterpret_cast<const uint2*>(ex.dm + (blk + i) * 2);
+      w.dm[i] = dm.x;
+      w.dm[i + 1] = dm.y;
+      if (Q == 3) {
+        const uint2 h = *reinterpret_cast<const uint2*>(ex.hi + (blk + i) * 4);
+        w.hi[i] = h.x;
+        w.hi[i + 1] = h.y;
+      }
+    }
+  }
+  if (Q != 3)
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) w.hi[i] = 0u;
+  return w;
+}
+
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+template <int Q, bool XF32, int NBL>
+__global__ __launch_bounds__(kWinThreads) void win_gateup_mma(const float* __restrict__ logits,
+                                                              int T, int k, Experts ex,
+                                                              const void* x, int32_t* idx_out,
+                                                              float* gates_out, WinList* gmeta,
+                                                              uint16_t* hwin) {
+  __shared__ WinRoute R;
+  __shared__ __attribute__((aligned(16))) _Float16 xs[kWinT * kMmaMaxH];
+  __shared__ float red[kWinWaves][kMmaBatch][2][16][kWinT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = ex.H;
+  WinList& wl = R.wl;
+
+  win_topk(R, logits, T, ex.E, k);
+  // the window's activations -> LDS fp16 in the MFMA K order; tokens >= T zero
+  for (int i = tid; i < kWinT * H / 4; i += kWinThreads) {
+    const int t = i / (H / 4), q = i % (H / 4);
+    float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+    if (t < T) {
+      if (XF32) {
+        const float4 f = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)t * H)[q];
+        v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
+      } else {
+        const uint2 u = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)t * H)[q];
+        v0 = bf16_lo(u.x); v1 = bf16_hi(u.x); v2 = bf16_lo(u.y); v3 = bf16_hi(u.y);
+      }
+    }
+    *reinterpret_cast<uint2*>(xs + t * H + 4 * q) = make_uint2(pack_half2(v0, v2), pack_half2(v1, v3));
+  }
+  const int n_act = win_list(R, ex, T, k, idx_out, gates_out, gmeta);  // ends with a barrier
+
+  const int rgrp = blockIdx.x / kMmaSlices, es = blockIdx.x % kMmaSlices;
+  const int c = lane >> 4, r16 = lane & 15;
+  const int kb0 = wave * (H / 256) + NBL * c;  // this lane's first block of the wave's slice
+  half8_t xf[NBL][4];  // B operand: token r16, the same K as the lane's weights
+#pragma unroll
+  for (int b = 0; b < NBL; ++b)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      half8_t v = {};
+      if (r16 < T) v = *reinterpret_cast<const half8_t*>(xs + r16 * H + 32 * (kb0 + b) + 8 * t);
+      xf[b][t] = v;
+    }
+  const size_t roff = (size_t)(16 * rgrp + r16) * (H / 32) + kb0;
+
+  for (int p0 = es; p0 < n_act; p0 += kMmaSlices * kMmaBatch) {
+    WRow<NBL> wg[kMmaBatch], wu[kMmaBatch];
+#pragma unroll
+    for (int j = 0; j < kMmaBatch; ++j) {
+      const int p = p0 + j * kMmaSlices;
+      if (p < n_act) {
+        const int e = wl.act_e[p];
+        wg[j] = load_wrow<Q, NBL>(ex, blk_gate(ex, e) + roff);
+        wu[j] = load_wrow<Q, NBL>(ex, blk_up(ex, e) + roff);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMmaBatch; ++j) {
+      const int p = p0 + j * kMmaSlices;
+      if (p >= n_act) break;
+      floatx4_t ag = {}, au = {};
+#pragma unroll
+      for (int b = 0; b < NBL; ++b) {
+        const WStage sg = wstage_block<Q>(wg[j].c[2 * b], wg[j].c[2 * b + 1], wg[j].hi[b], wg[j].dm[b]);
+        const WStage su = wstage_block<Q>(wu[j].c[2 * b], wu[j].c[2 * b + 1], wu[j].hi[b], wu[j].dm[b]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sg, t), xf[b][t], ag, 0, 0, 0);
+          au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(su, t), xf[b][t], au, 0, 0, 0);
+        }
+      }
+      // ag[v]: row 4 c + v of the group, token r16
+      if (r16 < kWinT) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          red[wave][j][0][4 * c + v][r16] = ag[v];
+          red[wave][j][1][4 * c + v][r16] = au[v];
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < kMmaBatch * 16 * kWinT; i += kWinThreads) {
+      const int j = i / (16 * kWinT), r = (i / kWinT) % 16, t = i % kWinT;
+      const int p = p0 + j * kMmaSlices;
+      if (p < n_act && ((wl.act_mask[p] >> t) & 1)) {
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWinWaves; ++w) {
+          g += red[w][j][0][r][t];
+          u += red[w][j][1][r][t];
+        }
+        hwin[((size_t)p * kWinT + t) * ex.I + 16 * rgrp + r] = (uint16_t)f32_to_bf16_bits(silu_mul(g, u));
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -284,12 +529,29 @@ __global__ __launch_bounds__(kWinThreads) void win_down(int T, Experts ex, const
   }
 }
 
+inline bool win_mma_ok(const Experts& ex) {
+  return ex.H % 1024 == 0 && ex.H <= kMmaMaxH && ex.I % 16 == 0;
+}
+
 template <int BPR_H, int BPR_I, int Q, bool XF32>
 hipError_t launch_w(const float* logits, int T, int k, const Experts& ex, const void* x,
                     int32_t* idx, float* gates, WinList* meta, uint16_t* hwin, void* y, int out_f32,
                     hipStream_t s) {
-  MOE_LAUNCH("win_gateup", s, (win_gateup<BPR_H, Q, XF32>), dim3(ex.I / win_gu_rows<BPR_H>()),
-             dim3(kWinThreads), 0, s, logits, T, k, ex, x, idx, gates, meta, hwin);
+  if (win_mma_ok(ex)) {
+    const dim3 grid(ex.I / 16 * kMmaSlices);
+    if (ex.H == 1024)
+      MOE_LAUNCH("win_gateup", s, (win_gateup_mma<Q, XF32, 1>), grid, dim3(kWinThreads), 0, s, logits,
+                 T, k, ex, x, idx, gates, meta, hwin);
+    else if (ex.H == 2048)
+      MOE_LAUNCH("win_gateup", s, (win_gateup_mma<Q, XF32, 2>), grid, dim3(kWinThreads), 0, s, logits,
+                 T, k, ex, x, idx, gates, meta, hwin);
+    else
+      MOE_LAUNCH("win_gateup", s, (win_gateup_mma<Q, XF32, 4>), grid, dim3(kWinThreads), 0, s, logits,
+                 T, k, ex, x, idx, gates, meta, hwin);
+  } else {
+    MOE_LAUNCH("win_gateup", s, (win_gateup<BPR_H, Q, XF32>), dim3(ex.I / win_gu_rows<BPR_H>()),
+               dim3(kWinThreads), 0, s, logits, T, k, ex, x, idx, gates, meta, hwin);
+  }
   MOE_LAUNCH("win_down", s, (win_down<BPR_I, Q>), dim3(ex.H / win_dn_rows<BPR_I>()),
              dim3(kWinThreads), 0, s, T, ex, meta, hwin, y, out_f32);
   return hipGetLastError();
