@@ -314,7 +314,8 @@ __global__ __launch_bounds__(kWinThreads) void win_gateup(const float* __restric
 // (lane / 16) feeds 8 weights of block (slice start + NBL c + b) per step, so
 // each lane streams NBL contiguous blocks of its row, and dequantises them in
 // registers (deq16.h). The slices' partial tiles are summed in LDS in slice
-// order (deterministic), then SwiGLU and the h store for routed tokens.
+// order (deterministic), then SwiGLU; h is stored as fp16 in the MFMA K order
+// for every token of the window (the down tiles read all of them).
 constexpr int kMmaSlices = 8;   // expert slices: workgroups per 16-row group
 constexpr int kMmaBatch = 4;    // experts per round
 constexpr int kMmaMaxH = 4096;
@@ -443,14 +444,16 @@ __global__ __launch_bounds__(kWinThreads) void win_gateup_mma(const float* __res
     for (int i = tid; i < kMmaBatch * 16 * kWinT; i += kWinThreads) {
       const int j = i / (16 * kWinT), r = (i / kWinT) % 16, t = i % kWinT;
       const int p = p0 + j * kMmaSlices;
-      if (p < n_act && ((wl.act_mask[p] >> t) & 1)) {
+      if (p < n_act && t < T) {  // every token (finite values) for the down tiles
         float g = 0.f, u = 0.f;
 #pragma unroll
         for (int w = 0; w < kWinWaves; ++w) {
           g += red[w][j][0][r][t];
           u += red[w][j][1][r][t];
         }
-        hwin[((size_t)p * kWinT + t) * ex.I + 16 * rgrp + r] = (uint16_t)f32_to_bf16_bits(silu_mul(g, u));
+        const int kpos = (r & ~3) | ((r & 1) << 1) | ((r >> 1) & 1);  // K order 0, 2, 1, 3
+        const _Float16 hv = (_Float16)silu_mul(g, u);
+        hwin[((size_t)p * kWinT + t) * ex.I + 16 * rgrp + kpos] = __builtin_bit_cast(uint16_t, hv);
       }
     }
     __syncthreads();
@@ -529,8 +532,95 @@ __global__ __launch_bounds__(kWinThreads) void win_down(int T, Experts ex, const
   }
 }
 
+// Down projection + combine on the matrix cores (I = 256 or 512).
+// Workgroup g owns rows 16g .. 16g + 15 of H for every active expert; wave w
+// takes K half w & 1 and the experts w / 2, w / 2 + 4, ...: per expert a
+// 16-row x 16-token tile (tokens past T zero) on v_mfma_f32_16x16x32_f16 with
+// h (fp16, MFMA K order) as the token operand, scaled by the routing gates and
+// summed in registers; the eight partial tiles are added in LDS in wave order
+// and the workgroup writes y.
+template <int Q, int NBL>
+__global__ __launch_bounds__(kWinThreads) void win_down_mma(int T, Experts ex, const WinList* gmeta,
+                                                            const uint16_t* hwin, void* y,
+                                                            int out_f32) {
+  __shared__ WinList wl;
+  __shared__ float red[kWinWaves][16][kWinT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int I = ex.I;
+  const int n_act = gmeta->n_act;
+  for (int p = tid; p < n_act; p += kWinThreads) {
+    wl.act_e[p] = gmeta->act_e[p];
+#pragma unroll
+    for (int t = 0; t < kWinT; ++t) wl.act_gate[p][t] = gmeta->act_gate[p][t];
+  }
+  __syncthreads();
+  const int c = lane >> 4, r16 = lane & 15;
+  const int ks = wave & 1, eq = wave >> 1;
+  const int kb0 = ks * (I / 64) + NBL * c;  // this lane's first block of the wave's K half
+  const size_t roff = (size_t)(16 * blockIdx.x + r16) * (I / 32) + kb0;
+  const bool tok = r16 < T;
+  floatx4_t acc = {};
+  auto load_h = [&](int p, half8_t (&hf)[NBL][4]) {
+    const _Float16* hp = reinterpret_cast<const _Float16*>(hwin) + ((size_t)p * kWinT + r16) * I;
+#pragma unroll
+    for (int b = 0; b < NBL; ++b)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        half8_t v = {};
+        if (tok) v = *reinterpret_cast<const half8_t*>(hp + 32 * (kb0 + b) + 8 * t);
+        hf[b][t] = v;
+      }
+  };
+  // up to kDnBatch experts per round: all their weight loads in flight at once,
+  // h (written by the gate/up kernel, in L2) double-buffered one expert ahead
+  constexpr int kDnBatch = 8;
+  for (int p0 = eq; p0 < n_act; p0 += 4 * kDnBatch) {
+    WRow<NBL> wd[kDnBatch];
+#pragma unroll
+    for (int j = 0; j < kDnBatch; ++j) {
+      const int p = p0 + 4 * j;
+      if (p < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[p]) + roff);
+    }
+    half8_t hf[2][NBL][4];
+    load_h(p0, hf[0]);
+#pragma unroll
+    for (int j = 0; j < kDnBatch; ++j) {
+      const int p = p0 + 4 * j;
+      if (p >= n_act) break;
+      if (j + 1 < kDnBatch && p + 4 < n_act) load_h(p + 4, hf[(j + 1) & 1]);
+      floatx4_t o = {};
+#pragma unroll
+      for (int b = 0; b < NBL; ++b) {
+        const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          o = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sw, t), hf[j & 1][b][t], o, 0, 0, 0);
+      }
+      const float g = tok ? wl.act_gate[p][r16] : 0.f;  // o[v]: row 4 c + v, token r16
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += g * o[v];
+    }
+  }
+  if (r16 < kWinT) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][4 * c + v][r16] = acc[v];
+  }
+  __syncthreads();
+  if (tid < 16 * kWinT) {
+    const int r = tid / kWinT, t = tid % kWinT;
+    if (t < T) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWinWaves; ++w) s += red[w][r][t];
+      const size_t o = (size_t)t * ex.H + 16 * blockIdx.x + r;
+      if (out_f32) static_cast<float*>(y)[o] = s;
+      else static_cast<uint16_t*>(y)[o] = (uint16_t)f32_to_bf16_bits(s);
+    }
+  }
+}
+
 inline bool win_mma_ok(const Experts& ex) {
-  return ex.H % 1024 == 0 && ex.H <= kMmaMaxH && ex.I % 16 == 0;
+  return ex.H % 1024 == 0 && ex.H <= kMmaMaxH && (ex.I == 256 || ex.I == 512);
 }
 
 template <int BPR_H, int BPR_I, int Q, bool XF32>
@@ -552,8 +642,18 @@ hipError_t launch_w(const float* logits, int T, int k, const Experts& ex, const 
     MOE_LAUNCH("win_gateup", s, (win_gateup<BPR_H, Q, XF32>), dim3(ex.I / win_gu_rows<BPR_H>()),
                dim3(kWinThreads), 0, s, logits, T, k, ex, x, idx, gates, meta, hwin);
   }
-  MOE_LAUNCH("win_down", s, (win_down<BPR_I, Q>), dim3(ex.H / win_dn_rows<BPR_I>()),
-             dim3(kWinThreads), 0, s, T, ex, meta, hwin, y, out_f32);
+  if (win_mma_ok(ex)) {
+    const dim3 grid(ex.H / 16);
+    if (ex.I == 256)
+      MOE_LAUNCH("win_down", s, (win_down_mma<Q, 1>), grid, dim3(kWinThreads), 0, s, T, ex, meta,
+                 hwin, y, out_f32);
+    else
+      MOE_LAUNCH("win_down", s, (win_down_mma<Q, 2>), grid, dim3(kWinThreads), 0, s, T, ex, meta,
+                 hwin, y, out_f32);
+  } else {
+    MOE_LAUNCH("win_down", s, (win_down<BPR_I, Q>), dim3(ex.H / win_dn_rows<BPR_I>()),
+               dim3(kWinThreads), 0, s, T, ex, meta, hwin, y, out_f32);
+  }
   return hipGetLastError();
 }
 
