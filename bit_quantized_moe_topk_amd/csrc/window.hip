@@ -374,8 +374,9 @@ __global__ __launch_bounds__(kWinThreads) void win_gateup_mma(const float* __res
   WinList& wl = R.wl;
 
   win_topk(R, logits, T, ex.E, k);
-  // the window's activations -> LDS fp16 in the MFMA K order; tokens >= T zero
-  for (int i = tid; i < kWinT * H / 4; i += kWinThreads) {
+  // the window's activations -> LDS fp16 in the MFMA K order (tokens >= T
+  // zero), by the waves that do not select experts
+  for (int i = tid - 64 * kWinT; i >= 0 && i < kWinT * H / 4; i += kWinThreads - 64 * kWinT) {
     const int t = i / (H / 4), q = i % (H / 4);
     float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
     if (t < T) {
