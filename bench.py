@@ -141,7 +141,7 @@ def build_instances(cfg, n: int, seed: int, keep_host: int = 0):
     fws_n = insts[0].ex.workspace_size(cfg.T, cfg.k, 0)
     fws = torch.empty(fws_n, dtype=torch.uint8, device="cuda")
     lws_n = L.moe_layer_workspace_size(insts[0].ex.handle, cfg.T, cfg.k, 0)
-    lws = torch.empty(lws_n, dtype=torch.uint8, device="cuda")
+    lws = torch.zeros(lws_n, dtype=torch.uint8, device="cuda")  # head: window counters
     for it in insts:
         it.bind(gws, fws, lws)
     return insts, hosts, (gws, fws, lws)
@@ -268,9 +268,13 @@ def run_decode(cfg, args):
     prof = kernel_profile(insts, L, stream, K)
     pb = expert_plane_bytes(cfg)
     step_layers = [stats[s % len(insts)] for s in range(K)]
-    kname = max((k for k in prof if k in ("win_gateup", "gemv_gateup", "win_down", "gemv_down")),
+    kname = max((k for k in prof
+                 if k in ("win_layer", "win_gateup", "gemv_gateup", "win_down", "gemv_down")),
                 key=lambda k: prof[k][1])
-    unit = pb["gateup"] if "gateup" in kname else pb["down"]
+    if kname == "win_layer":  # the whole window in one kernel: gate/up and down planes
+        unit = pb["gateup"] + pb["down"]
+    else:
+        unit = pb["gateup"] if "gateup" in kname else pb["down"]
     per_step_units = [st["touched"] if kname.startswith("win") else st["gemv_experts"]
                       for st in step_layers]
     k_bytes = sum(per_step_units) * unit

@@ -284,7 +284,10 @@ def ffn_q(x: torch.Tensor, ex: Experts, idx: torch.Tensor, gates: torch.Tensor,
 
 def layer(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fast",
           workspace: torch.Tensor | None = None):
-    """The whole layer (route, group, expert FFN, combine): returns (idx, gates, y)."""
+    """The whole layer (route, group, expert FFN, combine): returns (idx, gates, y).
+
+    A caller-provided `workspace` (uint8, at least moe_layer_workspace_size
+    bytes) must start zero-filled; the calls keep its first 8192 bytes zero."""
     mode = _MODES[mode]
     _need_cuda("logits", logits, torch.float32)
     _need_cuda("x", x, (torch.float32, torch.bfloat16))
@@ -297,8 +300,8 @@ def layer(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fa
     ydtype = torch.float32 if mode == CHECK_F32 else x.dtype
     y = torch.empty((T, H), dtype=ydtype, device=dev)
     nbytes = int(lib().moe_layer_workspace_size(ex.handle, T, k, mode))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if workspace is None:  # zero-filled: its head holds the decode window's counters
+        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
     xdt = F32 if x.dtype == torch.float32 else BF16
     _check("moe_layer", lib().moe_layer(_ptr(logits), _ptr(x), xdt, T, ex.handle, k, _ptr(idx),
                                         _ptr(gates), _ptr(y), mode, _ptr(workspace),

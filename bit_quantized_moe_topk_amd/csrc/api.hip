@@ -251,7 +251,7 @@ LayerLayout layer_layout(const Experts& d, int T, int k, int mode) {
     return L;
   }
   const size_t A = (size_t)T * (k + d.has_shared);
-  size_t off = 0;
+  size_t off = moe::kWinSyncBytes;  // kept zero for the decode window's counters
   L.counts = off;  off = align_up(off + sizeof(int32_t) * (d.E + 1));
   L.offsets = off; off = align_up(off + sizeof(int32_t) * (d.E + 2));
   L.perm = off;    off = align_up(off + sizeof(int32_t) * (A ? A : 1));

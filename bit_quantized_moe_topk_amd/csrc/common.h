@@ -112,6 +112,9 @@ struct FfnArgs {
 hipError_t launch_ffn_check(const Experts& ex, const FfnArgs& a, hipStream_t s);
 bool gemv_supported(int H, int I);
 // The two-kernel whole-layer path for a decode verify window (T <= 4).
+// Bytes at the head of every moe_layer workspace kept for the one-launch
+// decode window's counters (zero between calls; no other call form writes them).
+constexpr size_t kWinSyncBytes = 8192;
 bool window_supported(const Experts& ex, int T, int k);
 size_t window_workspace_bytes(const Experts& ex, int T, int k);
 hipError_t launch_window(const float* logits, int T, int k, const Experts& ex, const void* x,

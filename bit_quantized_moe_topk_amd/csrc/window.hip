@@ -83,7 +83,6 @@ constexpr int win_gu_rows() {  // pair-rows of I per workgroup
   return 64 / BPR > 2 ? 64 / BPR : 2;
 }
 constexpr int kWinWaves = kWinThreads / 64;
-constexpr int kWinGroups = 4;  // expert groups of the down kernel
 template <int BPR>
 constexpr int win_dn_rows() {  // rows of H per down workgroup: two row groups
   return 2 * (64 / BPR);
@@ -92,6 +91,7 @@ constexpr int kWinBatch = 4;   // experts whose weights a wave has in flight at 
 
 // LDS state of the window's routing, built by every workgroup.
 struct WinRoute {
+  static constexpr bool kSlow = true;  // room for more than 64 assignments
   int lidx[kWinT * kWinMaxK];
   float lgate[kWinT * kWinMaxK];
   int flag[MOE_MAX_E_DEV + 1];
@@ -103,18 +103,78 @@ struct WinRoute {
   TopkScratch tks[kWinT];
 };
 
+// The same for at most 64 assignments (T k <= 64), without the scan arrays.
+struct LayerRoute {
+  static constexpr bool kSlow = false;
+  int lidx[64];
+  float lgate[64];
+  uint32_t bits[64];
+  int pref[64];
+  WinList wl;
+  TopkScratch tks[kWinT];
+};
+
 // Routing, part 1: wave t selects token t's experts into LDS. Called before
 // the activation loads: loads complete in order, so the logits must not queue
 // behind them.
-__device__ inline void win_topk(WinRoute& R, const float* __restrict__ logits, int T, int E, int k) {
+// PER > 0: the lane count is fixed (E <= 64 PER), which bounds the registers.
+template <int PER = 0, typename RT>
+__device__ inline void win_topk(RT& R, const float* __restrict__ logits, int T, int E, int k) {
   const int wave = threadIdx.x >> 6;
-  if (wave < T)
-    topk_any(logits + (size_t)wave * E, E, k, R.lidx + wave * k, R.lgate + wave * k, &R.tks[wave]);
+  if (wave < T) {
+    const float* l = logits + (size_t)wave * E;
+    if (PER > 0) topk_token<(PER > 0 ? PER : 1)>(l, E, k, R.lidx + wave * k, R.lgate + wave * k, &R.tks[wave]);
+    else topk_any(l, E, k, R.lidx + wave * k, R.lgate + wave * k, &R.tks[wave]);
+  }
 }
 
 __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// More than 64 assignments: token masks per expert, a block scan over the
+// expert flags gives the ranks.
+__device__ inline int win_list_scan(WinRoute& R, const Experts& ex, int T, int k, bool publish,
+                                    int32_t* idx_out, float* gates_out, WinList* gmeta) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int E = ex.E, E_tot = ex.E_tot;
+  for (int e = tid; e < E_tot; e += NT) R.tmask[e] = 0;
+  __syncthreads();
+  for (int a = tid; a < T * k; a += NT) atomicOr(&R.tmask[R.lidx[a]], 1 << (a / k));
+  if (ex.has_shared && tid == 0) R.tmask[E] = (1 << T) - 1;
+  __syncthreads();
+  for (int e = tid; e < E_tot; e += NT) R.flag[e] = R.tmask[e] != 0;
+  __syncthreads();
+  const int n_act = block_exclusive_scan(R.flag, E_tot, R.wsum);
+  for (int e = tid; e < E_tot; e += NT) {
+    if (R.tmask[e]) {
+      const int p = R.flag[e];
+      R.wl.act_e[p] = e;
+      R.wl.act_mask[p] = R.tmask[e];
+#pragma unroll
+      for (int t = 0; t < kWinT; ++t) R.wl.act_gate[p][t] = 0.f;
+    }
+  }
+  if (tid == 0) R.wl.n_act = n_act;
+  __syncthreads();
+  for (int a = tid; a < T * k; a += NT) R.wl.act_gate[R.flag[R.lidx[a]]][a / k] = R.lgate[a];
+  if (ex.has_shared && tid < T) R.wl.act_gate[R.flag[E]][tid] = 1.0f;
+  __syncthreads();
+  if (publish) {
+    for (int a = tid; a < T * k; a += NT) {
+      idx_out[a] = R.lidx[a];
+      gates_out[a] = R.lgate[a];
+    }
+    if (gmeta && tid == 0) gmeta->n_act = n_act;
+    for (int p = tid; gmeta && p < n_act; p += NT) {
+      gmeta->act_e[p] = R.wl.act_e[p];
+      gmeta->act_mask[p] = R.wl.act_mask[p];
+#pragma unroll
+      for (int t = 0; t < kWinT; ++t) gmeta->act_gate[p][t] = R.wl.act_gate[p][t];
+    }
+  }
+  return n_act;
 }
 
 // Routing, part 2: the active-expert list (ascending expert, shared last) with
@@ -125,10 +185,11 @@ __device__ inline void wave_sync_lds() {
 // assignments set bits of an expert bitmap, a scan over its 64 words gives
 // every expert its rank (the number of routed experts below it), and each
 // assignment writes its expert, token bit and gate at that rank.
-__device__ inline int win_list(WinRoute& R, const Experts& ex, int T, int k, int32_t* idx_out,
-                               float* gates_out, WinList* gmeta) {
+template <typename RT>
+__device__ inline int win_list(RT& R, const Experts& ex, int T, int k, bool publish,
+                               int32_t* idx_out, float* gates_out, WinList* gmeta) {
   const int tid = threadIdx.x, NT = blockDim.x;
-  const int E = ex.E, E_tot = ex.E_tot;
+  const int E = ex.E;
   const int A = T * k;
   if (A <= 64) {
     __syncthreads();  // the top-k waves' lidx, lgate
@@ -173,13 +234,13 @@ __device__ inline int win_list(WinRoute& R, const Experts& ex, int T, int k, int
     }
     __syncthreads();
     const int n_act = R.wl.n_act;
-    if (blockIdx.x == 0) {
+    if (publish) {
       for (int a = tid; a < A; a += NT) {
         idx_out[a] = R.lidx[a];
         gates_out[a] = R.lgate[a];
       }
-      if (tid == 0) gmeta->n_act = n_act;
-      for (int p = tid; p < n_act; p += NT) {
+      if (gmeta && tid == 0) gmeta->n_act = n_act;
+      for (int p = tid; gmeta && p < n_act; p += NT) {
         gmeta->act_e[p] = R.wl.act_e[p];
         gmeta->act_mask[p] = R.wl.act_mask[p];
 #pragma unroll
@@ -188,42 +249,8 @@ __device__ inline int win_list(WinRoute& R, const Experts& ex, int T, int k, int
     }
     return n_act;
   }
-  for (int e = tid; e < E_tot; e += NT) R.tmask[e] = 0;
-  __syncthreads();
-  for (int a = tid; a < T * k; a += NT) atomicOr(&R.tmask[R.lidx[a]], 1 << (a / k));
-  if (ex.has_shared && tid == 0) R.tmask[E] = (1 << T) - 1;
-  __syncthreads();
-  for (int e = tid; e < E_tot; e += NT) R.flag[e] = R.tmask[e] != 0;
-  __syncthreads();
-  const int n_act = block_exclusive_scan(R.flag, E_tot, R.wsum);
-  for (int e = tid; e < E_tot; e += NT) {
-    if (R.tmask[e]) {
-      const int p = R.flag[e];
-      R.wl.act_e[p] = e;
-      R.wl.act_mask[p] = R.tmask[e];
-#pragma unroll
-      for (int t = 0; t < kWinT; ++t) R.wl.act_gate[p][t] = 0.f;
-    }
-  }
-  if (tid == 0) R.wl.n_act = n_act;
-  __syncthreads();
-  for (int a = tid; a < T * k; a += NT) R.wl.act_gate[R.flag[R.lidx[a]]][a / k] = R.lgate[a];
-  if (ex.has_shared && tid < T) R.wl.act_gate[R.flag[E]][tid] = 1.0f;
-  __syncthreads();
-  if (blockIdx.x == 0) {
-    for (int a = tid; a < T * k; a += NT) {
-      idx_out[a] = R.lidx[a];
-      gates_out[a] = R.lgate[a];
-    }
-    if (tid == 0) gmeta->n_act = n_act;
-    for (int p = tid; p < n_act; p += NT) {
-      gmeta->act_e[p] = R.wl.act_e[p];
-      gmeta->act_mask[p] = R.wl.act_mask[p];
-#pragma unroll
-      for (int t = 0; t < kWinT; ++t) gmeta->act_gate[p][t] = R.wl.act_gate[p][t];
-    }
-  }
-  return n_act;
+  if constexpr (RT::kSlow) return win_list_scan(R, ex, T, k, publish, idx_out, gates_out, gmeta);
+  return 0;  // not reached: callers with this state keep T k <= 64
 }
 
 template <int BPR, int Q, bool XF32>
@@ -243,7 +270,7 @@ __global__ __launch_bounds__(kWinThreads) void win_gateup(const float* __restric
     if (t < T) load_x_row<Q, XF32>(x, ex.H, t, b, xb[t]);
     else zero_xb(xb[t]);
   }
-  const int n_act = win_list(R, ex, T, k, idx_out, gates_out, gmeta);
+  const int n_act = win_list(R, ex, T, k, blockIdx.x == 0, idx_out, gates_out, gmeta);
 
   // gate/up + SwiGLU for this workgroup's pair-rows; wave w takes the active
   // experts w, w + 8, ..., kWinBatch at a time with all their loads in flight
@@ -358,109 +385,6 @@ __device__ inline WRow<NBL> load_wrow(const Experts& ex, size_t blk) {
   return w;
 }
 
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-
-template <int Q, bool XF32, int NBL>
-__global__ __launch_bounds__(kWinThreads) void win_gateup_mma(const float* __restrict__ logits,
-                                                              int T, int k, Experts ex,
-                                                              const void* x, int32_t* idx_out,
-                                                              float* gates_out, WinList* gmeta,
-                                                              uint16_t* hwin) {
-  __shared__ WinRoute R;
-  __shared__ __attribute__((aligned(16))) _Float16 xs[kWinT * kMmaMaxH];
-  __shared__ float red[kWinWaves][kMmaBatch][2][16][kWinT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = ex.H;
-  WinList& wl = R.wl;
-
-  win_topk(R, logits, T, ex.E, k);
-  // the window's activations -> LDS fp16 in the MFMA K order (tokens >= T
-  // zero), by the waves that do not select experts
-  for (int i = tid - 64 * kWinT; i >= 0 && i < kWinT * H / 4; i += kWinThreads - 64 * kWinT) {
-    const int t = i / (H / 4), q = i % (H / 4);
-    float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-    if (t < T) {
-      if (XF32) {
-        const float4 f = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)t * H)[q];
-        v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
-      } else {
-        const uint2 u = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)t * H)[q];
-        v0 = bf16_lo(u.x); v1 = bf16_hi(u.x); v2 = bf16_lo(u.y); v3 = bf16_hi(u.y);
-      }
-    }
-    *reinterpret_cast<uint2*>(xs + t * H + 4 * q) = make_uint2(pack_half2(v0, v2), pack_half2(v1, v3));
-  }
-  const int n_act = win_list(R, ex, T, k, idx_out, gates_out, gmeta);  // ends with a barrier
-
-  const int rgrp = blockIdx.x / kMmaSlices, es = blockIdx.x % kMmaSlices;
-  const int c = lane >> 4, r16 = lane & 15;
-  const int kb0 = wave * (H / 256) + NBL * c;  // this lane's first block of the wave's slice
-  half8_t xf[NBL][4];  // B operand: token r16, the same K as the lane's weights
-#pragma unroll
-  for (int b = 0; b < NBL; ++b)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      half8_t v = {};
-      if (r16 < T) v = *reinterpret_cast<const half8_t*>(xs + r16 * H + 32 * (kb0 + b) + 8 * t);
-      xf[b][t] = v;
-    }
-  const size_t roff = (size_t)(16 * rgrp + r16) * (H / 32) + kb0;
-
-  for (int p0 = es; p0 < n_act; p0 += kMmaSlices * kMmaBatch) {
-    WRow<NBL> wg[kMmaBatch], wu[kMmaBatch];
-#pragma unroll
-    for (int j = 0; j < kMmaBatch; ++j) {
-      const int p = p0 + j * kMmaSlices;
-      if (p < n_act) {
-        const int e = wl.act_e[p];
-        wg[j] = load_wrow<Q, NBL>(ex, blk_gate(ex, e) + roff);
-        wu[j] = load_wrow<Q, NBL>(ex, blk_up(ex, e) + roff);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kMmaBatch; ++j) {
-      const int p = p0 + j * kMmaSlices;
-      if (p >= n_act) break;
-      floatx4_t ag = {}, au = {};
-#pragma unroll
-      for (int b = 0; b < NBL; ++b) {
-        const WStage sg = wstage_block<Q>(wg[j].c[2 * b], wg[j].c[2 * b + 1], wg[j].hi[b], wg[j].dm[b]);
-        const WStage su = wstage_block<Q>(wu[j].c[2 * b], wu[j].c[2 * b + 1], wu[j].hi[b], wu[j].dm[b]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sg, t), xf[b][t], ag, 0, 0, 0);
-          au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(su, t), xf[b][t], au, 0, 0, 0);
-        }
-      }
-      // ag[v]: row 4 c + v of the group, token r16
-      if (r16 < kWinT) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          red[wave][j][0][4 * c + v][r16] = ag[v];
-          red[wave][j][1][4 * c + v][r16] = au[v];
-        }
-      }
-    }
-    __syncthreads();
-    for (int i = tid; i < kMmaBatch * 16 * kWinT; i += kWinThreads) {
-      const int j = i / (16 * kWinT), r = (i / kWinT) % 16, t = i % kWinT;
-      const int p = p0 + j * kMmaSlices;
-      if (p < n_act && t < T) {  // every token (finite values) for the down tiles
-        float g = 0.f, u = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWinWaves; ++w) {
-          g += red[w][j][0][r][t];
-          u += red[w][j][1][r][t];
-        }
-        const int kpos = (r & ~3) | ((r & 1) << 1) | ((r >> 1) & 1);  // K order 0, 2, 1, 3
-        const _Float16 hv = (_Float16)silu_mul(g, u);
-        hwin[((size_t)p * kWinT + t) * ex.I + 16 * rgrp + kpos] = __builtin_bit_cast(uint16_t, hv);
-      }
-    }
-    __syncthreads();
-  }
-}
-
 // Down projection + combine. A workgroup owns R = 2 * RPI rows of H for every
 // active expert: wave w takes row group w % 2 and the experts q, q + 4, ...
 // with q = w / 2, and sums gate * o over them in registers; the four expert
@@ -533,73 +457,176 @@ __global__ __launch_bounds__(kWinThreads) void win_down(int T, Experts ex, const
   }
 }
 
-// Down projection + combine on the matrix cores (I = 256 or 512).
-// Workgroup g owns rows 16g .. 16g + 15 of H for every active expert; wave w
-// takes K half w & 1 and the experts w / 2, w / 2 + 4, ...: per expert a
-// 16-row x 16-token tile (tokens past T zero) on v_mfma_f32_16x16x32_f16 with
-// h (fp16, MFMA K order) as the token operand, scaled by the routing gates and
-// summed in registers; the eight partial tiles are added in LDS in wave order
-// and the workgroup writes y.
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// Gate/up role: rows 16 rgrp .. 16 rgrp + 15 of I for the active experts es,
+// es + 8, ... (es = role % 8). xs holds the window's activations (fp16, MFMA K
+// order). Ends after the last h store of the role, behind a barrier.
 template <int Q, int NBL>
-__global__ __launch_bounds__(kWinThreads) void win_down_mma(int T, Experts ex, const WinList* gmeta,
-                                                            const uint16_t* hwin, void* y,
-                                                            int out_f32) {
-  __shared__ WinList wl;
-  __shared__ float red[kWinWaves][16][kWinT];
+__device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T, const Experts& ex,
+                                   const _Float16* xs,
+                                   float (&red)[kWinWaves][kMmaBatch][2][16][kWinT],
+                                   uint16_t* hwin) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = ex.H;
+  const int rgrp = role / kMmaSlices, es = role % kMmaSlices;
+  const int c = lane >> 4, r16 = lane & 15;
+  const int kb0 = wave * (H / 256) + NBL * c;  // this lane's first block of the wave's slice
+  half8_t xf[NBL][4];  // B operand: token r16, the same K as the lane's weights
+#pragma unroll
+  for (int b = 0; b < NBL; ++b)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      half8_t v = {};
+      if (r16 < T) v = *reinterpret_cast<const half8_t*>(xs + r16 * H + 32 * (kb0 + b) + 8 * t);
+      xf[b][t] = v;
+    }
+  const size_t roff = (size_t)(16 * rgrp + r16) * (H / 32) + kb0;
+
+  for (int p0 = es; p0 < n_act; p0 += kMmaSlices * kMmaBatch) {
+    WRow<NBL> wg[kMmaBatch], wu[kMmaBatch];
+#pragma unroll
+    for (int j = 0; j < kMmaBatch; ++j) {
+      const int p = p0 + j * kMmaSlices;
+      if (p < n_act) {
+        const int e = wl.act_e[p];
+        wg[j] = load_wrow<Q, NBL>(ex, blk_gate(ex, e) + roff);
+        wu[j] = load_wrow<Q, NBL>(ex, blk_up(ex, e) + roff);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMmaBatch; ++j) {
+      const int p = p0 + j * kMmaSlices;
+      if (p >= n_act) break;
+      floatx4_t ag = {}, au = {};
+#pragma unroll
+      for (int b = 0; b < NBL; ++b) {
+        const WStage sg = wstage_block<Q>(wg[j].c[2 * b], wg[j].c[2 * b + 1], wg[j].hi[b], wg[j].dm[b]);
+        const WStage su = wstage_block<Q>(wu[j].c[2 * b], wu[j].c[2 * b + 1], wu[j].hi[b], wu[j].dm[b]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sg, t), xf[b][t], ag, 0, 0, 0);
+          au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(su, t), xf[b][t], au, 0, 0, 0);
+        }
+      }
+      // ag[v]: row 4 c + v of the group, token r16
+      if (r16 < kWinT) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          red[wave][j][0][4 * c + v][r16] = ag[v];
+          red[wave][j][1][4 * c + v][r16] = au[v];
+        }
+      }
+    }
+    __syncthreads();
+    // rows 4 q + s and 4 q + s + 2 (s = 0, 1) sit side by side in the K
+    // order (0, 2, 1, 3): one 32-bit store each, coherent across the chip
+    // (agent scope) for the down roles that read h in the same launch
+    for (int i = tid; i < kMmaBatch * 8 * kWinT; i += kWinThreads) {
+      const int j = i / (8 * kWinT), pr = (i / kWinT) % 8, t = i % kWinT;
+      const int p = p0 + j * kMmaSlices;
+      if (p < n_act && t < T) {  // every token (finite values) for the down tiles
+        const int ra = 4 * (pr >> 1) + (pr & 1), rb = ra + 2;
+        float ga = 0.f, ua = 0.f, gb = 0.f, ub = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWinWaves; ++w) {
+          ga += red[w][j][0][ra][t];
+          ua += red[w][j][1][ra][t];
+          gb += red[w][j][0][rb][t];
+          ub += red[w][j][1][rb][t];
+        }
+        uint32_t* dst = reinterpret_cast<uint32_t*>(hwin + ((size_t)p * kWinT + t) * ex.I + 16 * rgrp +
+                                                    4 * (pr >> 1) + 2 * (pr & 1));
+        __hip_atomic_store(dst, pack_half2(silu_mul(ga, ua), silu_mul(gb, ub)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Down role: rows 16 grp .. 16 grp + 15 of H for every active expert; wave w
+// takes K half w & 1 and the experts w / 2, w / 2 + 4, ...: per expert a
+// 16-row x 16-token tile (tokens past T zero) with h (fp16, MFMA K order) as
+// the token operand, scaled by the routing gates and summed in registers; the
+// eight partial tiles are added in LDS in wave order and the role writes its
+// rows of y. The first round's weights are requested before wait(), which
+// returns once h is complete (false: it never was; the rows become NaN). h
+// then comes into LDS (hs, kHsBytes) a phase of experts at a time, every load
+// of a phase in flight at once.
+constexpr int kDnBatch = 4;           // experts per wave whose weights are in registers
+constexpr int kHsBytes = 64 * 1024;   // LDS for h: 16 experts at I = 512, 32 at I = 256
+
+template <int Q, int NBL, typename Wait>
+__device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, const Experts& ex,
+                                 const uint16_t* hwin, void* y, int out_f32, _Float16* hs,
+                                 float (&red)[kWinWaves][16][kWinT], Wait&& wait) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int I = ex.I;
-  const int n_act = gmeta->n_act;
-  for (int p = tid; p < n_act; p += kWinThreads) {
-    wl.act_e[p] = gmeta->act_e[p];
-#pragma unroll
-    for (int t = 0; t < kWinT; ++t) wl.act_gate[p][t] = gmeta->act_gate[p][t];
-  }
-  __syncthreads();
   const int c = lane >> 4, r16 = lane & 15;
   const int ks = wave & 1, eq = wave >> 1;
   const int kb0 = ks * (I / 64) + NBL * c;  // this lane's first block of the wave's K half
-  const size_t roff = (size_t)(16 * blockIdx.x + r16) * (I / 32) + kb0;
+  const size_t roff = (size_t)(16 * grp + r16) * (I / 32) + kb0;
   const bool tok = r16 < T;
-  floatx4_t acc = {};
-  auto load_h = [&](int p, half8_t (&hf)[NBL][4]) {
-    const _Float16* hp = reinterpret_cast<const _Float16*>(hwin) + ((size_t)p * kWinT + r16) * I;
-#pragma unroll
-    for (int b = 0; b < NBL; ++b)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        half8_t v = {};
-        if (tok) v = *reinterpret_cast<const half8_t*>(hp + 32 * (kb0 + b) + 8 * t);
-        hf[b][t] = v;
-      }
-  };
-  // up to kDnBatch experts per round: all their weight loads in flight at once,
-  // h (written by the gate/up kernel, in L2) double-buffered one expert ahead
-  constexpr int kDnBatch = 8;
-  for (int p0 = eq; p0 < n_act; p0 += 4 * kDnBatch) {
-    WRow<NBL> wd[kDnBatch];
+  const int per_phase = kHsBytes / (kWinT * I * 2);  // experts whose h fits in hs
+  WRow<NBL> wd[kDnBatch];
+  auto load_round = [&](int p0) {
 #pragma unroll
     for (int j = 0; j < kDnBatch; ++j) {
       const int p = p0 + 4 * j;
       if (p < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[p]) + roff);
     }
-    half8_t hf[2][NBL][4];
-    load_h(p0, hf[0]);
+  };
+  load_round(eq);
+  const bool ok = wait();
+  floatx4_t acc = {};
+  for (int r0 = 0; r0 < n_act; r0 += 4 * kDnBatch) {  // rounds: weights of 4 kDnBatch experts
+    if (r0 > 0) load_round(r0 + eq);
+    const int r1 = min(n_act, r0 + 4 * kDnBatch);
+    for (int ph0 = r0; ph0 < r1; ph0 += per_phase) {
+      const int n16 = min(per_phase, r1 - ph0) * kWinT * I / 8;
+      const uint4* src = reinterpret_cast<const uint4*>(hwin) + (size_t)ph0 * kWinT * I / 8;
+      // straight into LDS (each lane's 16 bytes land at the wave's base + 16
+      // lane), no registers held; every load of the phase in flight at once,
+      // agent-coherent (h was written in this launch on other CUs)
+      constexpr int kCopy = kHsBytes / 16 / kWinThreads;
+      constexpr int kCoherent = 16;  // cache policy: agent scope
+      __syncthreads();  // the previous phase's reads of hs are done
 #pragma unroll
-    for (int j = 0; j < kDnBatch; ++j) {
-      const int p = p0 + 4 * j;
-      if (p >= n_act) break;
-      if (j + 1 < kDnBatch && p + 4 < n_act) load_h(p + 4, hf[(j + 1) & 1]);
-      floatx4_t o = {};
+      for (int u = 0; u < kCopy; ++u)
+        if (tid + u * kWinThreads < n16)
+          __builtin_amdgcn_global_load_lds(
+              src + tid + u * kWinThreads,
+              (__attribute__((address_space(3))) void*)(reinterpret_cast<uint4*>(hs) + u * kWinThreads +
+                                                        64 * wave),
+              16, 0, kCoherent);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the LDS writes have landed
+      __syncthreads();
 #pragma unroll
-      for (int b = 0; b < NBL; ++b) {
-        const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
+      for (int j = 0; j < kDnBatch; ++j) {
+        const int p = r0 + eq + 4 * j;
+        if (p < ph0 || p >= ph0 + per_phase || p >= n_act) continue;
+        // columns past T read token 0's row (finite; their gate is 0): no
+        // branch, so all eight LDS reads of the expert issue together
+        const _Float16* hp = hs + ((size_t)(p - ph0) * kWinT + (tok ? r16 : 0)) * I;
+        half8_t hv[NBL][4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          o = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sw, t), hf[j & 1][b][t], o, 0, 0, 0);
+        for (int b = 0; b < NBL; ++b)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) hv[b][t] = *reinterpret_cast<const half8_t*>(hp + 32 * (kb0 + b) + 8 * t);
+        floatx4_t o = {};
+#pragma unroll
+        for (int b = 0; b < NBL; ++b) {
+          const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sw, t), hv[b][t], o, 0, 0, 0);
+        }
+        const float ga = wl.act_gate[p][r16 & (kWinT - 1)];
+        const float g = tok ? ga : 0.f;  // o[v]: row 4 c + v, token r16
+#pragma unroll
+        for (int v2 = 0; v2 < 4; ++v2) acc[v2] += g * o[v2];
       }
-      const float g = tok ? wl.act_gate[p][r16] : 0.f;  // o[v]: row 4 c + v, token r16
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += g * o[v];
     }
   }
   if (r16 < kWinT) {
@@ -613,48 +640,172 @@ __global__ __launch_bounds__(kWinThreads) void win_down_mma(int T, Experts ex, c
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < kWinWaves; ++w) s += red[w][r][t];
-      const size_t o = (size_t)t * ex.H + 16 * blockIdx.x + r;
+      if (!ok) s = __uint_as_float(0x7FC00000u);
+      const size_t o = (size_t)t * ex.H + 16 * grp + r;
       if (out_f32) static_cast<float*>(y)[o] = s;
       else static_cast<uint16_t*>(y)[o] = (uint16_t)f32_to_bf16_bits(s);
     }
   }
 }
 
-inline bool win_mma_ok(const Experts& ex) {
-  return ex.H % 1024 == 0 && ex.H <= kMmaMaxH && (ex.I == 256 || ex.I == 512);
+// Counters of the one-launch window, at the head of the workspace, each on a
+// 128-byte line of its own (atomics on one address serialise, so every counter
+// is shared by at most 16 workgroups). Zero when a launch starts; the launch's
+// last down workgroup zeroes them again. `guard` is never written: non-zero
+// means the head was not zeroed.
+constexpr int kSyncGroup = 16;   // workgroups per counter
+constexpr int kSyncLine = 32;    // uint32 per 128-byte line
+struct WinSync {
+  uint32_t guard[kSyncLine];
+  uint32_t up[16][kSyncLine];    // gate/up roles of group g whose h is released
+  uint32_t dn[16][kSyncLine];    // down roles of group g finished
+  uint32_t dn_all[kSyncLine];    // down groups finished
+};
+static_assert(sizeof(WinSync) <= kWinSyncBytes, "the window counters fit the workspace head");
+
+constexpr int kLayerPer = 8;  // logits per lane in the one-launch window: E <= 512
+constexpr long long kWinSpinTicks = 1ll << 24;  // wall-clock ticks a down role waits for h at most
+
+__device__ inline uint32_t sync_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t sync_add(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void sync_zero(uint32_t* p) {
+  __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The whole window in one launch on the matrix cores (H a multiple of 1,024 up
+// to 4,096; I 256 or 512). Every workgroup routes the window itself (top-k of
+// T logit rows, a few KB, and the active-expert list in LDS). Workgroups
+// 0 .. G-1 (G = 8 I / 16) are gate/up roles, the next D = H / 16 down roles.
+// A down role requests its weights (which depend only on the routing), then
+// waits until every gate/up role has released h. Workgroups are dispatched in
+// index order, so a waiting down role never holds back a gate/up role; the
+// wait is also bounded in time, past which the role writes NaN rows.
+template <int Q, bool XF32, int NBG, int NBD>
+__global__ __launch_bounds__(kWinThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const void* x,
+               int32_t* idx_out, float* gates_out, uint16_t* hwin, void* y, int out_f32,
+               WinSync* sync) {
+  __shared__ LayerRoute R;
+  // gate/up roles: activations (fp16, 32 KB) and partial tiles (16 KB); down roles: h
+  __shared__ __attribute__((aligned(16))) char buf[kHsBytes];
+  __shared__ float red_dn[kWinWaves][16][kWinT];
+  static_assert(kWinT * kMmaMaxH * 2 + kWinWaves * kMmaBatch * 2 * 16 * kWinT * 4 <= kHsBytes, "");
+  _Float16* xs = reinterpret_cast<_Float16*>(buf);
+  auto& red = *reinterpret_cast<float(*)[kWinWaves][kMmaBatch][2][16][kWinT]>(buf + kWinT * kMmaMaxH * 2);
+  __shared__ uint32_t guard_s;
+  __shared__ int bad_s;
+  const int tid = threadIdx.x;
+  const int H = ex.H;
+  const int G = ex.I / 16 * kMmaSlices, D = H / 16;
+  const int role = blockIdx.x;
+
+  win_topk<kLayerPer>(R, logits, T, ex.E, k);
+  // the window's activations -> LDS fp16 in the MFMA K order (tokens >= T
+  // zero), by the waves that do not select experts
+  for (int i = tid - 64 * kWinT; i >= 0 && i < kWinT * H / 4; i += kWinThreads - 64 * kWinT) {
+    const int t = i / (H / 4), q = i % (H / 4);
+    float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+    if (t < T) {
+      if (XF32) {
+        const float4 f = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)t * H)[q];
+        v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
+      } else {
+        const uint2 u = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)t * H)[q];
+        v0 = bf16_lo(u.x); v1 = bf16_hi(u.x); v2 = bf16_lo(u.y); v3 = bf16_hi(u.y);
+      }
+    }
+    *reinterpret_cast<uint2*>(xs + t * H + 4 * q) = make_uint2(pack_half2(v0, v2), pack_half2(v1, v3));
+  }
+  if (tid == kWinThreads - 64) guard_s = sync_load(sync->guard);
+  const int n_act = win_list(R, ex, T, k, false, nullptr, nullptr, nullptr);  // ends with a barrier
+
+  if (guard_s != 0u) {  // the head was not zeroed: y becomes NaN
+    for (int i = tid; i < T * H; i += kWinThreads) {
+      if (out_f32) static_cast<float*>(y)[i] = __uint_as_float(0x7FC00000u);
+      else static_cast<uint16_t*>(y)[i] = 0x7FC0u;
+    }
+    return;
+  }
+  if (role == 0)
+    for (int a = tid; a < T * k; a += kWinThreads) {
+      idx_out[a] = R.lidx[a];
+      gates_out[a] = R.lgate[a];
+    }
+  if (role < G) {
+    gateup_role<Q, NBG>(R.wl, n_act, role, T, ex, xs, red, hwin);
+    // The h stores are agent-coherent; a wave's store count reaching zero means
+    // they are performed chip-wide, so once every wave has waited for that,
+    // the role's count orders them before the down roles' reads (which are
+    // agent-coherent too). No cache write-back is needed.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (tid == 0) sync_add(sync->up[role / kSyncGroup]);
+    return;
+  }
+  auto wait = [&]() -> bool {
+    if (tid == 0) bad_s = 0;
+    __syncthreads();
+    if (tid < G / kSyncGroup) {  // lanes of wave 0, one counter each
+      const long long t0 = wall_clock64();
+      while (sync_load(sync->up[tid]) != (uint32_t)kSyncGroup) {
+        __builtin_amdgcn_s_sleep(1);
+        if (wall_clock64() - t0 > kWinSpinTicks) {
+          bad_s = 1;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    return bad_s == 0;
+  };
+  const int grp = role - G;
+  down_role<Q, NBD>(R.wl, n_act, grp, T, ex, hwin, y, out_f32, reinterpret_cast<_Float16*>(buf),
+                    red_dn, wait);
+  if (tid == 0 && bad_s == 0 && sync_add(sync->dn[grp / kSyncGroup]) == kSyncGroup - 1 &&
+      sync_add(sync->dn_all) == (uint32_t)(D / kSyncGroup - 1)) {
+    // every gate/up role has released h and every down role has passed its wait
+    for (int g = 0; g < G / kSyncGroup; ++g) sync_zero(sync->up[g]);
+    for (int g = 0; g < D / kSyncGroup; ++g) sync_zero(sync->dn[g]);
+    sync_zero(sync->dn_all);
+  }
+}
+
+inline bool win_mma_ok(const Experts& ex, int T, int k) {
+  return ex.H % 1024 == 0 && ex.H <= kMmaMaxH && (ex.I == 256 || ex.I == 512) &&
+         ex.E <= 64 * kLayerPer && T * k <= 64;
 }
 
 template <int BPR_H, int BPR_I, int Q, bool XF32>
 hipError_t launch_w(const float* logits, int T, int k, const Experts& ex, const void* x,
                     int32_t* idx, float* gates, WinList* meta, uint16_t* hwin, void* y, int out_f32,
                     hipStream_t s) {
-  if (win_mma_ok(ex)) {
-    const dim3 grid(ex.I / 16 * kMmaSlices);
-    if (ex.H == 1024)
-      MOE_LAUNCH("win_gateup", s, (win_gateup_mma<Q, XF32, 1>), grid, dim3(kWinThreads), 0, s, logits,
-                 T, k, ex, x, idx, gates, meta, hwin);
-    else if (ex.H == 2048)
-      MOE_LAUNCH("win_gateup", s, (win_gateup_mma<Q, XF32, 2>), grid, dim3(kWinThreads), 0, s, logits,
-                 T, k, ex, x, idx, gates, meta, hwin);
-    else
-      MOE_LAUNCH("win_gateup", s, (win_gateup_mma<Q, XF32, 4>), grid, dim3(kWinThreads), 0, s, logits,
-                 T, k, ex, x, idx, gates, meta, hwin);
-  } else {
-    MOE_LAUNCH("win_gateup", s, (win_gateup<BPR_H, Q, XF32>), dim3(ex.I / win_gu_rows<BPR_H>()),
-               dim3(kWinThreads), 0, s, logits, T, k, ex, x, idx, gates, meta, hwin);
-  }
-  if (win_mma_ok(ex)) {
-    const dim3 grid(ex.H / 16);
-    if (ex.I == 256)
-      MOE_LAUNCH("win_down", s, (win_down_mma<Q, 1>), grid, dim3(kWinThreads), 0, s, T, ex, meta,
-                 hwin, y, out_f32);
-    else
-      MOE_LAUNCH("win_down", s, (win_down_mma<Q, 2>), grid, dim3(kWinThreads), 0, s, T, ex, meta,
-                 hwin, y, out_f32);
-  } else {
-    MOE_LAUNCH("win_down", s, (win_down<BPR_I, Q>), dim3(ex.H / win_dn_rows<BPR_I>()),
-               dim3(kWinThreads), 0, s, T, ex, meta, hwin, y, out_f32);
-  }
+  MOE_LAUNCH("win_gateup", s, (win_gateup<BPR_H, Q, XF32>), dim3(ex.I / win_gu_rows<BPR_H>()),
+             dim3(kWinThreads), 0, s, logits, T, k, ex, x, idx, gates, meta, hwin);
+  MOE_LAUNCH("win_down", s, (win_down<BPR_I, Q>), dim3(ex.H / win_dn_rows<BPR_I>()),
+             dim3(kWinThreads), 0, s, T, ex, meta, hwin, y, out_f32);
+  return hipGetLastError();
+}
+
+template <int Q, bool XF32>
+hipError_t launch_layer(const float* logits, int T, int k, const Experts& ex, const void* x,
+                        int32_t* idx, float* gates, uint16_t* hwin, void* y, int out_f32,
+                        WinSync* sync, hipStream_t s) {
+  const dim3 grid(ex.I / 16 * kMmaSlices + ex.H / 16);
+#define L(NBG, NBD)                                                                               \
+  MOE_LAUNCH("win_layer", s, (win_layer<Q, XF32, NBG, NBD>), grid, dim3(kWinThreads), 0, s, logits, \
+             T, k, ex, x, idx, gates, hwin, y, out_f32, sync)
+  const int nbg = ex.H / 1024, nbd = ex.I / 256;
+  if (nbg == 1 && nbd == 1) L(1, 1);
+  else if (nbg == 1) L(1, 2);
+  else if (nbg == 2 && nbd == 1) L(2, 1);
+  else if (nbg == 2) L(2, 2);
+  else if (nbd == 1) L(4, 1);
+  else L(4, 2);
+#undef L
   return hipGetLastError();
 }
 
@@ -683,15 +834,18 @@ bool window_supported(const Experts& ex, int T, int k) {
   return ex.H % rows == 0 && ex.I % (64 / (ex.H / 32) > 2 ? 64 / (ex.H / 32) : 2) == 0;
 }
 
-// Window workspace: active list | h [n_act][kWinT][I] bf16.
+// Window workspace: counters (kWinSyncBytes, zero between calls) | active list |
+// h [n_act][kWinT][I] (fp16 in the MFMA K order for the one-launch form, bf16
+// otherwise).
 namespace {
 struct WinLayout {
-  size_t meta, h, total;
+  size_t sync, meta, h, total;
 };
 WinLayout win_layout(const Experts& ex, int T, int k) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   WinLayout L{};
   size_t off = 0;
+  L.sync = off; off = al(off + kWinSyncBytes);
   L.meta = off; off = al(off + sizeof(WinList));
   L.h = off;    off = al(off + sizeof(uint16_t) * ((size_t)T * k + ex.has_shared) * kWinT * ex.I);
   L.total = off;
@@ -708,6 +862,14 @@ hipError_t launch_window(const float* logits, int T, int k, const Experts& ex, c
   char* base = static_cast<char*>(ws);
   WinList* meta = reinterpret_cast<WinList*>(base + L.meta);
   uint16_t* hwin = reinterpret_cast<uint16_t*>(base + L.h);
+  if (win_mma_ok(ex, T, k)) {
+    WinSync* sync = reinterpret_cast<WinSync*>(base + L.sync);
+    if (ex.qtype == 3)
+      return xdtype == 0 ? launch_layer<3, true>(logits, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s)
+                         : launch_layer<3, false>(logits, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s);
+    return xdtype == 0 ? launch_layer<2, true>(logits, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s)
+                       : launch_layer<2, false>(logits, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s);
+  }
   const int bh = ex.H / 32, bi = ex.I / 32;
   if (ex.qtype == 3)
     return xdtype == 0 ? launch_wq<3, true>(bh, bi, logits, T, k, ex, x, idx, gates, meta, hwin, y, out_f32, s)

@@ -209,13 +209,24 @@ size_t moe_layer_workspace_size(const moe_experts *ex, int32_t T, int32_t k, int
 /* The whole routed MoE layer in one call: top-k routing of `logits` ([T][E]
  * f32), the grouping, the expert FFN and the combine, writing idx and gates
  * ([T][k]) and y ([T][H]). Results match moe_route_group followed by
- * moe_ffn_q within the FFN tolerance (idx and gates identically). A decode
- * verify window (fast mode, T <= 4, k <= 64, H/32 and I/32 in {4..64}) runs as
- * two kernels: the first routes the window in every workgroup and computes
- * gate/up for all active experts, the second computes the down projection and
- * sums the combine in registers, so its y is reproducible run to run. Other
- * calls run moe_route_group then moe_ffn_q inside the workspace.
- * ws: at least moe_layer_workspace_size(ex, T, k, mode) bytes. */
+ * moe_ffn_q within the FFN tolerance (idx and gates identically).
+ *
+ * A decode verify window ("Strata - the details", "How it works": the drafted
+ * tokens are checked in one pass) is fast mode with T <= 4, k <= 64 and H/32,
+ * I/32 in {4..64}. With H a multiple of 1024 up to 4096, I 256 or 512,
+ * E <= 512 and T k <= 64 it runs as ONE kernel: every workgroup routes the
+ * window itself; the first workgroups compute gate/up rows, the others down
+ * rows once counters at the head of `ws` show every gate/up row released; y is
+ * reproducible run to run. Other windows run as two kernels (gate/up, then
+ * down); other calls run moe_route_group then moe_ffn_q inside the workspace.
+ *
+ * ws: at least moe_layer_workspace_size(ex, T, k, mode) bytes. Its first 8192
+ * bytes must be zero before the first call that uses it (a zero-filled
+ * allocation); every moe_layer call leaves them zero, and no form of the call
+ * other than the one-kernel window writes them, so one zeroed workspace serves
+ * every shape. Calls that overlap in time must not share a workspace. A head
+ * that was not zeroed shows as NaN in the window's y (the first 128 bytes are
+ * checked; a down row also gives up waiting after about 0.2 s). */
 int moe_layer(const float *logits, const void *x, int32_t xdtype, int32_t T, const moe_experts *ex,
               int32_t k, int32_t *idx, float *gates, void *y, int32_t mode, void *ws,
               size_t ws_bytes, void *stream);

@@ -132,8 +132,9 @@ def test_route_group_fused_bit_exact(cid, T):
                                          (4, 4, "fast"), (4, 2, "fast"), (0, 4, "fast"),
                                          (0, 8, "fast"), (4, 64, "fast"), (1, 4, "check")])
 def test_layer_call(cid, T, mode):
-    """moe_layer (whole layer in one call; the two-kernel window path for T <= 4
-    in fast mode) against the oracle's route, grouping and layer."""
+    """moe_layer (whole layer in one call; the one-kernel window path for T <= 4
+    in fast mode at the decode shapes, the two-kernel one at the tiny shape)
+    against the oracle's route, grouping and layer."""
     torch = torch_cuda()
     import bit_quantized_moe_topk_amd as moe
     base = CONFIGS[cid]
@@ -157,6 +158,42 @@ def test_layer_call(cid, T, mode):
     if mode == "fast" and T <= 4:
         assert torch.equal(y, y2), "window path must be reproducible run to run"
     ex.close()
+
+
+def test_layer_window_shared_workspace():
+    """One zero-filled workspace serves window calls of two layer instances,
+    repeated, with a 64-token call of the same experts in between: the
+    one-kernel window's role counters at the head of the workspace come back to
+    zero after every call, and the other call form leaves them alone."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    base = CONFIGS[1].with_(T=64)
+    lays = [make_layer(base, seed=s) for s in (41, 42)]
+    devs = [upload(l) for l in lays]
+    exs = [experts_of(l, d) for l, d in zip(lays, devs)]
+    k = base.k
+    nbytes = max(int(moe.lib().moe_layer_workspace_size(exs[0].handle, T, k, 0)) for T in (4, 64))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    refs = []
+    for lay in lays:
+        idx_o, g_o = oracle.route(lay["logits"][:4], k)
+        win = dict(lay, cfg=base.with_(T=4), x=lay["x"][:4].copy(), logits=lay["logits"][:4].copy())
+        refs.append((idx_o, g_o, oracle_rows(win, idx_o, g_o)))
+    for rep in range(3):
+        for i, (dev, ex) in enumerate(zip(devs, exs)):
+            log(f"[shared ws] rep {rep} instance {i}: window")
+            idx, gates, y = moe.layer(dev["logits"][:4], dev["x"][:4], ex, k, workspace=ws)
+            torch.cuda.synchronize()
+            idx_o, g_o, ref = refs[i]
+            assert np.array_equal(idx.cpu().numpy(), idx_o)
+            assert rel_l2_rows(y_to_f64(y), ref).max() <= TOL_FAST
+            assert int(ws[:8192].count_nonzero()) == 0
+        log(f"[shared ws] rep {rep}: 64-token call")
+        moe.layer(devs[rep % 2]["logits"], devs[rep % 2]["x"], exs[rep % 2], k, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:8192].count_nonzero()) == 0
+    for ex in exs:
+        ex.close()
 
 
 def run_ffn(lay, dev, idx_np, gates_np, mode, use_gpu_grouping=False, tiled=False):
