@@ -568,65 +568,61 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
   const int kb0 = ks * (I / 64) + NBL * c;  // this lane's first block of the wave's K half
   const size_t roff = (size_t)(16 * grp + r16) * (I / 32) + kb0;
   const bool tok = r16 < T;
-  const int per_phase = kHsBytes / (kWinT * I * 2);  // experts whose h fits in hs
   WRow<NBL> wd[kDnBatch];
-  auto load_round = [&](int p0) {
 #pragma unroll
-    for (int j = 0; j < kDnBatch; ++j) {
-      const int p = p0 + 4 * j;
-      if (p < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[p]) + roff);
-    }
-  };
-  load_round(eq);
+  for (int j = 0; j < kDnBatch; ++j) {  // the first round's weights, before the wait
+    const int p = eq + 4 * j;
+    if (p < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[p]) + roff);
+  }
   const bool ok = wait();
   floatx4_t acc = {};
-  for (int r0 = 0; r0 < n_act; r0 += 4 * kDnBatch) {  // rounds: weights of 4 kDnBatch experts
-    if (r0 > 0) load_round(r0 + eq);
-    const int r1 = min(n_act, r0 + 4 * kDnBatch);
-    for (int ph0 = r0; ph0 < r1; ph0 += per_phase) {
-      const int n16 = min(per_phase, r1 - ph0) * kWinT * I / 8;
-      const uint4* src = reinterpret_cast<const uint4*>(hwin) + (size_t)ph0 * kWinT * I / 8;
-      // straight into LDS (each lane's 16 bytes land at the wave's base + 16
-      // lane), no registers held; every load of the phase in flight at once,
-      // agent-coherent (h was written in this launch on other CUs)
-      constexpr int kCopy = kHsBytes / 16 / kWinThreads;
-      constexpr int kCoherent = 16;  // cache policy: agent scope
-      __syncthreads();  // the previous phase's reads of hs are done
+  static_assert(kHsBytes / (kWinT * 512 * 2) >= 4 * kDnBatch, "h of one round fits hs (I <= 512)");
+  for (int r0 = 0; r0 < n_act; r0 += 4 * kDnBatch) {  // rounds of 4 kDnBatch experts
+    const int n16 = min(4 * kDnBatch, n_act - r0) * kWinT * I / 8;
+    const uint4* src = reinterpret_cast<const uint4*>(hwin) + (size_t)r0 * kWinT * I / 8;
+    // h of the round straight into LDS (each lane's 16 bytes land at the
+    // wave's base + 16 lane), no registers held; every load in flight at once,
+    // agent-coherent (h was written in this launch on other CUs)
+    constexpr int kCopy = kHsBytes / 16 / kWinThreads;
+    constexpr int kCoherent = 16;  // cache policy: agent scope
+    __syncthreads();  // the previous round's reads of hs are done
 #pragma unroll
-      for (int u = 0; u < kCopy; ++u)
-        if (tid + u * kWinThreads < n16)
-          __builtin_amdgcn_global_load_lds(
-              src + tid + u * kWinThreads,
-              (__attribute__((address_space(3))) void*)(reinterpret_cast<uint4*>(hs) + u * kWinThreads +
-                                                        64 * wave),
-              16, 0, kCoherent);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the LDS writes have landed
-      __syncthreads();
+    for (int u = 0; u < kCopy; ++u)
+      if (tid + u * kWinThreads < n16)
+        __builtin_amdgcn_global_load_lds(
+            src + tid + u * kWinThreads,
+            (__attribute__((address_space(3))) void*)(reinterpret_cast<uint4*>(hs) + u * kWinThreads +
+                                                      64 * wave),
+            16, 0, kCoherent);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the LDS writes have landed
+    __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kDnBatch; ++j) {
-        const int p = r0 + eq + 4 * j;
-        if (p < ph0 || p >= ph0 + per_phase || p >= n_act) continue;
-        // columns past T read token 0's row (finite; their gate is 0): no
-        // branch, so all eight LDS reads of the expert issue together
-        const _Float16* hp = hs + ((size_t)(p - ph0) * kWinT + (tok ? r16 : 0)) * I;
-        half8_t hv[NBL][4];
+    for (int j = 0; j < kDnBatch; ++j) {
+      const int p = r0 + eq + 4 * j;
+      if (p >= n_act) continue;
+      // columns past T read token 0's row (finite; their gate is 0): no
+      // branch, so all eight LDS reads of the expert issue together
+      const _Float16* hp = hs + ((size_t)(p - r0) * kWinT + (tok ? r16 : 0)) * I;
+      half8_t hv[NBL][4];
 #pragma unroll
-        for (int b = 0; b < NBL; ++b)
+      for (int b = 0; b < NBL; ++b)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) hv[b][t] = *reinterpret_cast<const half8_t*>(hp + 32 * (kb0 + b) + 8 * t);
-        floatx4_t o = {};
+        for (int t = 0; t < 4; ++t) hv[b][t] = *reinterpret_cast<const half8_t*>(hp + 32 * (kb0 + b) + 8 * t);
+      floatx4_t o = {};
 #pragma unroll
-        for (int b = 0; b < NBL; ++b) {
-          const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
+      for (int b = 0; b < NBL; ++b) {
+        const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sw, t), hv[b][t], o, 0, 0, 0);
-        }
-        const float ga = wl.act_gate[p][r16 & (kWinT - 1)];
-        const float g = tok ? ga : 0.f;  // o[v]: row 4 c + v, token r16
-#pragma unroll
-        for (int v2 = 0; v2 < 4; ++v2) acc[v2] += g * o[v2];
+        for (int t = 0; t < 4; ++t)
+          o = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sw, t), hv[b][t], o, 0, 0, 0);
       }
+      const float ga = wl.act_gate[p][r16 & (kWinT - 1)];
+      const float g = tok ? ga : 0.f;  // o[v]: row 4 c + v, token r16
+#pragma unroll
+      for (int v2 = 0; v2 < 4; ++v2) acc[v2] += g * o[v2];
+      // this slot's weights for the next round, in flight during the rest of this one
+      const int pn = p + 4 * kDnBatch;
+      if (pn < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[pn]) + roff);
     }
   }
   if (r16 < kWinT) {
