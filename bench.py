@@ -149,15 +149,17 @@ def build_instances(cfg, n: int, seed: int, keep_host: int = 0):
 
 def routing_stats(insts) -> list:
     """Per instance (from the idx the step wrote): experts on the GEMV path
-    (1..4 assignments), on the MFMA path, and the assignments on the MFMA path."""
+    (1..4 assignments, batches under 256 tokens only), on the MFMA path, and
+    the assignments on the MFMA path."""
     out = []
     for it in insts:
         cfg = it.cfg
         c = np.bincount(it.idx.cpu().numpy().reshape(-1), minlength=cfg.E).astype(np.int64)
         if cfg.shared:
             c = np.append(c, cfg.T)
-        gemv = int(((c >= 1) & (c <= 4)).sum())
-        mf = c > 4
+        gmax = 4 if cfg.T < 256 else 0
+        gemv = int(((c >= 1) & (c <= gmax)).sum())
+        mf = c > gmax
         out.append({"gemv_experts": gemv, "mfma_experts": int(mf.sum()),
                     "mfma_assignments": int(c[mf].sum()), "touched": int((c > 0).sum())})
     return out

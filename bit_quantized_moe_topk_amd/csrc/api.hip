@@ -228,7 +228,11 @@ int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, c
   if (mode == MOE_CHECK_F32) {
     e = moe::launch_ffn_check(d, a, s);
   } else {
-    a.gmax = moe::gemv_supported(d.H, d.I) ? moe::kGemvMaxTokens : 0;
+    // From a few hundred tokens on, experts with few assignments ride in the
+    // persistent matrix-core grid, where their weight reads overlap the other
+    // tiles' arithmetic; a separate GEMV pass would run on its own.
+    const bool small_batch = T < moe::kGemvBatchLimit || !moe::mfma_supported(d.H, d.I);
+    a.gmax = moe::gemv_supported(d.H, d.I) && small_batch ? moe::kGemvMaxTokens : 0;
     e = moe::launch_ffn_fast(d, a, s);
   }
   if (e == hipSuccess) e = moe::launch_combine(d, a, s);

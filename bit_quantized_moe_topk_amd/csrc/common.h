@@ -47,6 +47,7 @@ __host__ __device__ inline size_t blk_down(const Experts& x, int e) {
 // Experts with 1..kGemvMaxTokens assignments take the GEMV kernels (weights
 // streamed once, codes kept exact); the rest take the MFMA tile kernels.
 constexpr int kGemvMaxTokens = 4;
+constexpr int kGemvBatchLimit = 256;  // batches of at least this many tokens take no GEMV pass
 constexpr int kTileM = 64;  // assignments per tile of the fp32 check kernels
 // Up to this many tokens the per-assignment expert outputs are kept in fp32;
 // above it in bf16 (half the traffic of the combine).

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(1024) void route_group_small(const float* __restric
   write_shared(T, k, has_shared, perm, slot_of);
 }
 
-// Large inputs, step 1: per-segment counts into hist[e * nseg + seg] (global).
+// Large inputs, step 1: per-segment counts into hist[seg * E + e] (global,
+// segment-major so that every step's accesses are coalesced).
 __global__ __launch_bounds__(256) void group_count(const int32_t* __restrict__ idx, int T, int k,
                                                    int E, int has_shared, int nseg, int* hist,
                                                    int32_t* perm, int32_t* slot_of) {
@@ -153,16 +154,63 @@ __global__ __launch_bounds__(256) void group_count(const int32_t* __restrict__ i
   }
   __syncthreads();
   if (seg < nseg)
-    for (int e = lane; e < E; e += 64) hist[e * nseg + seg] = h[e];
+    for (int e = lane; e < E; e += 64) hist[(size_t)seg * E + e] = h[e];
   write_shared(T, k, has_shared, perm, slot_of);
 }
 
-// Step 2: one workgroup scans hist in place and writes counts / offsets.
+// Step 2: one workgroup turns hist into exclusive bases in (expert, segment)
+// order. Thread e sums expert e's segment counts (a segment's counts are
+// adjacent, so the workgroup's loads coalesce), a block scan over the expert
+// totals in LDS gives each expert's first slot, and thread e rewrites its
+// column as running bases. Eight loads in flight per thread.
 __global__ __launch_bounds__(1024) void group_scan(int T, int k, int E, int has_shared, int nseg,
                                                    int* hist, int32_t* counts, int32_t* offsets) {
-  __shared__ int tmp[16];
-  block_exclusive_scan(hist, E * nseg, tmp);
-  write_offsets(hist, nseg, E, T, k, has_shared, counts, offsets);
+  __shared__ int tot[MOE_MAX_E_DEV + 1];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, NT = blockDim.x;
+  constexpr int U = 8;
+  for (int e = tid; e < E; e += NT) {
+    int sum = 0, s = 0;
+    for (; s + U <= nseg; s += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = hist[(size_t)(s + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) sum += v[u];
+    }
+    for (; s < nseg; ++s) sum += hist[(size_t)s * E + e];
+    tot[e] = sum;
+  }
+  __syncthreads();
+  block_exclusive_scan(tot, E, wsum);
+  const int AR = T * k;
+  for (int e = tid; e <= E + 1; e += NT) {
+    if (e < E) offsets[e] = tot[e];
+    else if (e == E) offsets[E] = AR;
+    else offsets[E + 1] = AR + (has_shared ? T : 0);
+  }
+  for (int e = tid; e <= E; e += NT) {
+    if (e < E) counts[e] = (e + 1 < E ? tot[e + 1] : AR) - tot[e];
+    else counts[E] = has_shared ? T : 0;
+  }
+  for (int e = tid; e < E; e += NT) {
+    int run = tot[e], s = 0;
+    for (; s + U <= nseg; s += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = hist[(size_t)(s + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        hist[(size_t)(s + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; s < nseg; ++s) {
+      const int v = hist[(size_t)s * E + e];
+      hist[(size_t)s * E + e] = run;
+      run += v;
+    }
+  }
 }
 
 // Step 3: per-segment stable scatter from the scanned bases.
@@ -174,7 +222,7 @@ __global__ __launch_bounds__(256) void group_scatter(const int32_t* __restrict__
   const int seg = blockIdx.x * 4 + w;
   if (seg >= nseg) return;  // no barrier below: each wave only touches its own LDS row
   int* cnt = lds + w * E;
-  for (int e = lane; e < E; e += 64) cnt[e] = hist[e * nseg + seg];
+  for (int e = lane; e < E; e += 64) cnt[e] = hist[(size_t)seg * E + e];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   const int AR = T * k;
