@@ -95,12 +95,69 @@ __device__ inline void stage_mma(const _Float16* xb, const WStage (&w)[2],
   }
 }
 
-// Logical item of this workgroup in round r: consecutive items share an XCD
+// Tile map of one launch, built in LDS by every workgroup. Tiles are ordered
+// by cost class — tiles that fill all four 32-row groups first, then tiles of
+// two groups, then of one (Q2; Q3 runs every tile in full) — and within a
+// class by expert, M block and output tile.
+struct TileMap {
+  int b4[MOE_MAX_E_DEV + 2];  // exclusive prefix of each expert's four-group tiles
+  int b2[MOE_MAX_E_DEV + 2];  // of its two-group tile (0 or 1)
+  int b1[MOE_MAX_E_DEV + 2];  // of its one-group tile (0 or 1)
+  int wsum[16];
+  int n4, n2, n1;
+};
+
+// CLASSES = false keeps one class: every tile in expert order.
+template <int Q, bool CLASSES>
+__device__ inline void tilemap_init(TileMap& tm, const int32_t* __restrict__ counts, int E_tot,
+                                    int gmax) {
+  for (int e = threadIdx.x; e < E_tot; e += blockDim.x) {
+    const int M = counts[e];
+    int c4 = 0, c2 = 0, c1 = 0;
+    if (M > gmax) {
+      const int r = M % kBM;
+      c4 = M / kBM;
+      if (CLASSES && Q == 2 && r > 0 && r <= 32) c1 = 1;
+      else if (CLASSES && Q == 2 && r > 32 && r <= 64) c2 = 1;
+      else if (r > 0) c4 += 1;
+    }
+    tm.b4[e] = c4;
+    tm.b2[e] = c2;
+    tm.b1[e] = c1;
+  }
+  __syncthreads();
+  const int n4 = block_exclusive_scan(tm.b4, E_tot, tm.wsum);
+  const int n2 = block_exclusive_scan(tm.b2, E_tot, tm.wsum);
+  const int n1 = block_exclusive_scan(tm.b1, E_tot, tm.wsum);
+  if (threadIdx.x == 0) {
+    tm.b4[E_tot] = n4;
+    tm.b2[E_tot] = n2;
+    tm.b1[E_tot] = n1;
+    tm.n4 = n4;
+    tm.n2 = n2;
+    tm.n1 = n1;
+  }
+  __syncthreads();
+}
+
+// Items are dealt to the workgroups round by round; with SERP, in serpentine
+// order (round r runs positions forward when r is even, backward when odd),
+// so the cheap partial tiles at the end of the class order even out the
+// per-workgroup work. Within a round, consecutive items share an XCD
 // (workgroup g runs on XCD g % 8) when the grid is a multiple of 8.
-__device__ inline int item_of(int r) {
+__device__ inline int deal_pos() {
   const int g = blockIdx.x, G = gridDim.x;
-  if (G % 8) return r * G + g;
-  return r * G + (g % 8) * (G / 8) + g / 8;
+  return (G % 8) ? g : (g % 8) * (G / 8) + g / 8;
+}
+template <bool SERP>
+__device__ inline int item_of(int r) {
+  const int G = gridDim.x, p = deal_pos();
+  return r * G + ((SERP && (r & 1)) ? G - 1 - p : p);
+}
+template <bool SERP>
+__device__ inline int items_of_workgroup(int n_items) {
+  const int G = gridDim.x, R = n_items / G, rem = n_items % G, p = deal_pos();
+  return R + (rem > 0 && ((SERP && (R & 1)) ? G - 1 - p : p) < rem ? 1 : 0);
 }
 
 struct TileInfo {
@@ -109,14 +166,22 @@ struct TileInfo {
 
 // Wave-uniform description of work item `item` (values read from LDS are
 // moved to scalar registers).
-__device__ inline TileInfo tile_info(const WorkMap& wm, const int* offs, int E_tot, int n_nt,
+__device__ inline TileInfo tile_info(const TileMap& tm, const int* offs, int E_tot, int n_nt,
                                      int item) {
-  int tl;
+  const int ti = item / n_nt;
+  int e, blk;
+  if (ti < tm.n4) {
+    e = workmap_find(tm.b4, E_tot, ti);
+    blk = ti - tm.b4[e];
+  } else {
+    e = ti < tm.n4 + tm.n2 ? workmap_find(tm.b2, E_tot, ti - tm.n4)
+                           : workmap_find(tm.b1, E_tot, ti - tm.n4 - tm.n2);
+    blk = (offs[e + 1] - offs[e]) / kBM;  // the expert's last, partial M block
+  }
   TileInfo t;
-  const int e = workmap_tile(wm, E_tot, item / n_nt, tl);
   t.e = __builtin_amdgcn_readfirstlane(e);
   t.nt = item % n_nt;
-  const int m0 = tl * kBM;
+  const int m0 = blk * kBM;
   t.M = __builtin_amdgcn_readfirstlane(min(kBM, offs[e + 1] - offs[e] - m0));
   t.slot0 = __builtin_amdgcn_readfirstlane(offs[e] + m0);
   return t;
@@ -144,16 +209,18 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   constexpr int CH = kBM * (kBK / 8) / NT;    // 16-byte activation chunks per thread per stage
   __shared__ __attribute__((aligned(16))) _Float16 xs[2][kBM * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t ostage[NW][kStage];  // epilogue, per wave
-  __shared__ WorkMap wm;
+  __shared__ TileMap wm;
   __shared__ int offs[MOE_MAX_E_DEV + 2];
   for (int e = threadIdx.x; e <= ex.E_tot; e += NT) offs[e] = a.offsets[e];
-  workmap_init(wm, a.counts, ex.E_tot, a.gmax, kBM);
+  // gate/up: cost classes dealt in serpentine order; down (four output tiles
+  // per M block, whose outputs the combine reads next): expert order
+  constexpr bool kClasses = !DOWN;
+  tilemap_init<Q, kClasses>(wm, a.counts, ex.E_tot, a.gmax);
   const int K = DOWN ? ex.I : ex.H;
   const int n_nt = (DOWN ? ex.H : ex.I) / tile_rows<DOWN, NW>();
-  const int n_items = wm.n_tiles * n_nt;
+  const int n_items = (wm.n4 + wm.n2 + wm.n1) * n_nt;
   const int S = K / kBK;  // even: H % 256 == 0, I % 128 == 0
-  const int first = item_of(0);
-  const int n_my = first < n_items ? (n_items - first + gridDim.x - 1) / gridDim.x : 0;
+  const int n_my = items_of_workgroup<kClasses>(n_items);
   if (n_my == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const uint16_t* a16 = DOWN ? static_cast<const uint16_t*>(a.h) : a.x16;
@@ -165,7 +232,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   int anext[CH];
   int xt = 0, xsg = 0;    // tile round and stage of the next activation load
   auto xprep = [&](int r) {  // tile r's rows: permutation entries, not yet waited on
-    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
+    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of<kClasses>(r));
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int m = (tid + NT * u) >> 3;
@@ -217,7 +284,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   const uint2* dm2 = reinterpret_cast<const uint2*>(TILED ? ex.t_dm : ex.dm);
   const uint2* hi2 = reinterpret_cast<const uint2*>(TILED ? ex.t_hi : ex.hi);
   auto wsetup = [&](int r) {
-    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
+    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of<kClasses>(r));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row0 = t.nt * tile_rows<DOWN, NW>() + (DOWN ? 64 * wave + 32 * j : 32 * wave);
@@ -377,7 +444,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
     __syncthreads();
   };
   for (int r = 0; r < n_my; ++r) {
-    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of(r));
+    const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of<kClasses>(r));
     // wave-uniform; Q3 keeps one variant (its third-bit plane leaves no
     // registers for more)
     if (Q == 2 && t.M <= 32) tile(std::integral_constant<int, 1>{}, t);
