@@ -467,6 +467,9 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
                                    const _Float16* xs,
                                    float (&red)[kWinWaves][kMmaBatch][2][16][kWinT],
                                    uint16_t* hwin) {
+  // experts per round (at H = 4096 the activation operand alone takes 64
+  // registers: one expert at a time)
+  constexpr int kB = NBL >= 4 ? 1 : kMmaBatch;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = ex.H;
   const int rgrp = role / kMmaSlices, es = role % kMmaSlices;
@@ -483,10 +486,10 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
     }
   const size_t roff = (size_t)(16 * rgrp + r16) * (H / 32) + kb0;
 
-  for (int p0 = es; p0 < n_act; p0 += kMmaSlices * kMmaBatch) {
-    WRow<NBL> wg[kMmaBatch], wu[kMmaBatch];
+  for (int p0 = es; p0 < n_act; p0 += kMmaSlices * kB) {
+    WRow<NBL> wg[kB], wu[kB];
 #pragma unroll
-    for (int j = 0; j < kMmaBatch; ++j) {
+    for (int j = 0; j < kB; ++j) {
       const int p = p0 + j * kMmaSlices;
       if (p < n_act) {
         const int e = wl.act_e[p];
@@ -495,7 +498,7 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
       }
     }
 #pragma unroll
-    for (int j = 0; j < kMmaBatch; ++j) {
+    for (int j = 0; j < kB; ++j) {
       const int p = p0 + j * kMmaSlices;
       if (p >= n_act) break;
       floatx4_t ag = {}, au = {};
@@ -522,7 +525,7 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
     // rows 4 q + s and 4 q + s + 2 (s = 0, 1) sit side by side in the K
     // order (0, 2, 1, 3): one 32-bit store each, coherent across the chip
     // (agent scope) for the down roles that read h in the same launch
-    for (int i = tid; i < kMmaBatch * 8 * kWinT; i += kWinThreads) {
+    for (int i = tid; i < kB * 8 * kWinT; i += kWinThreads) {
       const int j = i / (8 * kWinT), pr = (i / kWinT) % 8, t = i % kWinT;
       const int p = p0 + j * kMmaSlices;
       if (p < n_act && t < T) {  // every token (finite values) for the down tiles
@@ -554,13 +557,19 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
 // returns once h is complete (false: it never was; the rows become NaN). h
 // then comes into LDS (hs, kHsBytes) a phase of experts at a time, every load
 // of a phase in flight at once.
-constexpr int kDnBatch = 4;           // experts per wave whose weights are in registers
+// experts per wave whose weights are in registers (Q3 rows carry a third-bit
+// plane, so fewer of them fit)
+template <int Q>
+constexpr int dn_batch() {
+  return Q == 3 ? 3 : 4;
+}
 constexpr int kHsBytes = 64 * 1024;   // LDS for h: 16 experts at I = 512, 32 at I = 256
 
 template <int Q, int NBL, typename Wait>
 __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, const Experts& ex,
                                  const uint16_t* hwin, void* y, int out_f32, _Float16* hs,
                                  float (&red)[kWinWaves][16][kWinT], Wait&& wait) {
+  constexpr int kDnBatch = dn_batch<Q>();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int I = ex.I;
   const int c = lane >> 4, r16 = lane & 15;

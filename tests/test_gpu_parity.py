@@ -160,6 +160,33 @@ def test_layer_call(cid, T, mode):
     ex.close()
 
 
+@pytest.mark.parametrize("name,kw", [("f32 activations", dict(xdtype="f32")),
+                                     ("k=16: 64 assignments", dict(k=16)),
+                                     ("k=20: two-kernel window", dict(k=20)),
+                                     ("H=4096, I=256", dict(H=4096, I=256, E=16, k=2)),
+                                     ("Q3, H=1024", dict(qtype=3, H=1024, E=64, k=4))])
+def test_layer_window_variants(name, kw):
+    """The decode window at the config-1 shapes with float32 activations, at
+    the one-kernel form's assignment limit (T k = 64) and past it (the
+    two-kernel form at H = 2048), and at the one-kernel form's other shapes
+    (H = 4096 with I = 256; Q3 at H = 1024), against the oracle."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfg = CONFIGS[1].with_(**kw)
+    lay = make_layer(cfg, seed=23)
+    dev = upload(lay)
+    ex = experts_of(lay, dev)
+    log(f"[window variant] {name}")
+    idx, gates, y = moe.layer(dev["logits"], dev["x"], ex, cfg.k)
+    torch.cuda.synchronize()
+    idx_o, g_o = oracle.route(lay["logits"], cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_o)
+    err = rel_l2_rows(y_to_f64(y), oracle_rows(lay, idx_o, g_o))
+    log(f"[window variant] {name}: max rel-L2 {err.max():.3e}")
+    assert err.max() <= TOL_FAST
+    ex.close()
+
+
 def test_layer_window_shared_workspace():
     """One zero-filled workspace serves window calls of two layer instances,
     repeated, with a 64-token call of the same experts in between: the
