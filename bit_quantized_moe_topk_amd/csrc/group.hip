@@ -23,13 +23,29 @@ constexpr int kSeg = 1024;  // assignment ids per wave segment
 
 __device__ inline int key_bits(int E) { return E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1)); }
 
+// The expert ids of up to 16 chunks of 64 consecutive assignment ids, loaded
+// before any is used so that one memory round trip covers them all (ids past
+// f1 read as -1).
+constexpr int kBatch = 16;
+__device__ inline void load_chunks(const int32_t* __restrict__ idx, int base, int f1,
+                                   int (&e)[kBatch]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int f = base + 64 * u + lane;
+    e[u] = f < f1 ? idx[f] : -1;
+  }
+}
+
 // Count the experts of ids [f0, f1) into hist[e * stride] (LDS, zeroed by caller).
 __device__ inline void wave_count(const int32_t* __restrict__ idx, int f0, int f1, int E,
                                   int* hist, int stride) {
-  const int lane = threadIdx.x & 63;
-  for (int f = f0 + lane; f < f1; f += 64) {
-    const int e = idx[f];
-    if (e >= 0 && e < E) atomicAdd(&hist[e * stride], 1);
+  for (int base = f0; base < f1; base += 64 * kBatch) {
+    int ev[kBatch];
+    load_chunks(idx, base, f1, ev);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (ev[u] >= 0 && ev[u] < E) atomicAdd(&hist[ev[u] * stride], 1);
   }
 }
 
@@ -40,23 +56,28 @@ __device__ inline void wave_scatter(const int32_t* __restrict__ idx, int f0, int
   const int lane = threadIdx.x & 63;
   const int nbits = key_bits(E);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = f0; base < f1; base += 64) {
-    const int f = base + lane;
-    const int e = f < f1 ? idx[f] : -1;
-    const bool ok = e >= 0 && e < E;
-    uint64_t mask = __ballot(ok);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = ok && ((e >> b) & 1);
-      const uint64_t bal = __ballot(bit);
-      mask &= bit ? bal : ~bal;
-    }
-    if (ok) {
-      const int rank = __popcll(mask & below);
-      const int n = __popcll(mask);
-      const int pos = cnt[e * stride] + rank;
-      perm[pos] = f;
-      slot_of[f] = pos;
-      if (rank == n - 1) cnt[e * stride] = pos + 1;
+  for (int b0 = f0; b0 < f1; b0 += 64 * kBatch) {
+    int ev[kBatch];
+    load_chunks(idx, b0, f1, ev);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int f = b0 + 64 * u + lane;
+      const int e = ev[u];
+      const bool ok = e >= 0 && e < E;
+      uint64_t mask = __ballot(ok);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = ok && ((e >> b) & 1);
+        const uint64_t bal = __ballot(bit);
+        mask &= bit ? bal : ~bal;
+      }
+      if (ok) {
+        const int rank = __popcll(mask & below);
+        const int n = __popcll(mask);
+        const int pos = cnt[e * stride] + rank;
+        perm[pos] = f;
+        slot_of[f] = pos;
+        if (rank == n - 1) cnt[e * stride] = pos + 1;
+      }
     }
   }
 }
@@ -213,21 +234,36 @@ __global__ __launch_bounds__(1024) void group_scan(int T, int k, int E, int has_
   }
 }
 
-// Step 3: per-segment stable scatter from the scanned bases.
+// Step 3: per-segment stable scatter from the scanned bases. One workgroup
+// per segment; its four waves take consecutive quarters of the segment, count
+// their experts, and start from the segment's base plus the earlier quarters'
+// counts, so the order stays ascending within every expert.
 __global__ __launch_bounds__(256) void group_scatter(const int32_t* __restrict__ idx, int T, int k,
                                                      int E, int nseg, const int* hist,
                                                      int32_t* perm, int32_t* slot_of) {
-  extern __shared__ int lds[];  // [4][E]
+  extern __shared__ int lds[];  // [4][E] quarter counts, then bases
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int seg = blockIdx.x * 4 + w;
-  if (seg >= nseg) return;  // no barrier below: each wave only touches its own LDS row
-  int* cnt = lds + w * E;
-  for (int e = lane; e < E; e += 64) cnt[e] = hist[(size_t)seg * E + e];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+  const int seg = blockIdx.x;
   const int AR = T * k;
   const int f0 = seg * kSeg, f1 = min(AR, f0 + kSeg);
-  wave_scatter(idx, f0, f1, E, cnt, 1, perm, slot_of);
+  const int g0 = min(f1, f0 + w * (kSeg / 4)), g1 = min(f1, g0 + kSeg / 4);
+  int* cnt = lds + w * E;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  wave_count(idx, g0, g1, E, cnt, 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int run = hist[(size_t)seg * E + e];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = lds[q * E + e];
+      lds[q * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  wave_scatter(idx, g0, g1, E, cnt, 1, perm, slot_of);
 }
 
 inline int nseg_of(int T, int k) { return (T * k + kSeg - 1) / kSeg; }
@@ -278,7 +314,7 @@ hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared,
                      hist, perm, slot_of);
   MOE_LAUNCH("group_scan", s, group_scan, dim3(1), dim3(1024), 0, s, T, k, E, has_shared, nseg, hist,
                      counts, offsets);
-  MOE_LAUNCH("group_scatter", s, group_scatter, dim3(blocks), dim3(256), lds, s, idx, T, k, E, nseg, hist,
+  MOE_LAUNCH("group_scatter", s, group_scatter, dim3(nseg), dim3(256), lds, s, idx, T, k, E, nseg, hist,
                      perm, slot_of);
   return hipGetLastError();
 }
