@@ -36,11 +36,21 @@ namespace {
 
 constexpr int kBM = 128;          // assignments per tile
 constexpr int kBK = 64;           // K per stage
-constexpr int kRow = 72;          // LDS row stride in halves (64 + 8 pad: 144 B)
+// Activation stage in LDS: kBM rows of 64 halves (128 B), the eight 16-byte
+// chunks of row m stored at chunk position q ^ (m & 7), so that the 32 rows a
+// fragment read touches spread over all banks without padding rows (which
+// lets a wave's direct global-to-LDS load fill 8 whole rows).
+constexpr int kRow = 64;
 // Epilogue staging per wave (16-bit outputs): down, 64 assignments x 64 rows
 // (stride 72); gate/up, 128 assignments x 32 rows (stride 40).
 constexpr int kStage = 128 * 40;
 __device__ inline half8_t frag(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
+
+// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_wave + 16 l (lds_wave must be the same for the whole wave).
+__device__ inline void lds_load16(const uint4* src, uint4* lds_wave) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave, 16, 0, 0);
+}
 
 // Two consecutive quantisation blocks of one weight row (the blocks a lane
 // needs for two consecutive stages): codes, third bits (Q3), d and m.
@@ -72,10 +82,12 @@ template <int NI, int Q>
 __device__ inline void stage_mma(const _Float16* xb, const WStage (&w)[2],
                                  float16_t (&acc)[4][2]) {
   const int lane = threadIdx.x & 63;
-  const _Float16* ap = xb + (lane & 31) * kRow + 32 * (lane >> 5);
+  // row 32 i + lane % 32, logical chunk 4 h + kk (h = lane / 32), swizzled
+  const _Float16* ap = xb + (lane & 31) * kRow;
+  const int hq = 4 * (lane >> 5), sw = lane & 7;
   half8_t af[2][NI], bf[2][2];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) af[0][i] = frag(ap + 32 * i * kRow);
+  for (int i = 0; i < NI; ++i) af[0][i] = frag(ap + 32 * i * kRow + 8 * (hq ^ sw));
 #pragma unroll
   for (int j = 0; j < 2; ++j) bf[0][j] = wfrag<Q>(w[j], 0);
 #pragma unroll
@@ -83,7 +95,7 @@ __device__ inline void stage_mma(const _Float16* xb, const WStage (&w)[2],
     const int c = kk & 1, n = c ^ 1;
     if (kk < 3) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) af[n][i] = frag(ap + 32 * i * kRow + 8 * (kk + 1));
+      for (int i = 0; i < NI; ++i) af[n][i] = frag(ap + 32 * i * kRow + 8 * ((hq + kk + 1) ^ sw));
 #pragma unroll
       for (int j = 0; j < 2; ++j) bf[n][j] = wfrag<Q>(w[j], kk + 1);
     }
@@ -207,7 +219,8 @@ template <int Q, bool DOWN, int NW, bool TILED>
 __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   constexpr int NT = 64 * NW;                 // threads
   constexpr int CH = kBM * (kBK / 8) / NT;    // 16-byte activation chunks per thread per stage
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2][kBM * kRow];
+  __shared__ __attribute__((aligned(16))) _Float16 xs0[kBM * kRow];  // even stages
+  __shared__ __attribute__((aligned(16))) _Float16 xs1[kBM * kRow];  // odd stages
   __shared__ __attribute__((aligned(16))) uint16_t ostage[NW][kStage];  // epilogue, per wave
   __shared__ TileMap wm;
   __shared__ int offs[MOE_MAX_E_DEV + 2];
@@ -225,17 +238,22 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const uint16_t* a16 = DOWN ? static_cast<const uint16_t*>(a.h) : a.x16;
 
-  // ---- activation cursor: chunk tid + NT u = row (c >> 3), LDS column 8 (c & 7) ----
-  // LDS column 8 q of stage s holds K column 32 (s + S (q / 4)) + 8 (q % 4).
+  // ---- activation cursor: wave w fills rows 8 (CH w + u) .. + 7 of a stage
+  // (u < CH) with one direct global-to-LDS load each: lane l lands at chunk
+  // position l % 8 of row 8 (CH w + u) + l / 8, so it loads logical chunk
+  // q = (l % 8) ^ (l / 8). Logical chunk q of stage s holds K column
+  // 32 (s + S (q / 4)) + 8 (q % 4) (canonical planes) or 64 s + 8 q (tiled).
   const uint4* x4 = reinterpret_cast<const uint4*>(a16);
   uint32_t xoff[CH];      // next stage's source chunk in 16-byte units (~0u: row past M)
   int anext[CH];
   int xt = 0, xsg = 0;    // tile round and stage of the next activation load
+  const int xq = (lane & 7) ^ (lane >> 3);
+  auto xrow = [&](int u) { return 8 * (CH * wave + u) + (lane >> 3); };
   auto xprep = [&](int r) {  // tile r's rows: permutation entries, not yet waited on
     const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of<kClasses>(r));
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int m = (tid + NT * u) >> 3;
+      const int m = xrow(u);
       anext[u] = m >= t.M ? -1 : (DOWN ? t.slot0 + m : a.perm[t.slot0 + m]);
     }
   };
@@ -247,17 +265,19 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
         r = token_of(r, a.T, a.k);
         r = (unsigned)r < (unsigned)a.T ? r : -1;
       }
-      const int q = (tid + NT * u) & 7;
-      const int col = TILED ? 8 * q : 32 * S * (q >> 2) + 8 * (q & 3);
+      const int col = TILED ? 8 * xq : 32 * S * (xq >> 2) + 8 * (xq & 3);
       xoff[u] = r < 0 ? ~0u : (uint32_t)(((size_t)r * K + col) / 8);
     }
   };
-  auto xload = [&](uint4 (&v)[CH]) {
+  // One stage into buf. Rows past M are not loaded: their LDS rows keep
+  // stale values, which only reach output rows the epilogue never stores.
+  auto xdma = [&](_Float16* buf) {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      // rows past M stay zero and are never loaded
-      v[u] = xoff[u] != ~0u ? x4[xoff[u]] : make_uint4(0, 0, 0, 0);
-      if (xoff[u] != ~0u) xoff[u] += TILED ? 8 : 4;  // the next stage
+      if (xoff[u] != ~0u) {
+        lds_load16(x4 + xoff[u], reinterpret_cast<uint4*>(buf) + 64 * (CH * wave + u));
+        xoff[u] += TILED ? 8 : 4;  // the next stage
+      }
     }
     if (++xsg == S) {
       xsg = 0;
@@ -265,13 +285,6 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
         xfin();
         if (xt + 1 < n_my) xprep(xt + 1);
       }
-    }
-  };
-  auto xstore = [&](const uint4 (&v)[CH], _Float16* buf) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int c = tid + NT * u;
-      *reinterpret_cast<uint4*>(buf + (c >> 3) * kRow + 8 * (c & 7)) = v[u];
     }
   };
 
@@ -318,14 +331,10 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   xfin();
   if (n_my > 1) xprep(1);
   wsetup(0);
-  uint4 xa[CH], xb[CH];  // activation stages in flight: even stages in xa, odd in xb
   WPair wq[2];           // the current stage pair's weight blocks
-  xload(xa);
-  xload(xb);             // total >= 2
-  wload(wq);
-  xstore(xa, xs[0]);
-  if (total > 2) xload(xa);
-  __syncthreads();
+  xdma(xs0);             // stage 0
+  wload(wq);             // stage pair 0, 1
+  __syncthreads();       // waits for the LDS writes of stage 0
 
   int g = 0;  // global stage index
   // One tile whose assignments fill LIVE 32-row activation groups; MFMAs of
@@ -345,23 +354,22 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = float16_t{};
     for (int s = 0; s < S; s += 2, g += 2) {
-      // even stage g: LDS buffer 0, weight block 0 of the pair
+      // even stage g: xs0, weight block 0 of the pair; stage g + 1 streams
+      // into xs1 (its last readers passed the previous barrier)
       WStage w[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) w[j] = wstage<Q>(wq[j], 0);
-      xstore(xb, xs[1]);             // stage g + 1 (total is even)
-      if (g + 3 < total) xload(xb);  // stage g + 3
-      stage_mma<LIVE, Q>(xs[0], w, acc);
-      __syncthreads();
-      // odd stage g + 1: LDS buffer 1, weight block 1
+      xdma(xs1);                     // stage g + 1 (total is even)
+      stage_mma<LIVE, Q>(xs0, w, acc);
+      __syncthreads();               // also waits for stage g + 1's LDS writes
+      // odd stage g + 1: xs1, weight block 1
 #pragma unroll
       for (int j = 0; j < 2; ++j) w[j] = wstage<Q>(wq[j], 1);
       if (g + 2 < total) {
         wload(wq);                   // stage pair g + 2, g + 3
-        xstore(xa, xs[0]);           // stage g + 2
+        xdma(xs0);                   // stage g + 2
       }
-      if (g + 4 < total) xload(xa);  // stage g + 4
-      stage_mma<LIVE, Q>(xs[1], w, acc);
+      stage_mma<LIVE, Q>(xs1, w, acc);
       if (s + 2 < S) __syncthreads();
     }
     // ---- epilogue ----
