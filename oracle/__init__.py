@@ -58,6 +58,32 @@ def _acc(prec: str):
     return np.float32 if prec == "f32" else np.float64
 
 
+def _bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact: bf16 is the top half of a float32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def router_logits(x: np.ndarray, w_bits: np.ndarray, bias=None) -> np.ndarray:
+    """Router scores in front of the top-k, float64 ``[T, E]``.
+
+    The pages keep the routers on the GPU and route each token to the experts
+    its router scores highest ("Strata - the details", "How it works"; Strata
+    README, "How does it work?"); the score is the plain product of the
+    token's hidden state with each expert's router row: ``logits[t, e] =
+    sum_h x[t, h] * w[e, h] (+ bias[e])``. ``x``: float32, or uint16 bf16
+    bits; ``w_bits``: uint16 bf16 bits ``[E, H]``; ``bias``: float32 ``[E]``
+    or None. Products and sums in float64 (a matrix product as one step).
+    """
+    xd = _bf16_to_f64(x) if np.asarray(x).dtype == np.uint16 else np.asarray(x, dtype=np.float64)
+    wd = _bf16_to_f64(w_bits)
+    if xd.ndim != 2 or wd.ndim != 2 or xd.shape[1] != wd.shape[1]:
+        raise ValueError("x [T, H] and w [E, H] must share H")
+    out = xd @ wd.T
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=np.float64)[None, :]
+    return out
+
+
 def route(logits: np.ndarray, k: int):
     """Top-k experts per token (ties to the lower index) and their softmax gates."""
     logits = np.ascontiguousarray(logits, dtype=np.float32)

@@ -34,7 +34,11 @@ Draw recipe (one seed generates everything)
 * router logits ``N(0,1)`` per token and expert, plus, for the skewed
   workloads, a per-layer bias ``-1.1 * ln(rank_e)`` where ``rank`` is a seeded
   permutation of ``1..E`` (a Zipf(1.1) expert popularity shared by every token
-  and stream of the layer).
+  and stream of the layer);
+* for the router in front of the layer: a bf16 router matrix ``[E][H]`` with
+  entries ``N(0,1)/sqrt(H)`` (so ``x . w_e`` is about ``N(0,1)`` for N(0,1)
+  activations) and, for the skewed workloads, the same per-layer Zipf bias as
+  a float32 vector ``[E]`` (zeros otherwise).
 """
 from __future__ import annotations
 
@@ -43,7 +47,7 @@ import numpy as np
 from .configs import LayerConfig
 
 # SeedSequence stream tags
-_S_LOGITS, _S_WEIGHTS, _S_ZIPF, _S_X = 0, 1, 2, 3
+_S_LOGITS, _S_WEIGHTS, _S_ZIPF, _S_X, _S_ROUTER = 0, 1, 2, 3, 4
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -83,6 +87,13 @@ def make_logits(cfg: LayerConfig, seed: int, layer: int = 0) -> np.ndarray:
     if cfg.zipf:
         noise = noise + zipf_bias(cfg, seed, layer)[None, :]
     return noise.astype(np.float32)
+
+
+def make_router(cfg: LayerConfig, seed: int, layer: int = 0):
+    """Router inputs: ``(w uint16 bf16 bits [E, H], bias float32 [E])``."""
+    w = _rng(seed, cfg.cid, layer, _S_ROUTER).standard_normal((cfg.E, cfg.H)) / np.sqrt(cfg.H)
+    bias = zipf_bias(cfg, seed, layer) if cfg.zipf else np.zeros(cfg.E)
+    return f32_to_bf16_bits(w.astype(np.float32)), bias.astype(np.float32)
 
 
 def make_x(cfg: LayerConfig, seed: int, layer: int = 0) -> np.ndarray:
