@@ -310,6 +310,37 @@ def run_decode(cfg, args):
     return res, hosts, insts
 
 
+def router_timing(args, reps: int = 50) -> dict:
+    """The router product in front of the layer (moe_router_logits), timed
+    with kernel-attached events at the decode window and the 8K chunk: not
+    part of the layer step above, which starts from logits."""
+    import torch
+    import bit_quantized_moe_topk_amd as moe
+    from synth import CONFIGS, make_router, make_x
+    out = {}
+    for name, cfg in (("decode_t4", CONFIGS[1]), ("prefill_t8192", CONFIGS[3])):
+        w, bias = make_router(cfg, args.seed)
+        x = torch.from_numpy(make_x(cfg, args.seed).view(np.int16)).cuda().view(torch.bfloat16)
+        wt = torch.from_numpy(w.view(np.int16)).cuda()
+        bt = torch.from_numpy(bias).cuda()
+        for _ in range(3):
+            moe.router_logits(x, wt, bt)
+        torch.cuda.synchronize()
+        moe.profile_begin(4 * reps)
+        gpu_hold(5.0)
+        for _ in range(reps):
+            moe.router_logits(x, wt, bt)
+        torch.cuda.synchronize()
+        prof = moe.profile_end()
+        kname, (n, ms) = max(prof.items(), key=lambda kv: kv[1][1])
+        us = 1e3 * ms / max(n, 1)
+        flops = 2.0 * cfg.T * cfg.H * cfg.E
+        out[name] = {"kernel": kname, "us": round(us, 2), "router_bytes": cfg.E * cfg.H * 2,
+                     "GB_s": round(cfg.E * cfg.H * 2 / (us * 1e-6) / 1e9, 1),
+                     "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 2)}
+    return out
+
+
 def run_prefill(cfg, args):
     import torch
     import bit_quantized_moe_topk_amd as moe
@@ -461,6 +492,9 @@ def main() -> int:
         log(f"prefill: {pre['tokens_per_s_end_to_end']:.0f} tokens/s end to end, "
             f"{pre['ms_per_layer']:.3f} ms/layer, mfma_gateup {pre['roofline']['achieved']} TFLOP/s")
 
+    router = router_timing(args)
+    log(f"router: {router}")
+
     cpu = None
     if not args.no_cpu_baseline and hosts:
         cpu = cpu_baseline(cfg, hosts, args)
@@ -492,6 +526,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "decode_detail": {k: v for k, v in dec.items() if k not in ("roofline",)},
         "prefill_8k": pre,
+        "router": router,
     }
     print(json.dumps(line), flush=True)
     return 0

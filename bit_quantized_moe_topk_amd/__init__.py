@@ -49,6 +49,8 @@ def lib() -> C.CDLL:
         P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = C.c_char_p
+        L.moe_router_logits.argtypes = [P, i32, i32, i32, P, P, i32, P, P]
+        L.moe_router_logits.restype = C.c_int
         L.moe_route_topk.argtypes = [P, i32, i32, i32, P, P, P]
         L.moe_route_topk.restype = C.c_int
         L.moe_group_workspace_size.argtypes = [i32, i32, i32]
@@ -127,6 +129,26 @@ def _need_cuda(name: str, t: torch.Tensor, dtype=None):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def router_logits(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None):
+    """Router scores x . w[e] (+ bias[e]): float32 [T, E]. x: f32 or bf16 [T, H];
+    w: bf16 [E, H] (or its uint16/int16 bit patterns); bias: f32 [E] or None."""
+    _need_cuda("x", x, (torch.float32, torch.bfloat16))
+    if w.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous CUDA bf16 (or 16-bit pattern) tensor [E, H]")
+    if bias is not None:
+        _need_cuda("bias", bias, torch.float32)
+    T, H = x.shape
+    E = w.shape[0]
+    if w.shape[1] != H or (bias is not None and bias.numel() != E):
+        raise ValueError("shape mismatch between x, w and bias")
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    xdt = F32 if x.dtype == torch.float32 else BF16
+    _check("moe_router_logits", lib().moe_router_logits(_ptr(x), xdt, T, H, _ptr(w),
+                                                        _ptr(bias) if bias is not None else None,
+                                                        E, _ptr(logits), _stream()))
+    return logits
 
 
 def route_topk(logits: torch.Tensor, k: int):
@@ -309,5 +331,5 @@ def layer(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fa
     return idx, gates, y
 
 
-__all__ = ["layer", "profile_begin", "profile_end", "route_topk", "route_group", "group", "Grouping", "Experts", "ffn_q", "lib", "status_string",
+__all__ = ["layer", "profile_begin", "profile_end", "router_logits", "route_topk", "route_group", "group", "Grouping", "Experts", "ffn_q", "lib", "status_string",
            "MoeError", "Q2", "Q3", "F32", "BF16", "FAST", "CHECK_F32", "MAX_E", "LIB_PATH"]

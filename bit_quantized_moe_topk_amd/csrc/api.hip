@@ -63,6 +63,17 @@ const char* moe_status_string(int32_t status) {
   }
 }
 
+int moe_router_logits(const void* x, int32_t xdtype, int32_t T, int32_t H, const uint16_t* w,
+                      const float* bias, int32_t E, float* logits, void* stream) {
+  if (T < 0 || H < 1 || E < 1 || (xdtype != MOE_F32 && xdtype != MOE_BF16)) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_E || !moe::router_supported(H, E)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * E > 0x7FFFFFFFLL || (long long)T * H > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w || !logits || !aligned16(x) || !aligned16(w)) return MOE_ERR_INVALID_ARG;
+  return status_of(moe::launch_router(x, xdtype, T, H, w, bias, E, logits,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* idx, float* gates,
                    void* stream) {
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;

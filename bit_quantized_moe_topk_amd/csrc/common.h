@@ -116,6 +116,11 @@ bool gemv_supported(int H, int I);
 // Bytes at the head of every moe_layer workspace kept for the one-launch
 // decode window's counters (zero between calls; no other call form writes them).
 constexpr size_t kWinSyncBytes = 8192;
+// Router product (router.hip): the matrix-core kernel from this many bf16 tokens.
+constexpr int kRouterMfmaMinT = 256;
+bool router_supported(int H, int E);
+hipError_t launch_router(const void* x, int xdtype, int T, int H, const uint16_t* w,
+                         const float* bias, int E, float* logits, hipStream_t s);
 bool window_supported(const Experts& ex, int T, int k);
 size_t window_workspace_bytes(const Experts& ex, int T, int k);
 hipError_t launch_window(const float* logits, int T, int k, const Experts& ex, const void* x,

@@ -68,6 +68,21 @@ extern "C" {
 
 /* ---- routing ------------------------------------------------------------ */
 
+/* Router scores in front of the top-k: the product of each token's hidden
+ * state with every expert's router row ("Strata - the details", "How it
+ * works": routers stay on the GPU and pick the experts that score highest).
+ *   logits[t][e] = sum_h x[t][h] * w[e][h] (+ bias[e] when bias != NULL)
+ * x: [T][H], float32 (xdtype MOE_F32) or bf16 (MOE_BF16), 16-byte aligned.
+ * w: [E][H] bf16 (row e = expert e's router row), 16-byte aligned.
+ * bias: [E] float32 or NULL.  logits: [T][E] float32.
+ * Products of bf16 values are exact in float32; sums are float32 in a fixed
+ * order (reproducible run to run; with bf16 x, at least 256 tokens and E a
+ * multiple of 128 the order is the matrix cores', else a lane split of H).
+ * Requires H % 256 == 0, H <= 4096, 1 <= E <= MOE_MAX_E, T >= 0 (T == 0: no
+ * launch). The result feeds moe_route_topk, moe_route_group or moe_layer. */
+int moe_router_logits(const void *x, int32_t xdtype, int32_t T, int32_t H, const uint16_t *w,
+                      const float *bias, int32_t E, float *logits, void *stream);
+
 /* Top-k expert selection and gates, per token.
  *
  * Per token t (the router step of "How it works"; 10 of 512 experts per token):

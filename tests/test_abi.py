@@ -131,3 +131,20 @@ def test_tiled_copy_validation():
             assert L.moe_experts_attach_tiled(h, None, 0, None) == moe.OK     # detach
         finally:
             L.moe_experts_destroy(h)
+
+
+def test_router_validation():
+    L = moe.lib()
+    bf16 = 1
+    # T == 0 launches nothing
+    assert L.moe_router_logits(FAKE, bf16, 0, 256, FAKE, None, 16, FAKE, None) == moe.OK
+    # H must be a multiple of 256; E within the limit; dtype known
+    assert L.moe_router_logits(FAKE, bf16, 4, 128, FAKE, None, 16, FAKE, None) == moe.ERR_UNSUPPORTED
+    assert L.moe_router_logits(FAKE, bf16, 4, 256, FAKE, None, 4096, FAKE, None) == moe.ERR_UNSUPPORTED
+    assert L.moe_router_logits(FAKE, 7, 4, 256, FAKE, None, 16, FAKE, None) == moe.ERR_INVALID_ARG
+    # missing or misaligned buffers
+    assert L.moe_router_logits(None, bf16, 4, 256, FAKE, None, 16, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_router_logits(FAKE, bf16, 4, 256, None, None, 16, FAKE, None) == moe.ERR_INVALID_ARG
+    assert L.moe_router_logits(C.c_void_p(0x10008), bf16, 4, 256, FAKE, None, 16, FAKE,
+                               None) == moe.ERR_INVALID_ARG
+    assert L.moe_router_logits(FAKE, bf16, -1, 256, FAKE, None, 16, FAKE, None) == moe.ERR_INVALID_ARG
