@@ -271,13 +271,16 @@ def run_decode(cfg, args):
     pb = expert_plane_bytes(cfg)
     step_layers = [stats[s % len(insts)] for s in range(K)]
     kname = max((k for k in prof
-                 if k in ("win_layer", "win_gateup", "gemv_gateup", "win_down", "gemv_down")),
-                key=lambda k: prof[k][1])
+                 if k in ("win_layer", "win_gateup", "gemv_gateup", "win_down", "gemv_down",
+                          "bat_gateup", "bat_down")),
+                key=lambda k: prof[k][1], default="")
+    if not kname:
+        raise RuntimeError(f"no decode expert kernel in the profile: {sorted(prof)}")
     if kname == "win_layer":  # the whole window in one kernel: gate/up and down planes
         unit = pb["gateup"] + pb["down"]
     else:
         unit = pb["gateup"] if "gateup" in kname else pb["down"]
-    per_step_units = [st["touched"] if kname.startswith("win") else st["gemv_experts"]
+    per_step_units = [st["touched"] if kname.startswith(("win", "bat")) else st["gemv_experts"]
                       for st in step_layers]
     k_bytes = sum(per_step_units) * unit
     n_k, k_ms = prof[kname]
@@ -289,7 +292,6 @@ def run_decode(cfg, args):
         "graph": graphs is not None,
         "kernels_us": kernels_us,
         "touched_experts_mean": float(np.mean([st["touched"] for st in stats])),
-        "gemv_experts_mean": float(np.mean([st["gemv_experts"] for st in stats])),
         "layer_weight_bytes_mean": float(touched_bytes),
         "layer_hbm_gbs": float(touched_bytes / (ms_per_step * 1e-3) / 1e9),
         "roofline": {
@@ -441,6 +443,7 @@ def main() -> int:
     ap.add_argument("--stage-calls", action="store_true",
                     help="decode steps call route_group + ffn_q instead of moe_layer")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-batched", action="store_true", help="skip the config-4 batched decode")
     ap.add_argument("--prefill-layers", type=int, default=0, help="0 = all 48")
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-tiled", action="store_true",
@@ -486,6 +489,27 @@ def main() -> int:
     del insts
     torch.cuda.empty_cache()
 
+    # batched decode (config 4: 16 streams x 4 tokens, Q3): reported beside the
+    # headline, through the general path (route + group, GEMV and matrix-core
+    # experts, combine)
+    bat = None
+    if not args.no_batched:
+        import copy
+        bargs = copy.copy(args)
+        bargs.rotation = 16
+        bargs.cpu_layers = 0
+        b, _, binsts = run_decode(CONFIGS[4], bargs)
+        for it in binsts:
+            it.ex.close()
+        del binsts
+        torch.cuda.empty_cache()
+        bat = {"workload": "batched decode: 16 streams x 4 tokens (T = 64) through one MoE layer "
+                           "(hidden 2048, 512 routed + 1 shared experts, top-10, intermediate 512, "
+                           "Q3 weights, bf16 activations); steps rotate over 16 seeded layer instances",
+               **{k: v for k, v in b.items()}}
+        log(f"batched decode: {b['tokens_per_s']:.0f} tokens/s, {b['ms_per_step'] * 1e3:.1f} us/step, "
+            f"layer {b['layer_hbm_gbs']:.0f} GB/s")
+
     pre = None
     if not args.no_prefill:
         pre = run_prefill(CONFIGS[3], args)
@@ -526,6 +550,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "decode_detail": {k: v for k, v in dec.items() if k not in ("roofline",)},
         "prefill_8k": pre,
+        "batched_decode_q3": bat,
         "router": router,
     }
     print(json.dumps(line), flush=True)

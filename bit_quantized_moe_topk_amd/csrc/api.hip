@@ -242,9 +242,13 @@ int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, c
     // From a few hundred tokens on, experts with few assignments ride in the
     // persistent matrix-core grid, where their weight reads overlap the other
     // tiles' arithmetic; a separate GEMV pass would run on its own.
-    const bool small_batch = T < moe::kGemvBatchLimit || !moe::mfma_supported(d.H, d.I);
-    a.gmax = moe::gemv_supported(d.H, d.I) && small_batch ? moe::kGemvMaxTokens : 0;
-    e = moe::launch_ffn_fast(d, a, s);
+    if (T < moe::kGemvBatchLimit && moe::batch_supported(d.H, d.I)) {
+      e = moe::launch_batch(d, a, s);
+    } else {
+      const bool small_batch = T < moe::kGemvBatchLimit || !moe::mfma_supported(d.H, d.I);
+      a.gmax = moe::gemv_supported(d.H, d.I) && small_batch ? moe::kGemvMaxTokens : 0;
+      e = moe::launch_ffn_fast(d, a, s);
+    }
   }
   if (e == hipSuccess) e = moe::launch_combine(d, a, s);
   return status_of(e);

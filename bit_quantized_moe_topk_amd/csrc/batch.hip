@@ -1,0 +1,478 @@
+// Expert FFN for small batches (up to a few hundred tokens, e.g. 16 decode
+// streams of a 4-token verify window) on gfx950 matrix cores.
+//
+// Each expert holds at most T of the batch's assignments, so the layer is
+// bound by reading the touched experts' packed weights once ("Strata - the
+// details", "Other GPUs": speed follows memory bandwidth). The work is cut
+// into many items of equal cost, one per (touched expert, chunk of output
+// rows, group of 16 of the expert's tokens), so that every CU streams weights
+// and no expert with many tokens leaves a long tail:
+//
+//   bat_gateup: chunk = 4 groups of 16 rows of I, for gate and up. The 8
+//               waves split K (wave w takes blocks w H/256 ...; lane group
+//               c = lane / 16 takes NBL consecutive blocks of its row). The
+//               lane's 16 tokens stay in registers as the fp16 operand of
+//               v_mfma_f32_16x16x32_f16 while the four row groups' weights
+//               stream through two register sets, dequantised in registers
+//               (deq16.h); the next item's first weights are requested while
+//               the last row groups compute. Each row group's eight partial
+//               tiles are summed in LDS in wave order, then SwiGLU; h is
+//               stored as fp16 in the MFMA K order.
+//   bat_down  : chunk = 256 rows of H (wave w: two groups of 16 rows over all
+//               of K = I). The item's 16 h rows come into LDS (double-buffered
+//               across items, the next item's rows requested early); outputs
+//               are scaled by the routing gate and stored per assignment slot
+//               for the combine.
+//
+// Both grids are persistent (two workgroups per CU): every workgroup builds a
+// map of the grouping in LDS (token groups per expert, slot offsets, and the
+// token id or gate of every slot) and takes items dealt round-robin; an
+// expert's consecutive items, which read the same weights, go to workgroups
+// of one XCD.
+#include "common.h"
+#include "deq16.h"
+#include "gemv.h"
+#include "sched.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBThreads = 512;
+constexpr int kBWaves = kBThreads / 64;
+constexpr int kGuRows = 4;     // 16-row groups of I per gate/up item
+constexpr int kDnRows = 2;     // 16-row groups of H per wave in a down item
+constexpr int kBMaxI = 512;
+constexpr int kBTab = 4096;    // slots whose token id / gate fit the LDS table
+
+// Grouping map of one launch in LDS.
+struct BatMap {
+  int base[MOE_MAX_E_DEV + 2];  // exclusive prefix over experts of ceil(M / 16)
+  int off[MOE_MAX_E_DEV + 2];   // slot offsets (offsets[0..E_tot])
+  int wsum[16];
+  int n;                        // token groups in all
+};
+
+// One item: expert e, output-row chunk, token group tg (tokens 16 tg ..).
+struct BatItem {
+  int e, chunk, tg, M, slot0;
+};
+
+// Fills the map, and tab[s] = fill(s) for every slot when the table is used;
+// all threads of the block call it.
+template <typename Fill>
+__device__ inline void batmap_init(BatMap& bm, const FfnArgs& a, int E_tot, bool use_tab, int A,
+                                   Fill&& fill) {
+  for (int e = threadIdx.x; e <= E_tot; e += blockDim.x) {
+    const int o = a.offsets[e];
+    bm.off[e] = o;
+    if (e < E_tot) bm.base[e] = (a.counts[e] + 15) >> 4;
+  }
+  if (use_tab)
+    for (int s = threadIdx.x; s < A; s += blockDim.x) fill(s);
+  __syncthreads();
+  const int n = block_exclusive_scan(bm.base, E_tot, bm.wsum);
+  if (threadIdx.x == 0) {
+    bm.base[E_tot] = n;
+    bm.n = n;
+  }
+  __syncthreads();
+}
+
+// Items of expert e are NC * G_e consecutive numbers from NC * base[e], in
+// (chunk, token group) order.
+__device__ inline BatItem bat_item(const BatMap& bm, int E_tot, int NC, int item) {
+  const int e = workmap_find(bm.base, E_tot, item / NC);
+  const int g0 = bm.base[e], G = bm.base[e + 1] - g0;
+  const int local = item - NC * g0;
+  BatItem it;
+  it.e = __builtin_amdgcn_readfirstlane(e);
+  it.chunk = __builtin_amdgcn_readfirstlane(local / G);
+  it.tg = __builtin_amdgcn_readfirstlane(local % G);
+  it.slot0 = __builtin_amdgcn_readfirstlane(bm.off[e]);
+  it.M = __builtin_amdgcn_readfirstlane(bm.off[e + 1] - bm.off[e]);
+  return it;
+}
+
+// First item of this workgroup; later ones follow every gridDim.x. Consecutive
+// item numbers go to workgroups of one XCD (workgroup g runs on XCD g % 8)
+// when the grid is a multiple of 8.
+__device__ inline int bat_first() {
+  const int g = blockIdx.x, G = gridDim.x;
+  return (G % 8) ? g : (g % 8) * (G / 8) + g / 8;
+}
+
+// --- gate/up ----------------------------------------------------------------
+
+// The lane's token operand: 8 kk .. 8 kk + 7 of each of its NBL blocks, fp16
+// in the MFMA K order (each group of four as 0, 2, 1, 3). XBF16: converted
+// from the bf16 activations (round to nearest even); else read from the fp16
+// copy.
+template <int NBL, bool XBF16>
+__device__ inline void load_xop(const FfnArgs& a, int H, int t, bool live, int kb0,
+                                half8_t (&xf)[NBL][4]) {
+  if (!live) {
+#pragma unroll
+    for (int b = 0; b < NBL; ++b)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) xf[b][kk] = half8_t{};
+    return;
+  }
+  const uint16_t* row = (XBF16 ? static_cast<const uint16_t*>(a.x) : a.x16) + (size_t)t * H + 32 * kb0;
+  const uint4* src = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+  for (int b = 0; b < NBL; ++b)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 v = src[4 * b + kk];
+      xf[b][kk] = XBF16 ? __builtin_bit_cast(half8_t, make_uint4(pack_half2(bf16_lo(v.x), bf16_lo(v.y)),
+                                                                 pack_half2(bf16_hi(v.x), bf16_hi(v.y)),
+                                                                 pack_half2(bf16_lo(v.z), bf16_lo(v.w)),
+                                                                 pack_half2(bf16_hi(v.z), bf16_hi(v.w))))
+                        : __builtin_bit_cast(half8_t, v);
+    }
+}
+
+// One row group: the wave's partial gate and up tiles into red. Four
+// accumulators (gate and up, each split in two by operand part or step
+// parity) keep consecutive MFMAs independent, so none waits on the previous
+// one's result.
+template <int Q, int NBL>
+__device__ inline void gu_partial(const WRow<NBL>& wg, const WRow<NBL>& wu, const half8_t (&xf)[NBL][4],
+                                  float (&red)[kBWaves][2][16][17]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane >> 4, r16 = lane & 15;
+  floatx4_t ag0 = {}, ag1 = {}, au0 = {}, au1 = {};
+#pragma unroll
+  for (int b = 0; b < NBL; ++b) {
+    if constexpr (Q == 3) {
+      // gate, then up: the split operands' planes of one row at a time
+      const WSplit sg = wsplit_block(wg.c[2 * b], wg.c[2 * b + 1], wg.hi[b], wg.dm[b]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        ag0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_lo(sg, kk), xf[b][kk], ag0, 0, 0, 0);
+        ag1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_hi(sg, kk), xf[b][kk], ag1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const WSplit su = wsplit_block(wu.c[2 * b], wu.c[2 * b + 1], wu.hi[b], wu.dm[b]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        au0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_lo(su, kk), xf[b][kk], au0, 0, 0, 0);
+        au1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_hi(su, kk), xf[b][kk], au1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      const WStage sg = wstage_block<Q>(wg.c[2 * b], wg.c[2 * b + 1], wg.hi[b], wg.dm[b]);
+#pragma unroll
+      for (int kk = 0; kk < 4; kk += 2) {
+        ag0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sg, kk), xf[b][kk], ag0, 0, 0, 0);
+        ag1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sg, kk + 1), xf[b][kk + 1], ag1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const WStage su = wstage_block<Q>(wu.c[2 * b], wu.c[2 * b + 1], wu.hi[b], wu.dm[b]);
+#pragma unroll
+      for (int kk = 0; kk < 4; kk += 2) {
+        au0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(su, kk), xf[b][kk], au0, 0, 0, 0);
+        au1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(su, kk + 1), xf[b][kk + 1], au1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // ag[v]: row 4 c + v of the group, token r16
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    red[wave][0][4 * c + v][r16] = ag0[v] + ag1[v];
+    red[wave][1][4 * c + v][r16] = au0[v] + au1[v];
+  }
+  // the caller reloads this row group's registers next: keep those loads
+  // after the arithmetic that still reads them
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Sum of the eight partial tiles (wave order), SwiGLU, h store: rows 4 q + s
+// and 4 q + s + 2 (s = 0, 1) sit side by side in the K order, one 32-bit
+// store per row pair and token. Taken by the 128 threads of waves 2 j, 2 j + 1
+// (j = row group mod 4), so the extra work rotates over the waves.
+__device__ inline void gu_finish(const float (&red)[kBWaves][2][16][17], int j, const BatItem& it,
+                                 int row0, int I, uint16_t* h) {
+  const int rt = (int)threadIdx.x - 128 * (j & 3);
+  if (rt < 0 || rt >= 128) return;
+  const int pr = rt >> 4, t = rt & 15;
+  const int m = 16 * it.tg + t;
+  if (m >= it.M) return;
+  const int ra = 4 * (pr >> 1) + (pr & 1), rb = ra + 2;
+  float ga = 0.f, ua = 0.f, gb = 0.f, ub = 0.f;
+#pragma unroll
+  for (int w = 0; w < kBWaves; ++w) {
+    ga += red[w][0][ra][t];
+    ua += red[w][1][ra][t];
+    gb += red[w][0][rb][t];
+    ub += red[w][1][rb][t];
+  }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(h + (size_t)(it.slot0 + m) * I + row0 + 4 * (pr >> 1) + 2 * (pr & 1));
+  *dst = pack_half2(silu_mul(ga, ua), silu_mul(gb, ub));
+}
+
+template <int Q, int NBL, bool XBF16>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void bat_gateup(Experts ex, FfnArgs a) {
+  constexpr int R = kGuRows;
+  __shared__ BatMap bm;
+  __shared__ int tok[kBTab];
+  __shared__ float red[2][kBWaves][2][16][17];  // two buffers: wave, gate/up, row, token
+  const int H = ex.H, I = ex.I, E_tot = ex.E_tot;
+  const int A = a.T * (a.k + ex.has_shared);
+  const bool use_tab = A <= kBTab;
+  batmap_init(bm, a, E_tot, use_tab, A, [&](int s) {
+    const int t = token_of(a.perm[s], a.T, a.k);
+    tok[s] = (unsigned)t < (unsigned)a.T ? t : 0;
+  });
+  const int NC = I / (16 * R);
+  const int n_items = bm.n * NC;
+  int item = bat_first();
+  if (item >= n_items) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int kb0 = wave * (H / 256) + NBL * (lane >> 4);  // the lane's first block of its rows
+  uint16_t* h = static_cast<uint16_t*>(a.h);
+  auto wrow = [&](const BatItem& it, int j, size_t mat0) {
+    return load_wrow<Q, NBL>(ex, mat0 + (size_t)(16 * (R * it.chunk + j) + r16) * (H / 32) + kb0);
+  };
+
+  BatItem it = bat_item(bm, E_tot, NC, item);
+  WRow<NBL> ga = wrow(it, 0, blk_gate(ex, it.e)), ua = wrow(it, 0, blk_up(ex, it.e));
+  WRow<NBL> gb = wrow(it, 1, blk_gate(ex, it.e)), ub = wrow(it, 1, blk_up(ex, it.e));
+  for (;;) {
+    half8_t xf[NBL][4];
+    {
+      const int m = 16 * it.tg + r16, slot = it.slot0 + m;
+      const bool live = m < it.M;
+      int t = 0;
+      if (live) {
+        if (use_tab) {
+          t = tok[slot];
+        } else {
+          t = token_of(a.perm[slot], a.T, a.k);
+          t = (unsigned)t < (unsigned)a.T ? t : 0;
+        }
+      }
+      load_xop<NBL, XBF16>(a, H, t, live, kb0, xf);
+    }
+    const int next = item + gridDim.x;
+    const bool more = next < n_items;
+    BatItem nx = it;
+    if (more) nx = bat_item(bm, E_tot, NC, next);
+    const int row0 = 16 * R * it.chunk;
+    // row group 0 (set a), then its weights make way for row group 2
+    gu_partial<Q, NBL>(ga, ua, xf, red[0]);
+    ga = wrow(it, 2, blk_gate(ex, it.e));
+    ua = wrow(it, 2, blk_up(ex, it.e));
+    __syncthreads();
+    gu_finish(red[0], 0, it, row0, I, h);
+    // row group 1 (set b) -> row group 3
+    gu_partial<Q, NBL>(gb, ub, xf, red[1]);
+    gb = wrow(it, 3, blk_gate(ex, it.e));
+    ub = wrow(it, 3, blk_up(ex, it.e));
+    __syncthreads();
+    gu_finish(red[1], 1, it, row0 + 16, I, h);
+    // row group 2 (set a) -> the next item's row group 0
+    gu_partial<Q, NBL>(ga, ua, xf, red[0]);
+    if (more) {
+      ga = wrow(nx, 0, blk_gate(ex, nx.e));
+      ua = wrow(nx, 0, blk_up(ex, nx.e));
+    }
+    __syncthreads();
+    gu_finish(red[0], 2, it, row0 + 32, I, h);
+    // row group 3 (set b) -> the next item's row group 1
+    gu_partial<Q, NBL>(gb, ub, xf, red[1]);
+    if (more) {
+      gb = wrow(nx, 1, blk_gate(ex, nx.e));
+      ub = wrow(nx, 1, blk_up(ex, nx.e));
+    }
+    __syncthreads();
+    gu_finish(red[1], 3, it, row0 + 48, I, h);
+    if (!more) break;
+    item = next;
+    it = nx;
+  }
+}
+
+// --- down -------------------------------------------------------------------
+
+// One 16-row x 16-token down tile over all of K; two accumulators (operand
+// part or step parity) keep consecutive MFMAs independent.
+template <int Q, int NBL>
+__device__ inline floatx4_t dn_tile(const WRow<NBL>& wd, const _Float16* hrow, int kb0) {
+  floatx4_t acc0 = {}, acc1 = {};
+#pragma unroll
+  for (int b = 0; b < NBL; ++b) {
+    half8_t xf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) xf[kk] = *reinterpret_cast<const half8_t*>(hrow + 32 * (kb0 + b) + 8 * kk);
+    if constexpr (Q == 3) {
+      const WSplit sd = wsplit_block(wd.c[2 * b], wd.c[2 * b + 1], wd.hi[b], wd.dm[b]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_lo(sd, kk), xf[kk], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_hi(sd, kk), xf[kk], acc1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      const WStage sd = wstage_block<Q>(wd.c[2 * b], wd.c[2 * b + 1], wd.hi[b], wd.dm[b]);
+#pragma unroll
+      for (int kk = 0; kk < 4; kk += 2) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sd, kk), xf[kk], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sd, kk + 1), xf[kk + 1], acc1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  return acc0 + acc1;
+}
+
+__device__ inline void dn_store(const FfnArgs& a, int H, int slot, int row, float g, floatx4_t v) {
+  const size_t o = (size_t)slot * H + row;
+  if (a.o) {
+    *reinterpret_cast<float4*>(a.o + o) = make_float4(g * v[0], g * v[1], g * v[2], g * v[3]);
+  } else {
+    *reinterpret_cast<uint2*>(a.ob + o) =
+        make_uint2(f32_to_bf16_bits(g * v[0]) | (f32_to_bf16_bits(g * v[1]) << 16),
+                   f32_to_bf16_bits(g * v[2]) | (f32_to_bf16_bits(g * v[3]) << 16));
+  }
+}
+
+// NBL = I / 128 (lane groups c cover all of K). Each thread carries HC
+// 16-byte chunks of the item's 16 h rows.
+template <int Q, int NBL>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void bat_down(Experts ex, FfnArgs a) {
+  constexpr int kRow = kBMaxI + 8;  // LDS row of h (halves), padded against bank conflicts
+  constexpr int I_ = 128 * NBL;
+  constexpr int HC = 16 * (I_ / 8) / kBThreads;  // h chunks per thread (I / 256)
+  static_assert(HC >= 1, "I >= 256");
+  __shared__ BatMap bm;
+  __shared__ float gtab[kBTab];
+  __shared__ __attribute__((aligned(16))) _Float16 hs[2][16 * kRow];
+  const int H = ex.H, E_tot = ex.E_tot;
+  const int A = a.T * (a.k + ex.has_shared);
+  const bool use_tab = A <= kBTab;
+  batmap_init(bm, a, E_tot, use_tab, A, [&](int s) { gtab[s] = gate_of(a, s); });
+  const int NC = H / (16 * kDnRows * kBWaves);
+  const int n_items = bm.n * NC;
+  int item = bat_first();
+  if (item >= n_items) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane >> 4, r16 = lane & 15;
+  const int kb0 = NBL * c;
+  const uint4* h4 = static_cast<const uint4*>(a.h);
+  auto wrow = [&](const BatItem& it, int j) {
+    const int row = 16 * kDnRows * (kBWaves * it.chunk + wave) + 16 * j + r16;
+    return load_wrow<Q, NBL>(ex, blk_down(ex, it.e) + (size_t)row * (I_ / 32) + kb0);
+  };
+  // h chunk q = tid + 512 u of the item: token row q / (I / 8), chunk q % (I / 8)
+  auto hload = [&](const BatItem& it, uint4 (&hv)[HC]) {
+#pragma unroll
+    for (int u = 0; u < HC; ++u) {
+      const int q = tid + kBThreads * u, r = q / (I_ / 8), col = q % (I_ / 8);
+      const int m = 16 * it.tg + r;
+      hv[u] = m < it.M ? h4[(size_t)(it.slot0 + m) * (I_ / 8) + col] : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  BatItem it = bat_item(bm, E_tot, NC, item);
+  WRow<NBL> w0 = wrow(it, 0), w1 = wrow(it, 1);
+  uint4 hv[HC];
+  hload(it, hv);
+  int buf = 0;
+  for (;;) {
+#pragma unroll
+    for (int u = 0; u < HC; ++u) {
+      const int q = tid + kBThreads * u, r = q / (I_ / 8), col = q % (I_ / 8);
+      *reinterpret_cast<uint4*>(&hs[buf][r * kRow + 8 * col]) = hv[u];
+    }
+    __syncthreads();  // hs[buf] complete; hs[buf ^ 1] no longer read
+    const int next = item + gridDim.x;
+    const bool more = next < n_items;
+    BatItem nx = it;
+    if (more) {
+      nx = bat_item(bm, E_tot, NC, next);
+      hload(nx, hv);
+    }
+    const int m = 16 * it.tg + r16, slot = it.slot0 + m;
+    const bool live = m < it.M;
+    const float g = live ? (use_tab ? gtab[slot] : gate_of(a, slot)) : 0.f;
+    const _Float16* hrow = &hs[buf][r16 * kRow];
+    const int row0 = 16 * kDnRows * (kBWaves * it.chunk + wave) + 4 * c;
+    const floatx4_t o0 = dn_tile<Q, NBL>(w0, hrow, kb0);
+    if (more) w0 = wrow(nx, 0);
+    const floatx4_t o1 = dn_tile<Q, NBL>(w1, hrow, kb0);
+    if (more) w1 = wrow(nx, 1);
+    if (live) {
+      dn_store(a, H, slot, row0, g, o0);
+      dn_store(a, H, slot, row0 + 16, g, o1);
+    }
+    if (!more) break;
+    item = next;
+    it = nx;
+    buf ^= 1;
+  }
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int Q>
+hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
+  const long A = (long)a.T * (a.k + ex.has_shared);
+  // token groups: sum over touched experts of ceil(M / 16) <= A / 16 + touched, and <= A
+  const long touched = A < ex.E_tot ? A : ex.E_tot;
+  const long groups = A / 16 + touched < A ? A / 16 + touched : A;
+  const long cap = 2L * device_cus();
+  const long gu_items = groups * (ex.I / (16 * kGuRows));
+  const long dn_items = groups * (ex.H / (16 * kDnRows * kBWaves));
+  const dim3 ggu((unsigned)(gu_items < cap ? gu_items : cap));
+  const dim3 gdn((unsigned)(dn_items < cap ? dn_items : cap));
+  const bool xbf16 = a.xdtype != 0;
+  if (!xbf16) {
+    const hipError_t e = launch_x16(ex, a, s);
+    if (e != hipSuccess) return e;
+  }
+#define MOE_BAT_GU(NBL)                                                                              \
+  do {                                                                                             \
+    if (xbf16) MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, NBL, true>), ggu, dim3(kBThreads), 0, s, ex, a); \
+    else MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, NBL, false>), ggu, dim3(kBThreads), 0, s, ex, a);     \
+  } while (0)
+  switch (ex.H / 1024) {
+    case 1: MOE_BAT_GU(1); break;
+    case 2: MOE_BAT_GU(2); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_BAT_GU
+  switch (ex.I / 128) {
+    case 2: MOE_LAUNCH("bat_down", s, (bat_down<Q, 2>), gdn, dim3(kBThreads), 0, s, ex, a); break;
+    case 4: MOE_LAUNCH("bat_down", s, (bat_down<Q, 4>), gdn, dim3(kBThreads), 0, s, ex, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool batch_supported(int H, int I) {
+  return (H == 1024 || H == 2048) && (I == 256 || I == 512) && H % (16 * kDnRows * kBWaves) == 0 &&
+         I % (16 * kGuRows) == 0 && I <= kBMaxI;
+}
+
+hipError_t launch_batch(const Experts& ex, const FfnArgs& a, hipStream_t s) {
+  return ex.qtype == 3 ? launch_bat_q<3>(ex, a, s) : launch_bat_q<2>(ex, a, s);
+}
+
+}  // namespace moe

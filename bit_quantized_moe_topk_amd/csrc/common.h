@@ -130,6 +130,14 @@ hipError_t launch_ffn_fast(const Experts& ex, const FfnArgs& a, hipStream_t s);
 // MFMA tiles of fast mode (experts with more than gmax assignments); writes x16.
 bool mfma_supported(int H, int I);
 hipError_t launch_mfma(const Experts& ex, const FfnArgs& a, hipStream_t s);
+// fp16 copy of x in the MFMA K order (a.x16), the activation operand of the
+// matrix-core FFN kernels.
+hipError_t launch_x16(const Experts& ex, const FfnArgs& a, hipStream_t s);
+// Small batches (fewer than kGemvBatchLimit tokens): every touched expert on
+// the small-batch matrix-core kernels (batch.hip); writes x16, h and the
+// per-slot outputs.
+bool batch_supported(int H, int I);
+hipError_t launch_batch(const Experts& ex, const FfnArgs& a, hipStream_t s);
 // Writes the tiled copy of ex's planes (t_codes, t_dm, t_hi must be set).
 hipError_t launch_tile_weights(const Experts& ex, hipStream_t s);
 hipError_t launch_combine(const Experts& ex, const FfnArgs& a, hipStream_t s);

@@ -68,6 +68,16 @@ __device__ inline half2_t fp4x2_to_f16(uint32_t w, int j) {
   }
 }
 
+// The same times 8 (E2M1 0.5 becomes 4).
+__device__ inline half2_t fp4x2_to_f16_x8(uint32_t w, int j) {
+  switch (j) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, 3);
+  }
+}
+
 // Weights 8 kk .. 8 kk + 7 of the block (in the K order above) as an MFMA operand.
 template <int Q>
 __device__ inline half8_t wfrag(const WStage& w, int kk) {
@@ -98,6 +108,116 @@ __device__ inline half8_t wfrag(const WStage& w, int kk) {
     }
   }
   return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// --- Q3 as two operands -----------------------------------------------------
+// d (q_lo + 4 q_hi) + m = (d q_lo + m) + 4 d q_hi: the two low code bits take
+// the Q2 path above (one fp16 rounding of d q_lo + m), and the third bit
+// becomes an exact 0 or 4 d. Each part feeds its own MFMA over the same K
+// positions, which costs far fewer VALU instructions than assembling 3-bit
+// codes: the third bits only need spreading to the nibble positions the Q2
+// planes use (byte j of a word's e plane holds codes 4j, 4j + 2 in its two
+// nibbles, the o plane codes 4j + 1, 4j + 3); the FP4 conversion with scale 8
+// turns nibble 0b0001 (E2M1 0.5) into 4, and one packed multiply by d
+// follows. (The conversion's scale acts as a power of two, so d itself cannot
+// be passed as the scale.)
+struct WSplit {
+  uint32_t e0, o0, e1, o1;      // low bits of code words 0, 1 as E2M1 nibbles (Q2 planes)
+  uint32_t he0, ho0, he1, ho1;  // third bits at the same nibble positions
+  half2_t d2, m2;
+};
+
+// Bits 2i of x (i = 0..7) in the bytes sel picks, moved to bit 4i of the
+// result: a byte permute, then two shift-or-mask steps.
+__device__ inline uint32_t spread_even(uint32_t x, uint32_t sel) {
+  x = __builtin_amdgcn_perm(x, x, sel);
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  return (x | (x << 2)) & 0x33333333u;
+}
+
+__device__ inline WSplit wsplit_block(uint32_t c0, uint32_t c1, uint32_t hi, uint32_t dm) {
+  WSplit st;
+  st.e0 = c0 & 0x33333333u;
+  st.o0 = (c0 >> 2) & 0x33333333u;
+  st.e1 = c1 & 0x33333333u;
+  st.o1 = (c1 >> 2) & 0x33333333u;
+  const uint32_t ev = hi & 0x55555555u, od = (hi >> 1) & 0x55555555u;
+  st.he0 = spread_even(ev, 0x0C010C00u);  // third bits of codes 0 .. 15
+  st.ho0 = spread_even(od, 0x0C010C00u);
+  st.he1 = spread_even(ev, 0x0C030C02u);  // codes 16 .. 31
+  st.ho1 = spread_even(od, 0x0C030C02u);
+  st.d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
+  st.m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
+  return st;
+}
+
+// Weights 8 kk .. 8 kk + 7 (K order above): d q_lo + m ...
+__device__ inline half8_t wfrag_lo(const WSplit& w, int kk) {
+  WStage s;
+  s.w0 = w.e0;
+  s.w1 = w.o0;
+  s.w2 = w.e1;
+  s.w3 = w.o1;
+  s.d2 = w.d2;
+  s.m2 = w.m2;
+  return wfrag<2>(s, kk);
+}
+
+// ... and 4 d q_hi at the same positions.
+__device__ inline half8_t wfrag_hi(const WSplit& w, int kk) {
+  const uint32_t e = kk < 2 ? w.he0 : w.he1, od = kk < 2 ? w.ho0 : w.ho1;
+  uint32_t o[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = 2 * (kk & 1) + u;
+    o[2 * u] = __builtin_bit_cast(uint32_t, fp4x2_to_f16_x8(e, j) * w.d2);
+    o[2 * u + 1] = __builtin_bit_cast(uint32_t, fp4x2_to_f16_x8(od, j) * w.d2);
+  }
+  return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// --- raw weight rows -------------------------------------------------------
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// NBL consecutive quantisation blocks of one weight row as loaded from the
+// canonical planes: two code words, the third-bit word (Q3) and the fp16 pair
+// (d, m) per block.
+template <int NBL>
+struct WRow {
+  uint32_t c[2 * NBL], hi[NBL], dm[NBL];
+};
+
+template <int Q, int NBL>
+__device__ inline WRow<NBL> load_wrow(const Experts& ex, size_t blk) {
+  WRow<NBL> w;
+  if (NBL == 1) {
+    const uint2 c = *reinterpret_cast<const uint2*>(ex.codes + blk * 8);
+    w.c[0] = c.x;
+    w.c[1] = c.y;
+    w.dm[0] = *reinterpret_cast<const uint32_t*>(ex.dm + blk * 2);
+    if (Q == 3) w.hi[0] = *reinterpret_cast<const uint32_t*>(ex.hi + blk * 4);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBL; i += 2) {
+      const uint4 c = *reinterpret_cast<const uint4*>(ex.codes + (blk + i) * 8);
+      w.c[2 * i] = c.x;
+      w.c[2 * i + 1] = c.y;
+      w.c[2 * i + 2] = c.z;
+      w.c[2 * i + 3] = c.w;
+      const uint2 dm = *reinterpret_cast<const uint2*>(ex.dm + (blk + i) * 2);
+      w.dm[i] = dm.x;
+      w.dm[i + 1] = dm.y;
+      if (Q == 3) {
+        const uint2 h = *reinterpret_cast<const uint2*>(ex.hi + (blk + i) * 4);
+        w.hi[i] = h.x;
+        w.hi[i + 1] = h.y;
+      }
+    }
+  }
+  if (Q != 3)
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) w.hi[i] = 0u;
+  return w;
 }
 
 }  // namespace moe

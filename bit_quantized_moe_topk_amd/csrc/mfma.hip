@@ -515,12 +515,8 @@ __global__ __launch_bounds__(256) void tile_weights(Experts ex, long n) {
 
 template <int Q>
 hipError_t launch_q(const Experts& ex, const FfnArgs& a, int grid, hipStream_t s) {
-  const long n8 = (long)a.T * ex.H / 8;
-  const int xg = (int)(n8 / 256 + 1 < 2048 ? n8 / 256 + 1 : 2048);
-  if (a.xdtype == 0)
-    MOE_LAUNCH("x_to_f16", s, x_to_f16<true>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
-  else
-    MOE_LAUNCH("x_to_f16", s, x_to_f16<false>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
+  const hipError_t xe = launch_x16(ex, a, s);
+  if (xe != hipSuccess) return xe;
   const bool g8 = ex.I % tile_rows<false, 8>() == 0, d8 = ex.H % tile_rows<true, 8>() == 0;
 #define MOE_TILES(NAME, DOWN, NW)                                                              \
   do {                                                                                         \
@@ -540,6 +536,16 @@ hipError_t launch_q(const Experts& ex, const FfnArgs& a, int grid, hipStream_t s
 }
 
 }  // namespace
+
+hipError_t launch_x16(const Experts& ex, const FfnArgs& a, hipStream_t s) {
+  const long n8 = (long)a.T * ex.H / 8;
+  const int xg = (int)(n8 / 256 + 1 < 2048 ? n8 / 256 + 1 : 2048);
+  if (a.xdtype == 0)
+    MOE_LAUNCH("x_to_f16", s, x_to_f16<true>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
+  else
+    MOE_LAUNCH("x_to_f16", s, x_to_f16<false>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
+  return hipGetLastError();
+}
 
 hipError_t launch_tile_weights(const Experts& ex, hipStream_t s) {
   const long n = (long)ex.E_tot * 3 * (long)tiled_records(ex) * 64;

@@ -347,44 +347,6 @@ constexpr int kMmaSlices = 8;   // expert slices: workgroups per 16-row group
 constexpr int kMmaBatch = 4;    // experts per round
 constexpr int kMmaMaxH = 4096;
 
-template <int NBL>
-struct WRow {  // NBL consecutive blocks of one row
-  uint32_t c[2 * NBL], hi[NBL], dm[NBL];
-};
-
-template <int Q, int NBL>
-__device__ inline WRow<NBL> load_wrow(const Experts& ex, size_t blk) {
-  WRow<NBL> w;
-  if (NBL == 1) {
-    const uint2 c = *reinterpret_cast<const uint2*>(ex.codes + blk * 8);
-    w.c[0] = c.x;
-    w.c[1] = c.y;
-    w.dm[0] = *reinterpret_cast<const uint32_t*>(ex.dm + blk * 2);
-    if (Q == 3) w.hi[0] = *reinterpret_cast<const uint32_t*>(ex.hi + blk * 4);
-  } else {
-#pragma unroll
-    for (int i = 0; i < NBL; i += 2) {
-      const uint4 c = *reinterpret_cast<const uint4*>(ex.codes + (blk + i) * 8);
-      w.c[2 * i] = c.x;
-      w.c[2 * i + 1] = c.y;
-      w.c[2 * i + 2] = c.z;
-      w.c[2 * i + 3] = c.w;
-      const uint2 dm = *reinterpret_cast<const uint2*>(ex.dm + (blk + i) * 2);
-      w.dm[i] = dm.x;
-      w.dm[i + 1] = dm.y;
-      if (Q == 3) {
-        const uint2 h = *reinterpret_cast<const uint2*>(ex.hi + (blk + i) * 4);
-        w.hi[i] = h.x;
-        w.hi[i + 1] = h.y;
-      }
-    }
-  }
-  if (Q != 3)
-#pragma unroll
-    for (int i = 0; i < NBL; ++i) w.hi[i] = 0u;
-  return w;
-}
-
 // Down projection + combine. A workgroup owns R = 2 * RPI rows of H for every
 // active expert: wave w takes row group w % 2 and the experts q, q + 4, ...
 // with q = w / 2, and sums gate * o over them in registers; the four expert
@@ -457,7 +419,6 @@ __global__ __launch_bounds__(kWinThreads) void win_down(int T, Experts ex, const
   }
 }
 
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 // Gate/up role: rows 16 rgrp .. 16 rgrp + 15 of I for the active experts es,
 // es + 8, ... (es = role % 8). xs holds the window's activations (fp16, MFMA K

@@ -223,6 +223,31 @@ def test_layer_window_shared_workspace():
         ex.close()
 
 
+def test_layer_window_unzeroed_head_gives_nan():
+    """A workspace whose head was not zeroed (the never-written guard word is
+    set from the host) makes the one-kernel window write NaN rows at once,
+    without waiting on any counter; zeroing the head restores exact results."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfg = CONFIGS[1]
+    lay = make_layer(cfg, seed=43)
+    dev = upload(lay)
+    ex = experts_of(lay, dev)
+    nbytes = int(moe.lib().moe_layer_workspace_size(ex.handle, cfg.T, cfg.k, 0))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    y_ok = moe.layer(dev["logits"], dev["x"], ex, cfg.k, workspace=ws)[2]
+    ws[:4] = 7  # the guard word
+    log("[window guard] head not zero")
+    y_bad = moe.layer(dev["logits"], dev["x"], ex, cfg.k, workspace=ws)[2]
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(y_bad.float()).all())
+    ws.zero_()
+    y_again = moe.layer(dev["logits"], dev["x"], ex, cfg.k, workspace=ws)[2]
+    torch.cuda.synchronize()
+    assert torch.equal(y_ok, y_again)
+    ex.close()
+
+
 def run_ffn(lay, dev, idx_np, gates_np, mode, use_gpu_grouping=False, tiled=False):
     torch = torch_cuda()
     import bit_quantized_moe_topk_amd as moe
