@@ -23,44 +23,49 @@ constexpr int kSeg = 1024;  // assignment ids per wave segment
 
 __device__ inline int key_bits(int E) { return E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1)); }
 
-// The expert ids of up to 16 chunks of 64 consecutive assignment ids, loaded
+// The expert ids of up to KB chunks of 64 consecutive assignment ids, loaded
 // before any is used so that one memory round trip covers them all (ids past
-// f1 read as -1).
+// f1 read as -1). Large inputs take KB = 16; the one-workgroup kernels take
+// fewer, since their code runs once per launch from a cold instruction cache
+// and every unrolled chunk costs fetch time.
 constexpr int kBatch = 16;
-__device__ inline void load_chunks(const int32_t* __restrict__ idx, int base, int f1,
-                                   int (&e)[kBatch]) {
+constexpr int kBatchSmall = 2;  // group_fused: ids come from global memory
+template <int KB>
+__device__ inline void load_chunks(const int32_t* __restrict__ idx, int base, int f1, int (&e)[KB]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
+  for (int u = 0; u < KB; ++u) {
     const int f = base + 64 * u + lane;
     e[u] = f < f1 ? idx[f] : -1;
   }
 }
 
 // Count the experts of ids [f0, f1) into hist[e * stride] (LDS, zeroed by caller).
+template <int KB = kBatch>
 __device__ inline void wave_count(const int32_t* __restrict__ idx, int f0, int f1, int E,
                                   int* hist, int stride) {
-  for (int base = f0; base < f1; base += 64 * kBatch) {
-    int ev[kBatch];
-    load_chunks(idx, base, f1, ev);
+  for (int base = f0; base < f1; base += 64 * KB) {
+    int ev[KB];
+    load_chunks<KB>(idx, base, f1, ev);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
+    for (int u = 0; u < KB; ++u)
       if (ev[u] >= 0 && ev[u] < E) atomicAdd(&hist[ev[u] * stride], 1);
   }
 }
 
 // Stable scatter of ids [f0, f1) using the running counters cnt[e * stride].
+template <int KB = kBatch>
 __device__ inline void wave_scatter(const int32_t* __restrict__ idx, int f0, int f1, int E,
                                     int* cnt, int stride, int32_t* __restrict__ perm,
                                     int32_t* __restrict__ slot_of) {
   const int lane = threadIdx.x & 63;
   const int nbits = key_bits(E);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int b0 = f0; b0 < f1; b0 += 64 * kBatch) {
-    int ev[kBatch];
-    load_chunks(idx, b0, f1, ev);
+  for (int b0 = f0; b0 < f1; b0 += 64 * KB) {
+    int ev[KB];
+    load_chunks<KB>(idx, b0, f1, ev);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int u = 0; u < KB; ++u) {
       const int f = b0 + 64 * u + lane;
       const int e = ev[u];
       const bool ok = e >= 0 && e < E;
@@ -105,9 +110,10 @@ __device__ inline void write_shared(int T, int k, int has_shared, int32_t* perm,
   }
 }
 
-// All three steps in one workgroup: one wave per segment (nseg <= 16).
+// All three steps in one workgroup: one wave per segment of seg_len ids
+// (nseg <= 16 segments).
 __global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ idx, int T, int k,
-                                                    int E, int has_shared, int nseg,
+                                                    int E, int has_shared, int nseg, int seg_len,
                                                     int32_t* counts, int32_t* offsets,
                                                     int32_t* perm, int32_t* slot_of) {
   extern __shared__ int lds[];  // [E * nseg] bases, then [16] wave totals
@@ -117,43 +123,45 @@ __global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ 
   for (int i = threadIdx.x; i < E * nseg; i += blockDim.x) hist[i] = 0;
   __syncthreads();
   const int seg = threadIdx.x >> 6;
-  const int f0 = min(AR, seg * kSeg), f1 = min(AR, f0 + kSeg);
-  if (seg < nseg) wave_count(idx, f0, f1, E, hist + seg, nseg);
+  const int f0 = min(AR, seg * seg_len), f1 = min(AR, f0 + seg_len);
+  if (seg < nseg) wave_count<kBatchSmall>(idx, f0, f1, E, hist + seg, nseg);
   __syncthreads();
   block_exclusive_scan(hist, E * nseg, tmp);
   write_offsets(hist, nseg, E, T, k, has_shared, counts, offsets);
   __syncthreads();  // the bases are read above before the scatter advances them
-  if (seg < nseg) wave_scatter(idx, f0, f1, E, hist + seg, nseg, perm, slot_of);
+  if (seg < nseg) wave_scatter<kBatchSmall>(idx, f0, f1, E, hist + seg, nseg, perm, slot_of);
   write_shared(T, k, has_shared, perm, slot_of);
 }
 
 // Top-k and grouping in one workgroup for small batches (a decode verify
-// window): every wave selects experts for its tokens into global memory and
-// into LDS, then the workgroup groups the LDS copy as group_fused does.
+// window, a few of them batched): every wave selects experts for its tokens
+// into global memory and into LDS, then the workgroup groups the LDS copy as
+// group_fused does, one wave per segment of seg_len ids.
 template <int PER_LANE>
 __global__ __launch_bounds__(1024) void route_group_small(const float* __restrict__ logits, int T,
-                                                          int E, int k, int has_shared,
-                                                          int32_t* idx, float* gates,
+                                                          int E, int k, int has_shared, int nseg,
+                                                          int seg_len, int32_t* idx, float* gates,
                                                           int32_t* counts, int32_t* offsets,
                                                           int32_t* perm, int32_t* slot_of) {
-  extern __shared__ int lds[];  // [T*k] expert ids, [E] bases, [16] wave totals
+  extern __shared__ int lds[];  // [T*k] expert ids, [E * nseg] bases, [16] wave totals
   __shared__ TopkScratch sc[16];
   int* lidx = lds;
   int* hist = lds + T * k;
-  int* wsum = hist + E;
+  int* wsum = hist + E * nseg;
   const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int t = wv; t < T; t += nw)
     topk_token<PER_LANE>(logits + (size_t)t * E, E, k, idx + (size_t)t * k, gates + (size_t)t * k,
                          &sc[wv], lidx + t * k);
-  for (int i = threadIdx.x; i < E; i += blockDim.x) hist[i] = 0;
+  for (int i = threadIdx.x; i < E * nseg; i += blockDim.x) hist[i] = 0;
   __syncthreads();
   const int AR = T * k;
-  if (wv == 0) wave_count(lidx, 0, AR, E, hist, 1);
+  const int f0 = min(AR, wv * seg_len), f1 = min(AR, f0 + seg_len);
+  if (wv < nseg) wave_count<1>(lidx, f0, f1, E, hist + wv, nseg);
   __syncthreads();
-  block_exclusive_scan(hist, E, wsum);
-  write_offsets(hist, 1, E, T, k, has_shared, counts, offsets);
-  __syncthreads();
-  if (wv == 0) wave_scatter(lidx, 0, AR, E, hist, 1, perm, slot_of);
+  block_exclusive_scan(hist, E * nseg, wsum);
+  write_offsets(hist, nseg, E, T, k, has_shared, counts, offsets);
+  __syncthreads();  // the bases are read above before the scatter advances them
+  if (wv < nseg) wave_scatter<1>(lidx, f0, f1, E, hist + wv, nseg, perm, slot_of);
   write_shared(T, k, has_shared, perm, slot_of);
 }
 
@@ -273,9 +281,25 @@ inline bool use_fused(int T, int k, int E) {
   return n <= 16 && (size_t)E * n + 16 <= 16384;
 }
 
+// One token per wave (at most 16): past that, the top-k kernel (a wave per
+// token over many workgroups) and group_fused take less time than waves
+// selecting several tokens in turn.
 inline bool small_route_group(int T, int k, int E) {
-  return T <= 64 && T * k <= kSeg &&
+  return T <= 16 && T * k <= kSeg &&
          (size_t)(T * k + E + 16) * sizeof(int) + 16 * sizeof(TopkScratch) <= 65536;
+}
+
+// Segments for a one-workgroup grouping of A ids: as many as there are waves
+// (at most max_seg), of a multiple of 64 ids each, while E ints of bases per
+// segment fit in lds_ints; returns the segment count and sets seg_len.
+inline int small_segments(int A, int E, int max_seg, size_t lds_ints, int& seg_len) {
+  int n = (A + 63) / 64;
+  if (n > max_seg) n = max_seg;
+  while (n > 1 && (size_t)E * n > lds_ints) --n;
+  if (n < 1) n = 1;
+  seg_len = ((A + n - 1) / n + 63) / 64 * 64;
+  if (seg_len < 64) seg_len = 64;
+  return (A + seg_len - 1) / seg_len;
 }
 
 template <int P>
@@ -283,9 +307,12 @@ hipError_t launch_rg(const float* logits, int T, int E, int k, int has_shared, i
                      float* gates, int32_t* counts, int32_t* offsets, int32_t* perm,
                      int32_t* slot_of, hipStream_t s) {
   const int waves = T < 16 ? T : 16;
-  const size_t lds = (size_t)(T * k + E + 16) * sizeof(int);
+  const size_t budget = (65536 - 16 * sizeof(TopkScratch)) / sizeof(int) - (size_t)T * k - 16;
+  int seg_len = 64;
+  const int nseg = small_segments(T * k, E, waves, budget, seg_len);
+  const size_t lds = ((size_t)T * k + (size_t)E * nseg + 16) * sizeof(int);
   MOE_LAUNCH("route_group", s, route_group_small<P>, dim3(1), dim3(64 * waves), lds, s, logits, T,
-             E, k, has_shared, idx, gates, counts, offsets, perm, slot_of);
+             E, k, has_shared, nseg, seg_len, idx, gates, counts, offsets, perm, slot_of);
   return hipGetLastError();
 }
 
@@ -301,10 +328,12 @@ hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared,
                         hipStream_t s) {
   const int nseg = nseg_of(T, k);
   if (use_fused(T, k, E)) {
-    const size_t lds = ((size_t)E * nseg + 16) * sizeof(int);
-    const int threads = 64 * (nseg > 0 ? nseg : 1);
-    MOE_LAUNCH("group_fused", s, group_fused, dim3(1), dim3(threads), lds, s, idx, T, k, E, has_shared, nseg,
-                       counts, offsets, perm, slot_of);
+    int seg_len = kSeg;
+    const int nf = small_segments(T * k, E, 16, 16384 - 16, seg_len);
+    const size_t lds = ((size_t)E * nf + 16) * sizeof(int);
+    const int threads = 64 * (nf > 0 ? nf : 1);
+    MOE_LAUNCH("group_fused", s, group_fused, dim3(1), dim3(threads), lds, s, idx, T, k, E, has_shared, nf,
+               seg_len, counts, offsets, perm, slot_of);
     return hipGetLastError();
   }
   int* hist = static_cast<int*>(scratch);

@@ -83,15 +83,22 @@ struct alignas(16) TopkScratch {
 // slot r. When more than 64 codes reach tau (heavy ties), or k > 64, rounds
 // take over: each finds the largest remaining code with a DPP max and the
 // lowest index holding it, and retires it.
+//
+// topk_load fetches a row (lane + 64 i for slot i, all loads back to back,
+// clamped address, no branch, so their latencies overlap); topk_select works
+// on a fetched row, so a caller can have several rows in flight at once.
 template <int PER_LANE>
-__device__ inline void topk_token(const float* __restrict__ l, int E, int k, int32_t* idx_t,
-                                  float* g_t, TopkScratch* sc, int32_t* lds_idx = nullptr) {
+__device__ inline void topk_load(const float* __restrict__ l, int E, float (&raw)[PER_LANE]) {
   const int lane = threadIdx.x & 63;
-  // All loads issue back to back (clamped address, no branch), so their
-  // latencies overlap; padding slots get code 0 afterwards.
-  float raw[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) raw[i] = l[min(lane + 64 * i, E - 1)];
+}
+
+template <int PER_LANE>
+__device__ inline void topk_select(const float (&raw)[PER_LANE], int E, int k, int32_t* idx_t,
+                                   float* g_t, TopkScratch* sc, int32_t* lds_idx = nullptr) {
+  const int lane = threadIdx.x & 63;
+  // padding slots get code 0
   uint32_t key[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) key[i] = lane + 64 * i < E ? orderable(raw[i]) : 0u;
@@ -192,6 +199,14 @@ __device__ inline void topk_token(const float* __restrict__ l, int E, int k, int
   for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
   if (lane < k) g_t[lane] = ej / sum;
   for (int j = 64 + lane; j < k; j += 64) g_t[j] = expf(g_t[j] - top) / sum;
+}
+
+template <int PER_LANE>
+__device__ inline void topk_token(const float* __restrict__ l, int E, int k, int32_t* idx_t,
+                                  float* g_t, TopkScratch* sc, int32_t* lds_idx = nullptr) {
+  float raw[PER_LANE];
+  topk_load<PER_LANE>(l, E, raw);
+  topk_select<PER_LANE>(raw, E, k, idx_t, g_t, sc, lds_idx);
 }
 
 }  // namespace moe

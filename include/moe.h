@@ -125,7 +125,7 @@ int moe_group(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t has_s
 
 /* Top-k routing followed by the grouping, in one call: the same results as
  * moe_route_topk then moe_group (idx, gates, counts, offsets, perm, slot_of as
- * defined there). Small batches (T <= 64 and T*k <= 1024, the decode verify
+ * defined there). Small batches (T <= 16 and T*k <= 1024, e.g. decode verify
  * windows) run as one workgroup in a single launch; larger ones run the two
  * steps' kernels back to back. ws: at least moe_group_workspace_size(T, k, E)
  * bytes. T == 0 writes the empty grouping (counts, offsets) only. */

@@ -336,6 +336,29 @@ def test_prefill_8k_sampled_rows(layer):
         assert err.max() <= tol
 
 
+@pytest.mark.parametrize("T,E,k", [(16, 512, 64), (12, 2048, 40), (9, 64, 7)])
+def test_route_group_segments_bit_exact(T, E, k):
+    """The one-workgroup route + group with several grouping segments (up to
+    one per wave, fewer where the per-segment bases would overflow LDS), and
+    the two-launch form past 16 tokens, equal the oracle."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    rng = np.random.default_rng(T * 1000 + k)
+    for TT in (T, 4 * T):
+        lg = rng.standard_normal((TT, E)).astype(np.float32)
+        lg[:, :3] += 2.0  # a few hot experts: long runs inside segments
+        log(f"[route_group segments] T={TT} E={E} k={k}")
+        idx, gates, g = moe.route_group(torch.from_numpy(lg).cuda(), k, True)
+        torch.cuda.synchronize()
+        idx_o, _ = oracle.route(lg, k)
+        assert np.array_equal(idx.cpu().numpy(), idx_o)
+        ref = oracle.group(idx_o, E, True)
+        got = (g.counts.cpu().numpy(), g.offsets.cpu().numpy(), g.perm.cpu().numpy(),
+               g.slot_of.cpu().numpy())
+        for name, a, b in zip(("counts", "offsets", "perm", "slot_of"), got, ref):
+            assert np.array_equal(a, b), name
+
+
 def test_group_size_invariance():
     """A token evaluated alone and inside its verify window agree within tolerance."""
     lay, dev = layer_for(1)
