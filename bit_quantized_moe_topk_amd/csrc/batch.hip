@@ -15,7 +15,8 @@
 //               v_mfma_f32_16x16x32_f16 while the four row groups' weights
 //               stream through two register sets, dequantised in registers
 //               (deq16.h); the next item's first weights are requested while
-//               the last row groups compute. Each row group's eight partial
+//               the last row groups compute (Q3 operands: deq16.h, "Q3
+//               through the FP4 conversion"). Each row group's eight partial
 //               tiles are summed in LDS in wave order, then SwiGLU; h is
 //               stored as fp16 in the MFMA K order.
 //   bat_down  : chunk = 256 rows of H (wave w: two groups of 16 rows over all
@@ -133,9 +134,8 @@ __device__ inline void load_xop(const FfnArgs& a, int H, int t, bool live, int k
 }
 
 // One row group: the wave's partial gate and up tiles into red. Four
-// accumulators (gate and up, each split in two by operand part or step
-// parity) keep consecutive MFMAs independent, so none waits on the previous
-// one's result.
+// accumulators (gate and up, each split in two by step parity) keep
+// consecutive MFMAs independent, so none waits on the previous one's result.
 template <int Q, int NBL>
 __device__ inline void gu_partial(const WRow<NBL>& wg, const WRow<NBL>& wu, const half8_t (&xf)[NBL][4],
                                   float (&red)[kBWaves][2][16][17]) {
@@ -147,16 +147,16 @@ __device__ inline void gu_partial(const WRow<NBL>& wg, const WRow<NBL>& wu, cons
       // gate, then up: the split operands' planes of one row at a time
       const WSplit sg = wsplit_block(wg.c[2 * b], wg.c[2 * b + 1], wg.hi[b], wg.dm[b]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        ag0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_lo(sg, kk), xf[b][kk], ag0, 0, 0, 0);
-        ag1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_hi(sg, kk), xf[b][kk], ag1, 0, 0, 0);
+      for (int kk = 0; kk < 4; kk += 2) {
+        ag0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(sg, kk), xf[b][kk], ag0, 0, 0, 0);
+        ag1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(sg, kk + 1), xf[b][kk + 1], ag1, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       const WSplit su = wsplit_block(wu.c[2 * b], wu.c[2 * b + 1], wu.hi[b], wu.dm[b]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        au0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_lo(su, kk), xf[b][kk], au0, 0, 0, 0);
-        au1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_hi(su, kk), xf[b][kk], au1, 0, 0, 0);
+      for (int kk = 0; kk < 4; kk += 2) {
+        au0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(su, kk), xf[b][kk], au0, 0, 0, 0);
+        au1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(su, kk + 1), xf[b][kk + 1], au1, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     } else {
@@ -297,8 +297,8 @@ void bat_gateup(Experts ex, FfnArgs a) {
 
 // --- down -------------------------------------------------------------------
 
-// One 16-row x 16-token down tile over all of K; two accumulators (operand
-// part or step parity) keep consecutive MFMAs independent.
+// One 16-row x 16-token down tile over all of K; two accumulators (step
+// parity) keep consecutive MFMAs independent.
 template <int Q, int NBL>
 __device__ inline floatx4_t dn_tile(const WRow<NBL>& wd, const _Float16* hrow, int kb0) {
   floatx4_t acc0 = {}, acc1 = {};
@@ -310,9 +310,9 @@ __device__ inline floatx4_t dn_tile(const WRow<NBL>& wd, const _Float16* hrow, i
     if constexpr (Q == 3) {
       const WSplit sd = wsplit_block(wd.c[2 * b], wd.c[2 * b + 1], wd.hi[b], wd.dm[b]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_lo(sd, kk), xf[kk], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_hi(sd, kk), xf[kk], acc1, 0, 0, 0);
+      for (int kk = 0; kk < 4; kk += 2) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(sd, kk), xf[kk], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(sd, kk + 1), xf[kk + 1], acc1, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     } else {

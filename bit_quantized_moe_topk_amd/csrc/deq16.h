@@ -110,17 +110,14 @@ __device__ inline half8_t wfrag(const WStage& w, int kk) {
   return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-// --- Q3 as two operands -----------------------------------------------------
-// d (q_lo + 4 q_hi) + m = (d q_lo + m) + 4 d q_hi: the two low code bits take
-// the Q2 path above (one fp16 rounding of d q_lo + m), and the third bit
-// becomes an exact 0 or 4 d. Each part feeds its own MFMA over the same K
-// positions, which costs far fewer VALU instructions than assembling 3-bit
-// codes: the third bits only need spreading to the nibble positions the Q2
-// planes use (byte j of a word's e plane holds codes 4j, 4j + 2 in its two
-// nibbles, the o plane codes 4j + 1, 4j + 3); the FP4 conversion with scale 8
-// turns nibble 0b0001 (E2M1 0.5) into 4, and one packed multiply by d
-// follows. (The conversion's scale acts as a power of two, so d itself cannot
-// be passed as the scale.)
+// --- Q3 through the FP4 conversion ----------------------------------------
+// A 3-bit code is q = q_lo + 4 q_hi. The two low bits take the Q2 path above
+// (an FP4 conversion with scale 2 gives q_lo exactly); the third bits, spread
+// to the same nibble positions (byte j of a word's e plane holds codes 4j,
+// 4j + 2 in its two nibbles, the o plane codes 4j + 1, 4j + 3), go through the
+// FP4 conversion with scale 8, which turns nibble 0b0001 (E2M1 0.5) into an
+// exact 4. One exact fp16 add gives q, then one fused d*q + m rounds once, as
+// in wfrag<3>, for far fewer VALU instructions than assembling 3-bit fields.
 struct WSplit {
   uint32_t e0, o0, e1, o1;      // low bits of code words 0, 1 as E2M1 nibbles (Q2 planes)
   uint32_t he0, ho0, he1, ho1;  // third bits at the same nibble positions
@@ -151,27 +148,18 @@ __device__ inline WSplit wsplit_block(uint32_t c0, uint32_t c1, uint32_t hi, uin
   return st;
 }
 
-// Weights 8 kk .. 8 kk + 7 (K order above): d q_lo + m ...
-__device__ inline half8_t wfrag_lo(const WSplit& w, int kk) {
-  WStage s;
-  s.w0 = w.e0;
-  s.w1 = w.o0;
-  s.w2 = w.e1;
-  s.w3 = w.o1;
-  s.d2 = w.d2;
-  s.m2 = w.m2;
-  return wfrag<2>(s, kk);
-}
-
-// ... and 4 d q_hi at the same positions.
-__device__ inline half8_t wfrag_hi(const WSplit& w, int kk) {
-  const uint32_t e = kk < 2 ? w.he0 : w.he1, od = kk < 2 ? w.ho0 : w.ho1;
+// Weights 8 kk .. 8 kk + 7 of the block in the K order above.
+__device__ inline half8_t wfrag_split(const WSplit& w, int kk) {
+  const uint32_t e = kk < 2 ? w.e0 : w.e1, od = kk < 2 ? w.o0 : w.o1;
+  const uint32_t he = kk < 2 ? w.he0 : w.he1, ho = kk < 2 ? w.ho0 : w.ho1;
   uint32_t o[4];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int j = 2 * (kk & 1) + u;
-    o[2 * u] = __builtin_bit_cast(uint32_t, fp4x2_to_f16_x8(e, j) * w.d2);
-    o[2 * u + 1] = __builtin_bit_cast(uint32_t, fp4x2_to_f16_x8(od, j) * w.d2);
+    const half2_t qa = fp4x2_to_f16(e, j) + fp4x2_to_f16_x8(he, j);
+    const half2_t qb = fp4x2_to_f16(od, j) + fp4x2_to_f16_x8(ho, j);
+    o[2 * u] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qa, w.d2, w.m2));
+    o[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qb, w.d2, w.m2));
   }
   return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
