@@ -216,7 +216,7 @@ def kernel_profile(insts, L, stream, steps: int, chunk: int = 32) -> dict:
     return moe.profile_end()
 
 
-def run_decode(cfg, args):
+def run_decode(cfg, args, workload: str = "decode"):
     import torch
     import bit_quantized_moe_topk_amd as moe
     L = moe.lib()
@@ -301,7 +301,7 @@ def run_decode(cfg, args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(k_bytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if k_ms else None,
-            "traffic": measured_traffic(kname, "decode"),
+            "traffic": measured_traffic(kname, workload),
             "launches": n_k,
             "avg_us": round(1e3 * k_ms / max(n_k, 1), 2),
             "bytes_per_launch": round(k_bytes / max(n_k, 1)),
@@ -498,7 +498,7 @@ def main() -> int:
         bargs = copy.copy(args)
         bargs.rotation = 16
         bargs.cpu_layers = 0
-        b, _, binsts = run_decode(CONFIGS[4], bargs)
+        b, _, binsts = run_decode(CONFIGS[4], bargs, workload="batched_decode")
         for it in binsts:
             it.ex.close()
         del binsts

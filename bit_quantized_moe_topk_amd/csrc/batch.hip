@@ -118,7 +118,7 @@ __device__ inline void load_xop(const FfnArgs& a, int H, int t, bool live, int k
       for (int kk = 0; kk < 4; ++kk) xf[b][kk] = half8_t{};
     return;
   }
-  const uint16_t* row = (XBF16 ? static_cast<const uint16_t*>(a.x) : a.x16) + (size_t)t * H + 32 * kb0;
+  const uint16_t* row = (XBF16 ? static_cast<const uint16_t*>(a.x) : a.x16) + (uint32_t)(t * H + 32 * kb0);
   const uint4* src = reinterpret_cast<const uint4*>(row);
 #pragma unroll
   for (int b = 0; b < NBL; ++b)
@@ -133,54 +133,46 @@ __device__ inline void load_xop(const FfnArgs& a, int H, int t, bool live, int k
     }
 }
 
-// One row group: the wave's partial gate and up tiles into red. Four
-// accumulators (gate and up, each split in two by step parity) keep
-// consecutive MFMAs independent, so none waits on the previous one's result.
+// One row group: the wave's partial gate and up tiles into red (gate, then
+// up: one row's operand planes live at a time).
 template <int Q, int NBL>
 __device__ inline void gu_partial(const WRow<NBL>& wg, const WRow<NBL>& wu, const half8_t (&xf)[NBL][4],
                                   float (&red)[kBWaves][2][16][17]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane >> 4, r16 = lane & 15;
-  floatx4_t ag0 = {}, ag1 = {}, au0 = {}, au1 = {};
+  floatx4_t ag = {}, au = {};
 #pragma unroll
   for (int b = 0; b < NBL; ++b) {
     if constexpr (Q == 3) {
-      // gate, then up: the split operands' planes of one row at a time
-      const WSplit sg = wsplit_block(wg.c[2 * b], wg.c[2 * b + 1], wg.hi[b], wg.dm[b]);
+      // one code word (16 weights) of one row at a time
 #pragma unroll
-      for (int kk = 0; kk < 4; kk += 2) {
-        ag0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(sg, kk), xf[b][kk], ag0, 0, 0, 0);
-        ag1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(sg, kk + 1), xf[b][kk + 1], ag1, 0, 0, 0);
+      for (int w = 0; w < 2; ++w) {
+        const WSplitWord sg = wsplit_word(wg.c[2 * b + w], wg.hi[b], wg.dm[b], w);
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_word(sg, 0), xf[b][2 * w], ag, 0, 0, 0);
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_word(sg, 1), xf[b][2 * w + 1], ag, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const WSplitWord su = wsplit_word(wu.c[2 * b + w], wu.hi[b], wu.dm[b], w);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_word(su, 0), xf[b][2 * w], au, 0, 0, 0);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_word(su, 1), xf[b][2 * w + 1], au, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      const WSplit su = wsplit_block(wu.c[2 * b], wu.c[2 * b + 1], wu.hi[b], wu.dm[b]);
-#pragma unroll
-      for (int kk = 0; kk < 4; kk += 2) {
-        au0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(su, kk), xf[b][kk], au0, 0, 0, 0);
-        au1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(su, kk + 1), xf[b][kk + 1], au1, 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
     } else {
       const WStage sg = wstage_block<Q>(wg.c[2 * b], wg.c[2 * b + 1], wg.hi[b], wg.dm[b]);
 #pragma unroll
-      for (int kk = 0; kk < 4; kk += 2) {
-        ag0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sg, kk), xf[b][kk], ag0, 0, 0, 0);
-        ag1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sg, kk + 1), xf[b][kk + 1], ag1, 0, 0, 0);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sg, kk), xf[b][kk], ag, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       const WStage su = wstage_block<Q>(wu.c[2 * b], wu.c[2 * b + 1], wu.hi[b], wu.dm[b]);
 #pragma unroll
-      for (int kk = 0; kk < 4; kk += 2) {
-        au0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(su, kk), xf[b][kk], au0, 0, 0, 0);
-        au1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(su, kk + 1), xf[b][kk + 1], au1, 0, 0, 0);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(su, kk), xf[b][kk], au, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   // ag[v]: row 4 c + v of the group, token r16
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    red[wave][0][4 * c + v][r16] = ag0[v] + ag1[v];
-    red[wave][1][4 * c + v][r16] = au0[v] + au1[v];
+    red[wave][0][4 * c + v][r16] = ag[v];
+    red[wave][1][4 * c + v][r16] = au[v];
   }
   // the caller reloads this row group's registers next: keep those loads
   // after the arithmetic that still reads them
@@ -226,15 +218,16 @@ void bat_gateup(Experts ex, FfnArgs a) {
     tok[s] = (unsigned)t < (unsigned)a.T ? t : 0;
   });
   const int NC = I / (16 * R);
-  const int n_items = bm.n * NC;
+  const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
   int item = bat_first();
   if (item >= n_items) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int kb0 = wave * (H / 256) + NBL * (lane >> 4);  // the lane's first block of its rows
   uint16_t* h = static_cast<uint16_t*>(a.h);
+  const uint32_t lane_blk = (uint32_t)(r16 * (H / 32) + kb0);  // block of the lane's row and K slice
   auto wrow = [&](const BatItem& it, int j, size_t mat0) {
-    return load_wrow<Q, NBL>(ex, mat0 + (size_t)(16 * (R * it.chunk + j) + r16) * (H / 32) + kb0);
+    return load_wrow_at<Q, NBL>(ex, mat0 + (size_t)(16 * (R * it.chunk + j)) * (H / 32), lane_blk);
   };
 
   BatItem it = bat_item(bm, E_tot, NC, item);
@@ -356,16 +349,18 @@ void bat_down(Experts ex, FfnArgs a) {
   const bool use_tab = A <= kBTab;
   batmap_init(bm, a, E_tot, use_tab, A, [&](int s) { gtab[s] = gate_of(a, s); });
   const int NC = H / (16 * kDnRows * kBWaves);
-  const int n_items = bm.n * NC;
+  const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
   int item = bat_first();
   if (item >= n_items) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane >> 4, r16 = lane & 15;
   const int kb0 = NBL * c;
   const uint4* h4 = static_cast<const uint4*>(a.h);
+  // the lane's row inside the item's chunk, and its first block
+  const uint32_t lane_blk = (uint32_t)((16 * kDnRows * wave + r16) * (I_ / 32) + kb0);
   auto wrow = [&](const BatItem& it, int j) {
-    const int row = 16 * kDnRows * (kBWaves * it.chunk + wave) + 16 * j + r16;
-    return load_wrow<Q, NBL>(ex, blk_down(ex, it.e) + (size_t)row * (I_ / 32) + kb0);
+    const size_t ubase = blk_down(ex, it.e) + (size_t)(16 * kDnRows * kBWaves * it.chunk + 16 * j) * (I_ / 32);
+    return load_wrow_at<Q, NBL>(ex, ubase, lane_blk);
   };
   // h chunk q = tid + 512 u of the item: token row q / (I / 8), chunk q % (I / 8)
   auto hload = [&](const BatItem& it, uint4 (&hv)[HC]) {

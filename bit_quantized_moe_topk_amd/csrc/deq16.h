@@ -148,6 +148,39 @@ __device__ inline WSplit wsplit_block(uint32_t c0, uint32_t c1, uint32_t hi, uin
   return st;
 }
 
+// The planes of one code word w (0: codes 0 .. 15, 1: codes 16 .. 31), for
+// callers short of registers: weights 8 kk .. 8 kk + 7 for kk = 2 w, 2 w + 1.
+struct WSplitWord {
+  uint32_t e, o, he, ho;
+  half2_t d2, m2;
+};
+
+__device__ inline WSplitWord wsplit_word(uint32_t c, uint32_t hi, uint32_t dm, int w) {
+  WSplitWord st;
+  st.e = c & 0x33333333u;
+  st.o = (c >> 2) & 0x33333333u;
+  const uint32_t sel = w ? 0x0C030C02u : 0x0C010C00u;
+  st.he = spread_even(hi & 0x55555555u, sel);
+  st.ho = spread_even((hi >> 1) & 0x55555555u, sel);
+  st.d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
+  st.m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
+  return st;
+}
+
+// Weights 8 kk .. 8 kk + 7 of the block, kk = 2 w + half.
+__device__ inline half8_t wfrag_word(const WSplitWord& w, int half) {
+  uint32_t o[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = 2 * half + u;
+    const half2_t qa = fp4x2_to_f16(w.e, j) + fp4x2_to_f16_x8(w.he, j);
+    const half2_t qb = fp4x2_to_f16(w.o, j) + fp4x2_to_f16_x8(w.ho, j);
+    o[2 * u] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qa, w.d2, w.m2));
+    o[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qb, w.d2, w.m2));
+  }
+  return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
 // Weights 8 kk .. 8 kk + 7 of the block in the K order above.
 __device__ inline half8_t wfrag_split(const WSplit& w, int kk) {
   const uint32_t e = kk < 2 ? w.e0 : w.e1, od = kk < 2 ? w.o0 : w.o1;
@@ -174,6 +207,45 @@ template <int NBL>
 struct WRow {
   uint32_t c[2 * NBL], hi[NBL], dm[NBL];
 };
+
+// The same with the block index split into a wave-uniform part (ubase, kept
+// in scalar registers) and a 32-bit per-lane part, so that no 64-bit per-lane
+// address stays live between loads.
+template <int Q, int NBL>
+__device__ inline WRow<NBL> load_wrow_at(const Experts& ex, size_t ubase, uint32_t lane_blk) {
+  const uint8_t* cb = ex.codes + ubase * 8;
+  const uint16_t* db = ex.dm + ubase * 2;
+  const uint8_t* hb = Q == 3 ? ex.hi + ubase * 4 : nullptr;
+  WRow<NBL> w;
+  if (NBL == 1) {
+    const uint2 c = *reinterpret_cast<const uint2*>(cb + 8 * lane_blk);
+    w.c[0] = c.x;
+    w.c[1] = c.y;
+    w.dm[0] = *reinterpret_cast<const uint32_t*>(db + 2 * lane_blk);
+    if (Q == 3) w.hi[0] = *reinterpret_cast<const uint32_t*>(hb + 4 * lane_blk);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBL; i += 2) {
+      const uint4 c = *reinterpret_cast<const uint4*>(cb + 8 * (lane_blk + i));
+      w.c[2 * i] = c.x;
+      w.c[2 * i + 1] = c.y;
+      w.c[2 * i + 2] = c.z;
+      w.c[2 * i + 3] = c.w;
+      const uint2 dm = *reinterpret_cast<const uint2*>(db + 2 * (lane_blk + i));
+      w.dm[i] = dm.x;
+      w.dm[i + 1] = dm.y;
+      if (Q == 3) {
+        const uint2 h = *reinterpret_cast<const uint2*>(hb + 4 * (lane_blk + i));
+        w.hi[i] = h.x;
+        w.hi[i + 1] = h.y;
+      }
+    }
+  }
+  if (Q != 3)
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) w.hi[i] = 0u;
+  return w;
+}
 
 template <int Q, int NBL>
 __device__ inline WRow<NBL> load_wrow(const Experts& ex, size_t blk) {
