@@ -14,13 +14,9 @@
 // block of a row; a wave issues all its block loads before computing, then
 // reduces its partial sums across the row's lanes in one batched transpose.
 //
-// Prefill shape (more assignments per expert): tiles of 64 assignments x 64
-// output rows on v_mfma_f32_32x32x16_f16. Each K step dequantises a weight tile
-// to fp16 (w = d*q + m, one rounding) into LDS and gathers the tile's activation
-// rows through the grouping permutation into LDS as fp16. Gate and up share the
-// activation fragment and SwiGLU runs in the epilogue. The pages' prompt path
-// likewise multiplies quantised experts without first expanding them to FP16
-// ("Faster prompts").
+// Used for experts with 1..4 assignments in batches under 256 tokens whose
+// shapes the small-batch matrix-core kernels (batch.hip) do not cover; the
+// other experts of such a batch run on the matrix-core tiles (mfma.hip).
 //
 // Combine: the down kernels store gate * o per assignment slot (fp32 for few
 // tokens, bf16 for many) and the combine kernel sums each token's slots in a

@@ -210,7 +210,14 @@ size_t moe_ffn_q_workspace_size(const moe_experts *ex, int32_t T, int32_t k, int
  *         it, or all four NULL to have it computed inside `ws`.
  * y     : [T][H]; dtype xdtype in MOE_FAST, float32 in MOE_CHECK_F32.
  * ws    : device scratch of at least moe_ffn_q_workspace_size(ex, T, k, mode).
- * T == 0 is valid and launches nothing. */
+ * T == 0 is valid and launches nothing.
+ *
+ * Execution (fast mode; results agree within the FFN tolerance whichever form
+ * runs): below 256 tokens with H 1024 or 2048 and I 256 or 512, every touched
+ * expert runs on the small-batch matrix-core kernels (work items of expert,
+ * output rows and 16 of its tokens); other batches below 256 tokens run
+ * experts with 1..4 assignments on the GEMV kernels and the rest on the
+ * matrix-core tiles; from 256 tokens on every expert runs on the tiles. */
 int moe_ffn_q(const void *x, int32_t xdtype, int32_t T, const moe_experts *ex,
               const int32_t *idx, const float *gates, int32_t k, const int32_t *counts,
               const int32_t *offsets, const int32_t *perm, const int32_t *slot_of, void *y,
