@@ -17,48 +17,92 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ inline float4 load4(const uint16_t* p) {
-  const uint2 v = *reinterpret_cast<const uint2*>(p);
-  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+// 16 bytes of o: 4 fp32 or 8 bf16 values, as fp32.
+template <typename OT>
+struct Piece {
+  static constexpr int N = 16 / sizeof(OT);
+  float v[N];
+};
+__device__ inline Piece<float> unpack(uint4 u, const float*) {
+  Piece<float> p;
+  p.v[0] = __uint_as_float(u.x);
+  p.v[1] = __uint_as_float(u.y);
+  p.v[2] = __uint_as_float(u.z);
+  p.v[3] = __uint_as_float(u.w);
+  return p;
+}
+__device__ inline Piece<uint16_t> unpack(uint4 u, const uint16_t*) {
+  Piece<uint16_t> p;
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p.v[2 * i] = __uint_as_float(w[i] << 16);
+    p.v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  return p;
 }
 
-// One thread per 4 consecutive output elements of a token row.
+constexpr int kCombineBatch = 8;  // slot rows of one token in flight at once
+
+// One thread per 16 bytes of o (4 fp32 or 8 bf16 outputs) of a token row. The
+// token's slot indices are read first (one scalar load each), then up to
+// kCombineBatch slot rows are requested before any is added; the sum runs in
+// slot order j = 0 .. n-1, so the result does not depend on the batching.
 template <typename OT, bool OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ o,
                                                       const int32_t* __restrict__ slot_of, int T,
                                                       int k, int has_shared, int H, void* y) {
-  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  constexpr int V = Piece<OT>::N;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * V;
   if (c >= H) return;
   const int n = k + has_shared;
   const int A = T * n;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < n; ++j) {
-      const int a = j < k ? t * k + j : T * k + t;
-      const int sl = slot_of[a];
-      if ((unsigned)sl >= (unsigned)A) continue;  // only for an invalid grouping
-      const float4 v = load4(o + (size_t)sl * H + c);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < n; j0 += kCombineBatch) {
+      uint4 u[kCombineBatch];
+      bool ok[kCombineBatch];
+#pragma unroll
+      for (int b = 0; b < kCombineBatch; ++b) {
+        const int j = j0 + b;
+        int sl = -1;
+        if (j < n) sl = slot_of[j < k ? t * k + j : T * k + t];
+        ok[b] = (unsigned)sl < (unsigned)A;  // false past n, or for an invalid grouping
+        u[b] = ok[b] ? *reinterpret_cast<const uint4*>(o + (size_t)sl * H + c) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < kCombineBatch; ++b) {
+        if (!ok[b]) continue;
+        const Piece<OT> p = unpack(u[b], o);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] += p.v[i];
+      }
     }
     if (OUT_F32) {
-      *reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * H + c) = acc;
+      float* dst = static_cast<float*>(y) + (size_t)t * H + c;
+#pragma unroll
+      for (int i = 0; i < V; i += 4)
+        *reinterpret_cast<float4*>(dst + i) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
     } else {
-      uint2 p;
-      p.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
-      p.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)t * H + c) = p;
+      uint32_t w[V / 2];
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i)
+        w[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i]) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+      uint16_t* dst = static_cast<uint16_t*>(y) + (size_t)t * H + c;
+      if constexpr (V == 8)
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      else
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
     }
   }
 }
 
 template <typename OT>
 hipError_t launch_t(const Experts& ex, const FfnArgs& a, const OT* o, hipStream_t s) {
-  dim3 grid((ex.H / 4 + 255) / 256, a.T < 65535 ? a.T : 65535);
+  constexpr int V = Piece<OT>::N;
+  dim3 grid((ex.H / V + 255) / 256, a.T < 65535 ? a.T : 65535);
   if (a.out_f32)
     MOE_LAUNCH("combine", s, (combine_kernel<OT, true>), grid, dim3(256), 0, s, o, a.slot_of, a.T,
                a.k, ex.has_shared, ex.H, a.y);
