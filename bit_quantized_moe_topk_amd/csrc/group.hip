@@ -70,6 +70,7 @@ __device__ inline void wave_scatter(const int32_t* __restrict__ idx, int f0, int
       const int e = ev[u];
       const bool ok = e >= 0 && e < E;
       uint64_t mask = __ballot(ok);
+      if (mask == 0) continue;  // a chunk past the range: nothing to rank
       for (int b = 0; b < nbits; ++b) {
         const bool bit = ok && ((e >> b) & 1);
         const uint64_t bal = __ballot(bit);
@@ -188,28 +189,35 @@ __global__ __launch_bounds__(256) void group_count(const int32_t* __restrict__ i
 }
 
 // Step 2: one workgroup turns hist into exclusive bases in (expert, segment)
-// order. Thread e sums expert e's segment counts (a segment's counts are
-// adjacent, so the workgroup's loads coalesce), a block scan over the expert
-// totals in LDS gives each expert's first slot, and thread e rewrites its
-// column as running bases. Eight loads in flight per thread.
+// order. Two threads per expert take the first and second half of its
+// segments (a segment's counts are adjacent, so the workgroup's loads
+// coalesce), 16 loads in flight each; a block scan over the expert totals in
+// LDS gives each expert's first slot, and each thread rewrites its half of
+// the column as running bases.
 __global__ __launch_bounds__(1024) void group_scan(int T, int k, int E, int has_shared, int nseg,
                                                    int* hist, int32_t* counts, int32_t* offsets) {
   __shared__ int tot[MOE_MAX_E_DEV + 1];
+  __shared__ int part[2][MOE_MAX_E_DEV];  // per expert: the halves' sums
   __shared__ int wsum[16];
   const int tid = threadIdx.x, NT = blockDim.x;
-  constexpr int U = 8;
-  for (int e = tid; e < E; e += NT) {
-    int sum = 0, s = 0;
-    for (; s + U <= nseg; s += U) {
+  constexpr int U = 16;
+  const int mid = nseg / 2;
+  // half-column sums
+  for (int i = tid; i < 2 * E; i += NT) {
+    const int e = i % E, hf = i / E;
+    const int s0 = hf ? mid : 0, s1 = hf ? nseg : mid;
+    int sum = 0;
+    for (int s = s0; s < s1; s += U) {  // every round a full batch of loads (the tail predicated)
       int v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = hist[(size_t)(s + u) * E + e];
+      for (int u = 0; u < U; ++u) v[u] = s + u < s1 ? hist[(size_t)(s + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < U; ++u) sum += v[u];
     }
-    for (; s < nseg; ++s) sum += hist[(size_t)s * E + e];
-    tot[e] = sum;
+    part[hf][e] = sum;
   }
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) tot[e] = part[0][e] + part[1][e];
   __syncthreads();
   block_exclusive_scan(tot, E, wsum);
   const int AR = T * k;
@@ -222,22 +230,20 @@ __global__ __launch_bounds__(1024) void group_scan(int T, int k, int E, int has_
     if (e < E) counts[e] = (e + 1 < E ? tot[e + 1] : AR) - tot[e];
     else counts[E] = has_shared ? T : 0;
   }
-  for (int e = tid; e < E; e += NT) {
-    int run = tot[e], s = 0;
-    for (; s + U <= nseg; s += U) {
+  // running bases: the second half starts after the first half's sum
+  for (int i = tid; i < 2 * E; i += NT) {
+    const int e = i % E, hf = i / E;
+    const int s0 = hf ? mid : 0, s1 = hf ? nseg : mid;
+    int run = tot[e] + (hf ? part[0][e] : 0);
+    for (int s = s0; s < s1; s += U) {
       int v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = hist[(size_t)(s + u) * E + e];
+      for (int u = 0; u < U; ++u) v[u] = s + u < s1 ? hist[(size_t)(s + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        hist[(size_t)(s + u) * E + e] = run;
+        if (s + u < s1) hist[(size_t)(s + u) * E + e] = run;
         run += v[u];
       }
-    }
-    for (; s < nseg; ++s) {
-      const int v = hist[(size_t)s * E + e];
-      hist[(size_t)s * E + e] = run;
-      run += v;
     }
   }
 }
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(256) void group_scatter(const int32_t* __restrict__
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  wave_count(idx, g0, g1, E, cnt, 1);
+  wave_count<kSeg / 256>(idx, g0, g1, E, cnt, 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) {
     int run = hist[(size_t)seg * E + e];
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(256) void group_scatter(const int32_t* __restrict__
     }
   }
   __syncthreads();
-  wave_scatter(idx, g0, g1, E, cnt, 1, perm, slot_of);
+  wave_scatter<kSeg / 256>(idx, g0, g1, E, cnt, 1, perm, slot_of);
 }
 
 inline int nseg_of(int T, int k) { return (T * k + kSeg - 1) / kSeg; }
