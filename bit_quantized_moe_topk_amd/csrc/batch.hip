@@ -347,7 +347,8 @@ void bat_down(Experts ex, FfnArgs a) {
   const int H = ex.H, E_tot = ex.E_tot;
   const int A = a.T * (a.k + ex.has_shared);
   const bool use_tab = A <= kBTab;
-  batmap_init(bm, a, E_tot, use_tab, A, [&](int s) { gtab[s] = gate_of(a, s); });
+  // the gate table is filled after the first item's loads are in flight (below)
+  batmap_init(bm, a, E_tot, false, A, [](int) {});
   const int NC = H / (16 * kDnRows * kBWaves);
   const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
   int item = bat_first();
@@ -376,6 +377,11 @@ void bat_down(Experts ex, FfnArgs a) {
   WRow<NBL> w0 = wrow(it, 0), w1 = wrow(it, 1);
   uint4 hv[HC];
   hload(it, hv);
+  // routing gate of every slot (perm, then gates: two dependent loads), read
+  // while the first item's loads are in flight; the loop's first barrier
+  // publishes it
+  if (use_tab)
+    for (int s = tid; s < A; s += kBThreads) gtab[s] = gate_of(a, s);
   int buf = 0;
   for (;;) {
 #pragma unroll
