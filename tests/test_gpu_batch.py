@@ -5,8 +5,9 @@ the C ABI; two runs must agree bit for bit.
 Cases on the small-batch matrix-core kernels cover several 16-token groups
 per expert and more than 64 tokens of one expert (h staged in chunks), both
 quantisations, H = 1024 / I = 256, float32 activations, no shared expert, a
-single token and a ragged batch; two shapes outside those kernels run the
-GEMV kernels (experts with 1..4 assignments) beside the matrix-core tiles.
+single token, a ragged batch and more slots than the LDS tables hold; two
+shapes outside those kernels run the GEMV kernels (experts with 1..4
+assignments) beside the matrix-core tiles.
 """
 import numpy as np
 import pytest
@@ -26,6 +27,8 @@ CASES = [
     ("Q2 H=1024 I=256 T=37 f32", dict(T=37, H=1024, I=256, E=32, k=4, qtype=2, xdtype="f32"), None),
     ("Q3 H=1024 I=512 T=9 no shared", dict(T=9, H=1024, E=48, k=6, shared=0), None),
     ("Q2 T=1", dict(T=1, qtype=2), None),
+    # more than 4,096 assignment slots: token ids and gates read without the LDS tables
+    ("Q3 T=100 k=48 E=64: 4,900 slots", dict(T=100, E=64, k=48), None),
     # outside the small-batch kernels' shapes: GEMV for 1..4 assignments, tiles for the rest
     ("Q2 H=4096 I=256 T=20: GEMV + tiles", dict(T=20, H=4096, I=256, E=32, k=4, qtype=2), 3),
     ("Q3 H=512 I=128 T=40: GEMV + tiles", dict(T=40, H=512, I=128, E=24, k=3), None),
