@@ -8,18 +8,18 @@
 // rows, group of 16 of the expert's tokens), so that every CU streams weights
 // and no expert with many tokens leaves a long tail:
 //
-//   bat_gateup: chunk = 4 groups of 16 rows of I, for gate and up. The 8
+//   bat_gateup: chunk = 2 groups of 16 rows of I, for gate and up. The 8
 //               waves split K (wave w takes blocks w H/256 ...; lane group
 //               c = lane / 16 takes NBL consecutive blocks of its row). The
 //               lane's 16 tokens stay in registers as the fp16 operand of
-//               v_mfma_f32_16x16x32_f16 while the four row groups' weights
+//               v_mfma_f32_16x16x32_f16 while the row groups' weights
 //               stream through two register sets, dequantised in registers
 //               (deq16.h); the next item's first weights are requested while
 //               the last row groups compute (Q3 operands: deq16.h, "Q3
 //               through the FP4 conversion"). Each row group's eight partial
 //               tiles are summed in LDS in wave order, then SwiGLU; h is
 //               stored as fp16 in the MFMA K order.
-//   bat_down  : chunk = 256 rows of H (wave w: two groups of 16 rows over all
+//   bat_down  : chunk = 128 rows of H (wave w: one group of 16 rows over all
 //               of K = I). The item's 16 h rows come into LDS (double-buffered
 //               across items, the next item's rows requested early); outputs
 //               are scaled by the routing gate and stored per assignment slot
@@ -40,8 +40,8 @@ namespace {
 
 constexpr int kBThreads = 512;
 constexpr int kBWaves = kBThreads / 64;
-constexpr int kGuRows = 4;     // 16-row groups of I per gate/up item
-constexpr int kDnRows = 2;     // 16-row groups of H per wave in a down item
+constexpr int kGuRows = 2;     // 16-row groups of I per gate/up item (2 or 4)
+constexpr int kDnRows = 1;     // 16-row groups of H per wave in a down item (1 or 2)
 constexpr int kBMaxI = 512;
 constexpr int kBTab = 4096;    // slots whose token id / gate fit the LDS table
 
@@ -207,6 +207,7 @@ template <int Q, int NBL, bool XBF16>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void bat_gateup(Experts ex, FfnArgs a) {
   constexpr int R = kGuRows;
+  static_assert(R == 2 || R == 4, "the row-group pipeline takes 2 or 4 groups per item");
   __shared__ BatMap bm;
   __shared__ int tok[kBTab];
   __shared__ float red[2][kBWaves][2][16][17];  // two buffers: wave, gate/up, row, token
@@ -254,34 +255,36 @@ void bat_gateup(Experts ex, FfnArgs a) {
     BatItem nx = it;
     if (more) nx = bat_item(bm, E_tot, NC, next);
     const int row0 = 16 * R * it.chunk;
-    // row group 0 (set a), then its weights make way for row group 2
-    gu_partial<Q, NBL>(ga, ua, xf, red[0]);
-    ga = wrow(it, 2, blk_gate(ex, it.e));
-    ua = wrow(it, 2, blk_up(ex, it.e));
-    __syncthreads();
-    gu_finish(red[0], 0, it, row0, I, h);
-    // row group 1 (set b) -> row group 3
-    gu_partial<Q, NBL>(gb, ub, xf, red[1]);
-    gb = wrow(it, 3, blk_gate(ex, it.e));
-    ub = wrow(it, 3, blk_up(ex, it.e));
-    __syncthreads();
-    gu_finish(red[1], 1, it, row0 + 16, I, h);
-    // row group 2 (set a) -> the next item's row group 0
+    if constexpr (R == 4) {
+      // row group 0 (set a), then its weights make way for row group 2
+      gu_partial<Q, NBL>(ga, ua, xf, red[0]);
+      ga = wrow(it, 2, blk_gate(ex, it.e));
+      ua = wrow(it, 2, blk_up(ex, it.e));
+      __syncthreads();
+      gu_finish(red[0], 0, it, row0, I, h);
+      // row group 1 (set b) -> row group 3
+      gu_partial<Q, NBL>(gb, ub, xf, red[1]);
+      gb = wrow(it, 3, blk_gate(ex, it.e));
+      ub = wrow(it, 3, blk_up(ex, it.e));
+      __syncthreads();
+      gu_finish(red[1], 1, it, row0 + 16, I, h);
+    }
+    // row group R - 2 (set a) -> the next item's row group 0
     gu_partial<Q, NBL>(ga, ua, xf, red[0]);
     if (more) {
       ga = wrow(nx, 0, blk_gate(ex, nx.e));
       ua = wrow(nx, 0, blk_up(ex, nx.e));
     }
     __syncthreads();
-    gu_finish(red[0], 2, it, row0 + 32, I, h);
-    // row group 3 (set b) -> the next item's row group 1
+    gu_finish(red[0], R - 2, it, row0 + 16 * (R - 2), I, h);
+    // row group R - 1 (set b) -> the next item's row group 1
     gu_partial<Q, NBL>(gb, ub, xf, red[1]);
     if (more) {
       gb = wrow(nx, 1, blk_gate(ex, nx.e));
       ub = wrow(nx, 1, blk_up(ex, nx.e));
     }
     __syncthreads();
-    gu_finish(red[1], 3, it, row0 + 48, I, h);
+    gu_finish(red[1], R - 1, it, row0 + 16 * (R - 1), I, h);
     if (!more) break;
     item = next;
     it = nx;
@@ -337,6 +340,7 @@ __device__ inline void dn_store(const FfnArgs& a, int H, int slot, int row, floa
 template <int Q, int NBL>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void bat_down(Experts ex, FfnArgs a) {
+  static_assert(kDnRows == 1 || kDnRows == 2, "one or two row groups per wave");
   constexpr int kRow = kBMaxI + 8;  // LDS row of h (halves), padded against bank conflicts
   constexpr int I_ = 128 * NBL;
   constexpr int HC = 16 * (I_ / 8) / kBThreads;  // h chunks per thread (I / 256)
@@ -374,7 +378,8 @@ void bat_down(Experts ex, FfnArgs a) {
   };
 
   BatItem it = bat_item(bm, E_tot, NC, item);
-  WRow<NBL> w0 = wrow(it, 0), w1 = wrow(it, 1);
+  WRow<NBL> w0 = wrow(it, 0), w1;
+  if constexpr (kDnRows == 2) w1 = wrow(it, 1);
   uint4 hv[HC];
   hload(it, hv);
   // routing gate of every slot (perm, then gates: two dependent loads), read
@@ -404,12 +409,12 @@ void bat_down(Experts ex, FfnArgs a) {
     const int row0 = 16 * kDnRows * (kBWaves * it.chunk + wave) + 4 * c;
     const floatx4_t o0 = dn_tile<Q, NBL>(w0, hrow, kb0);
     if (more) w0 = wrow(nx, 0);
-    const floatx4_t o1 = dn_tile<Q, NBL>(w1, hrow, kb0);
-    if (more) w1 = wrow(nx, 1);
-    if (live) {
-      dn_store(a, H, slot, row0, g, o0);
-      dn_store(a, H, slot, row0 + 16, g, o1);
+    if constexpr (kDnRows == 2) {
+      const floatx4_t o1 = dn_tile<Q, NBL>(w1, hrow, kb0);
+      if (more) w1 = wrow(nx, 1);
+      if (live) dn_store(a, H, slot, row0 + 16, g, o1);
     }
+    if (live) dn_store(a, H, slot, row0, g, o0);
     if (!more) break;
     item = next;
     it = nx;
