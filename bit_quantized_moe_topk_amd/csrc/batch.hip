@@ -25,11 +25,11 @@
 //               are scaled by the routing gate and stored per assignment slot
 //               for the combine.
 //
-// Both grids are persistent (two workgroups per CU): every workgroup builds a
-// map of the grouping in LDS (token groups per expert, slot offsets, and the
-// token id or gate of every slot) and takes items dealt round-robin; an
-// expert's consecutive items, which read the same weights, go to workgroups
-// of one XCD.
+// Both grids are persistent (gate/up: two workgroups per CU, down: three):
+// every workgroup builds a map of the grouping in LDS (token groups per
+// expert, slot offsets, and the token id or gate of every slot) and takes
+// items dealt round-robin; an expert's consecutive items, which read the same
+// weights, go to workgroups of one XCD.
 #include "common.h"
 #include "deq16.h"
 #include "gemv.h"
@@ -43,15 +43,19 @@ constexpr int kBWaves = kBThreads / 64;
 constexpr int kGuRows = 2;     // 16-row groups of I per gate/up item (2 or 4)
 constexpr int kDnRows = 1;     // 16-row groups of H per wave in a down item (1 or 2)
 constexpr int kBMaxI = 512;
-constexpr int kBTab = 4096;    // slots whose token id / gate fit the LDS table
+constexpr int kBTab = 4096;    // slots whose token id fits the gate/up LDS table
+constexpr int kBTabDn = 2048;  // slots whose gate fits the down LDS table
 
-// Grouping map of one launch in LDS.
+// Grouping map of one launch in LDS. Its two per-expert arrays live in the
+// launch's dynamic LDS (bat_map_bytes), so a layer with few experts leaves
+// room for more workgroups per CU:
+//   base[E_tot + 1]: exclusive prefix over experts of ceil(M / 16), then the total;
+//   off[E_tot + 1] : slot offsets (offsets[0..E_tot]).
 struct BatMap {
-  int base[MOE_MAX_E_DEV + 2];  // exclusive prefix over experts of ceil(M / 16)
-  int off[MOE_MAX_E_DEV + 2];   // slot offsets (offsets[0..E_tot])
   int wsum[16];
-  int n;                        // token groups in all
+  int n;  // token groups in all
 };
+inline size_t bat_map_bytes(int E_tot) { return 2 * sizeof(int) * (size_t)(E_tot + 2); }
 
 // One item: expert e, output-row chunk, token group tg (tokens 16 tg ..).
 struct BatItem {
@@ -61,19 +65,19 @@ struct BatItem {
 // Fills the map, and tab[s] = fill(s) for every slot when the table is used;
 // all threads of the block call it.
 template <typename Fill>
-__device__ inline void batmap_init(BatMap& bm, const FfnArgs& a, int E_tot, bool use_tab, int A,
-                                   Fill&& fill) {
+__device__ inline void batmap_init(BatMap& bm, int* base, int* off, const FfnArgs& a, int E_tot,
+                                   bool use_tab, int A, Fill&& fill) {
   for (int e = threadIdx.x; e <= E_tot; e += blockDim.x) {
     const int o = a.offsets[e];
-    bm.off[e] = o;
-    if (e < E_tot) bm.base[e] = (a.counts[e] + 15) >> 4;
+    off[e] = o;
+    if (e < E_tot) base[e] = (a.counts[e] + 15) >> 4;
   }
   if (use_tab)
     for (int s = threadIdx.x; s < A; s += blockDim.x) fill(s);
   __syncthreads();
-  const int n = block_exclusive_scan(bm.base, E_tot, bm.wsum);
+  const int n = block_exclusive_scan(base, E_tot, bm.wsum);
   if (threadIdx.x == 0) {
-    bm.base[E_tot] = n;
+    base[E_tot] = n;
     bm.n = n;
   }
   __syncthreads();
@@ -81,16 +85,16 @@ __device__ inline void batmap_init(BatMap& bm, const FfnArgs& a, int E_tot, bool
 
 // Items of expert e are NC * G_e consecutive numbers from NC * base[e], in
 // (chunk, token group) order.
-__device__ inline BatItem bat_item(const BatMap& bm, int E_tot, int NC, int item) {
-  const int e = workmap_find(bm.base, E_tot, item / NC);
-  const int g0 = bm.base[e], G = bm.base[e + 1] - g0;
+__device__ inline BatItem bat_item(const int* base, const int* off, int E_tot, int NC, int item) {
+  const int e = workmap_find(base, E_tot, item / NC);
+  const int g0 = base[e], G = base[e + 1] - g0;
   const int local = item - NC * g0;
   BatItem it;
   it.e = __builtin_amdgcn_readfirstlane(e);
   it.chunk = __builtin_amdgcn_readfirstlane(local / G);
   it.tg = __builtin_amdgcn_readfirstlane(local % G);
-  it.slot0 = __builtin_amdgcn_readfirstlane(bm.off[e]);
-  it.M = __builtin_amdgcn_readfirstlane(bm.off[e + 1] - bm.off[e]);
+  it.slot0 = __builtin_amdgcn_readfirstlane(off[e]);
+  it.M = __builtin_amdgcn_readfirstlane(off[e + 1] - off[e]);
   return it;
 }
 
@@ -209,12 +213,15 @@ void bat_gateup(Experts ex, FfnArgs a) {
   constexpr int R = kGuRows;
   static_assert(R == 2 || R == 4, "the row-group pipeline takes 2 or 4 groups per item");
   __shared__ BatMap bm;
+  extern __shared__ int bat_dyn[];  // base, off (bat_map_bytes)
   __shared__ int tok[kBTab];
   __shared__ float red[2][kBWaves][2][16][17];  // two buffers: wave, gate/up, row, token
   const int H = ex.H, I = ex.I, E_tot = ex.E_tot;
   const int A = a.T * (a.k + ex.has_shared);
   const bool use_tab = A <= kBTab;
-  batmap_init(bm, a, E_tot, use_tab, A, [&](int s) {
+  int* base = bat_dyn;
+  int* off = bat_dyn + E_tot + 2;
+  batmap_init(bm, base, off, a, E_tot, use_tab, A, [&](int s) {
     const int t = token_of(a.perm[s], a.T, a.k);
     tok[s] = (unsigned)t < (unsigned)a.T ? t : 0;
   });
@@ -231,7 +238,7 @@ void bat_gateup(Experts ex, FfnArgs a) {
     return load_wrow_at<Q, NBL>(ex, mat0 + (size_t)(16 * (R * it.chunk + j)) * (H / 32), lane_blk);
   };
 
-  BatItem it = bat_item(bm, E_tot, NC, item);
+  BatItem it = bat_item(base, off, E_tot, NC, item);
   WRow<NBL> ga = wrow(it, 0, blk_gate(ex, it.e)), ua = wrow(it, 0, blk_up(ex, it.e));
   WRow<NBL> gb = wrow(it, 1, blk_gate(ex, it.e)), ub = wrow(it, 1, blk_up(ex, it.e));
   for (;;) {
@@ -253,7 +260,7 @@ void bat_gateup(Experts ex, FfnArgs a) {
     const int next = item + gridDim.x;
     const bool more = next < n_items;
     BatItem nx = it;
-    if (more) nx = bat_item(bm, E_tot, NC, next);
+    if (more) nx = bat_item(base, off, E_tot, NC, next);
     const int row0 = 16 * R * it.chunk;
     if constexpr (R == 4) {
       // row group 0 (set a), then its weights make way for row group 2
@@ -338,7 +345,7 @@ __device__ inline void dn_store(const FfnArgs& a, int H, int slot, int row, floa
 // NBL = I / 128 (lane groups c cover all of K). Each thread carries HC
 // 16-byte chunks of the item's 16 h rows.
 template <int Q, int NBL>
-__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(6)))
 void bat_down(Experts ex, FfnArgs a) {
   static_assert(kDnRows == 1 || kDnRows == 2, "one or two row groups per wave");
   constexpr int kRow = kBMaxI + 8;  // LDS row of h (halves), padded against bank conflicts
@@ -346,13 +353,16 @@ void bat_down(Experts ex, FfnArgs a) {
   constexpr int HC = 16 * (I_ / 8) / kBThreads;  // h chunks per thread (I / 256)
   static_assert(HC >= 1, "I >= 256");
   __shared__ BatMap bm;
-  __shared__ float gtab[kBTab];
+  extern __shared__ int bat_dyn[];  // base, off (bat_map_bytes)
+  __shared__ float gtab[kBTabDn];
   __shared__ __attribute__((aligned(16))) _Float16 hs[2][16 * kRow];
   const int H = ex.H, E_tot = ex.E_tot;
   const int A = a.T * (a.k + ex.has_shared);
-  const bool use_tab = A <= kBTab;
+  const bool use_tab = A <= kBTabDn;
+  int* base = bat_dyn;
+  int* off = bat_dyn + E_tot + 2;
   // the gate table is filled after the first item's loads are in flight (below)
-  batmap_init(bm, a, E_tot, false, A, [](int) {});
+  batmap_init(bm, base, off, a, E_tot, false, A, [](int) {});
   const int NC = H / (16 * kDnRows * kBWaves);
   const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
   int item = bat_first();
@@ -377,7 +387,7 @@ void bat_down(Experts ex, FfnArgs a) {
     }
   };
 
-  BatItem it = bat_item(bm, E_tot, NC, item);
+  BatItem it = bat_item(base, off, E_tot, NC, item);
   WRow<NBL> w0 = wrow(it, 0), w1;
   if constexpr (kDnRows == 2) w1 = wrow(it, 1);
   uint4 hv[HC];
@@ -399,7 +409,7 @@ void bat_down(Experts ex, FfnArgs a) {
     const bool more = next < n_items;
     BatItem nx = it;
     if (more) {
-      nx = bat_item(bm, E_tot, NC, next);
+      nx = bat_item(base, off, E_tot, NC, next);
       hload(nx, hv);
     }
     const int m = 16 * it.tg + r16, slot = it.slot0 + m;
@@ -441,11 +451,14 @@ hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   // token groups: sum over touched experts of ceil(M / 16) <= A / 16 + touched, and <= A
   const long touched = A < ex.E_tot ? A : ex.E_tot;
   const long groups = A / 16 + touched < A ? A / 16 + touched : A;
-  const long cap = 2L * device_cus();
+  // resident workgroups per CU: gate/up 2 (registers), down 3 (LDS, with the
+  // map of a layer of up to ~1,000 experts)
+  const long cap_gu = 2L * device_cus(), cap_dn = 3L * device_cus();
   const long gu_items = groups * (ex.I / (16 * kGuRows));
   const long dn_items = groups * (ex.H / (16 * kDnRows * kBWaves));
-  const dim3 ggu((unsigned)(gu_items < cap ? gu_items : cap));
-  const dim3 gdn((unsigned)(dn_items < cap ? dn_items : cap));
+  const dim3 ggu((unsigned)(gu_items < cap_gu ? gu_items : cap_gu));
+  const dim3 gdn((unsigned)(dn_items < cap_dn ? dn_items : cap_dn));
+  const size_t map = bat_map_bytes(ex.E_tot);
   const bool xbf16 = a.xdtype != 0;
   if (!xbf16) {
     const hipError_t e = launch_x16(ex, a, s);
@@ -453,8 +466,8 @@ hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   }
 #define MOE_BAT_GU(NBL)                                                                              \
   do {                                                                                             \
-    if (xbf16) MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, NBL, true>), ggu, dim3(kBThreads), 0, s, ex, a); \
-    else MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, NBL, false>), ggu, dim3(kBThreads), 0, s, ex, a);     \
+    if (xbf16) MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, NBL, true>), ggu, dim3(kBThreads), map, s, ex, a); \
+    else MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, NBL, false>), ggu, dim3(kBThreads), map, s, ex, a);     \
   } while (0)
   switch (ex.H / 1024) {
     case 1: MOE_BAT_GU(1); break;
@@ -463,8 +476,8 @@ hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   }
 #undef MOE_BAT_GU
   switch (ex.I / 128) {
-    case 2: MOE_LAUNCH("bat_down", s, (bat_down<Q, 2>), gdn, dim3(kBThreads), 0, s, ex, a); break;
-    case 4: MOE_LAUNCH("bat_down", s, (bat_down<Q, 4>), gdn, dim3(kBThreads), 0, s, ex, a); break;
+    case 2: MOE_LAUNCH("bat_down", s, (bat_down<Q, 2>), gdn, dim3(kBThreads), map, s, ex, a); break;
+    case 4: MOE_LAUNCH("bat_down", s, (bat_down<Q, 4>), gdn, dim3(kBThreads), map, s, ex, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

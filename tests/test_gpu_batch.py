@@ -27,6 +27,7 @@ CASES = [
     ("Q2 H=1024 I=256 T=37 f32", dict(T=37, H=1024, I=256, E=32, k=4, qtype=2, xdtype="f32"), None),
     ("Q3 H=1024 I=512 T=9 no shared", dict(T=9, H=1024, E=48, k=6, shared=0), None),
     ("Q2 T=1", dict(T=1, qtype=2), None),
+    ("Q2 E=2048 k=8 T=48: the largest expert map", dict(T=48, E=2048, k=8, qtype=2), None),
     # more than 4,096 assignment slots: token ids and gates read without the LDS tables
     ("Q3 T=100 k=48 E=64: 4,900 slots", dict(T=100, E=64, k=48), None),
     # outside the small-batch kernels' shapes: GEMV for 1..4 assignments, tiles for the rest
