@@ -16,7 +16,7 @@
 //               stream through two register sets, dequantised in registers
 //               (deq16.h); the next item's first weights are requested while
 //               the last row groups compute (Q3 operands: deq16.h, "Q3
-//               through the FP4 conversion"). Each row group's eight partial
+//               through the FP8 conversion"). Each row group's eight partial
 //               tiles are summed in LDS in wave order, then SwiGLU; h is
 //               stored as fp16 in the MFMA K order.
 //   bat_down  : chunk = 128 rows of H (wave w: one group of 16 rows over all
@@ -108,11 +108,13 @@ __device__ inline int bat_first() {
 
 // --- gate/up ----------------------------------------------------------------
 
-// The lane's token operand: 8 kk .. 8 kk + 7 of each of its NBL blocks, fp16
-// in the MFMA K order (each group of four as 0, 2, 1, 3). XBF16: converted
-// from the bf16 activations (round to nearest even); else read from the fp16
-// copy.
-template <int NBL, bool XBF16>
+// The lane's token operand: the activations of its NBL blocks, fp16, in the
+// weight operand's K order. Q2: operand kk holds weights 8 kk .. 8 kk + 7,
+// each group of four as 0, 2, 1, 3 (the order of the fp16 copy). Q3: operand
+// 2 w + h holds weights 16 w + 4 (i & 3) + 2 h + (i >> 2) at position i (the
+// FP8 form's order). XBF16: converted from the bf16 activations (round to
+// nearest even); else taken from the fp16 copy.
+template <int Q, int NBL, bool XBF16>
 __device__ inline void load_xop(const FfnArgs& a, int H, int t, bool live, int kb0,
                                 half8_t (&xf)[NBL][4]) {
   if (!live) {
@@ -124,6 +126,33 @@ __device__ inline void load_xop(const FfnArgs& a, int H, int t, bool live, int k
   }
   const uint16_t* row = (XBF16 ? static_cast<const uint16_t*>(a.x) : a.x16) + (uint32_t)(t * H + 32 * kb0);
   const uint4* src = reinterpret_cast<const uint4*>(row);
+  if constexpr (Q == 3) {
+#pragma unroll
+    for (int b = 0; b < NBL; ++b)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint4 v0 = src[4 * b + 2 * w], v1 = src[4 * b + 2 * w + 1];
+        if (XBF16) {
+          // v0: weights 0 .. 7 of the word (two per dword, low half first), v1: 8 .. 15
+          xf[b][2 * w] = __builtin_bit_cast(
+              half8_t, make_uint4(pack_half2(bf16_lo(v0.x), bf16_lo(v0.z)), pack_half2(bf16_lo(v1.x), bf16_lo(v1.z)),
+                                  pack_half2(bf16_hi(v0.x), bf16_hi(v0.z)), pack_half2(bf16_hi(v1.x), bf16_hi(v1.z))));
+          xf[b][2 * w + 1] = __builtin_bit_cast(
+              half8_t, make_uint4(pack_half2(bf16_lo(v0.y), bf16_lo(v0.w)), pack_half2(bf16_lo(v1.y), bf16_lo(v1.w)),
+                                  pack_half2(bf16_hi(v0.y), bf16_hi(v0.w)), pack_half2(bf16_hi(v1.y), bf16_hi(v1.w))));
+        } else {
+          // fp16 copy: dwords hold weights (0, 2), (1, 3), (4, 6), (5, 7) of each eight
+          constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
+          xf[b][2 * w] = __builtin_bit_cast(
+              half8_t, make_uint4(__builtin_amdgcn_perm(v0.z, v0.x, kLo), __builtin_amdgcn_perm(v1.z, v1.x, kLo),
+                                  __builtin_amdgcn_perm(v0.w, v0.y, kLo), __builtin_amdgcn_perm(v1.w, v1.y, kLo)));
+          xf[b][2 * w + 1] = __builtin_bit_cast(
+              half8_t, make_uint4(__builtin_amdgcn_perm(v0.z, v0.x, kHi), __builtin_amdgcn_perm(v1.z, v1.x, kHi),
+                                  __builtin_amdgcn_perm(v0.w, v0.y, kHi), __builtin_amdgcn_perm(v1.w, v1.y, kHi)));
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < NBL; ++b)
 #pragma unroll
@@ -150,13 +179,13 @@ __device__ inline void gu_partial(const WRow<NBL>& wg, const WRow<NBL>& wu, cons
       // one code word (16 weights) of one row at a time
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        const WSplitWord sg = wsplit_word(wg.c[2 * b + w], wg.hi[b], wg.dm[b], w);
-        ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_word(sg, 0), xf[b][2 * w], ag, 0, 0, 0);
-        ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_word(sg, 1), xf[b][2 * w + 1], ag, 0, 0, 0);
+        const WByteWord sg = wbyte_word(wg.c[2 * b + w], wg.hi[b], wg.dm[b], w);
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_byte(sg, 0), xf[b][2 * w], ag, 0, 0, 0);
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_byte(sg, 1), xf[b][2 * w + 1], ag, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        const WSplitWord su = wsplit_word(wu.c[2 * b + w], wu.hi[b], wu.dm[b], w);
-        au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_word(su, 0), xf[b][2 * w], au, 0, 0, 0);
-        au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_word(su, 1), xf[b][2 * w + 1], au, 0, 0, 0);
+        const WByteWord su = wbyte_word(wu.c[2 * b + w], wu.hi[b], wu.dm[b], w);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_byte(su, 0), xf[b][2 * w], au, 0, 0, 0);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_byte(su, 1), xf[b][2 * w + 1], au, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -183,10 +212,13 @@ __device__ inline void gu_partial(const WRow<NBL>& wg, const WRow<NBL>& wu, cons
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Sum of the eight partial tiles (wave order), SwiGLU, h store: rows 4 q + s
-// and 4 q + s + 2 (s = 0, 1) sit side by side in the K order, one 32-bit
-// store per row pair and token. Taken by the 128 threads of waves 2 j, 2 j + 1
-// (j = row group mod 4), so the extra work rotates over the waves.
+// Sum of the eight partial tiles (wave order), SwiGLU, h store in the down
+// operand's K order, one 32-bit store per pair of positions (2 p, 2 p + 1) and
+// token. Q2: positions 4 q + 2 s, + 1 hold rows 4 q + s, 4 q + s + 2; Q3 (16
+// rows, one code word of down): positions 2 p, 2 p + 1 hold rows r, r + 4 with
+// r = p / 2 + 8 (p & 1). Taken by the 128 threads of waves 2 j, 2 j + 1 (j =
+// row group mod 4), so the extra work rotates over the waves.
+template <int Q>
 __device__ inline void gu_finish(const float (&red)[kBWaves][2][16][17], int j, const BatItem& it,
                                  int row0, int I, uint16_t* h) {
   const int rt = (int)threadIdx.x - 128 * (j & 3);
@@ -194,7 +226,8 @@ __device__ inline void gu_finish(const float (&red)[kBWaves][2][16][17], int j, 
   const int pr = rt >> 4, t = rt & 15;
   const int m = 16 * it.tg + t;
   if (m >= it.M) return;
-  const int ra = 4 * (pr >> 1) + (pr & 1), rb = ra + 2;
+  const int ra = Q == 3 ? (pr >> 1) + 8 * (pr & 1) : 4 * (pr >> 1) + (pr & 1);
+  const int rb = ra + (Q == 3 ? 4 : 2);
   float ga = 0.f, ua = 0.f, gb = 0.f, ub = 0.f;
 #pragma unroll
   for (int w = 0; w < kBWaves; ++w) {
@@ -203,7 +236,7 @@ __device__ inline void gu_finish(const float (&red)[kBWaves][2][16][17], int j, 
     gb += red[w][0][rb][t];
     ub += red[w][1][rb][t];
   }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(h + (size_t)(it.slot0 + m) * I + row0 + 4 * (pr >> 1) + 2 * (pr & 1));
+  uint32_t* dst = reinterpret_cast<uint32_t*>(h + (size_t)(it.slot0 + m) * I + row0 + 2 * pr);
   *dst = pack_half2(silu_mul(ga, ua), silu_mul(gb, ub));
 }
 
@@ -255,7 +288,7 @@ void bat_gateup(Experts ex, FfnArgs a) {
           t = (unsigned)t < (unsigned)a.T ? t : 0;
         }
       }
-      load_xop<NBL, XBF16>(a, H, t, live, kb0, xf);
+      load_xop<Q, NBL, XBF16>(a, H, t, live, kb0, xf);
     }
     const int next = item + gridDim.x;
     const bool more = next < n_items;
@@ -268,13 +301,13 @@ void bat_gateup(Experts ex, FfnArgs a) {
       ga = wrow(it, 2, blk_gate(ex, it.e));
       ua = wrow(it, 2, blk_up(ex, it.e));
       __syncthreads();
-      gu_finish(red[0], 0, it, row0, I, h);
+      gu_finish<Q>(red[0], 0, it, row0, I, h);
       // row group 1 (set b) -> row group 3
       gu_partial<Q, NBL>(gb, ub, xf, red[1]);
       gb = wrow(it, 3, blk_gate(ex, it.e));
       ub = wrow(it, 3, blk_up(ex, it.e));
       __syncthreads();
-      gu_finish(red[1], 1, it, row0 + 16, I, h);
+      gu_finish<Q>(red[1], 1, it, row0 + 16, I, h);
     }
     // row group R - 2 (set a) -> the next item's row group 0
     gu_partial<Q, NBL>(ga, ua, xf, red[0]);
@@ -283,7 +316,7 @@ void bat_gateup(Experts ex, FfnArgs a) {
       ua = wrow(nx, 0, blk_up(ex, nx.e));
     }
     __syncthreads();
-    gu_finish(red[0], R - 2, it, row0 + 16 * (R - 2), I, h);
+    gu_finish<Q>(red[0], R - 2, it, row0 + 16 * (R - 2), I, h);
     // row group R - 1 (set b) -> the next item's row group 1
     gu_partial<Q, NBL>(gb, ub, xf, red[1]);
     if (more) {
@@ -291,7 +324,7 @@ void bat_gateup(Experts ex, FfnArgs a) {
       ub = wrow(nx, 1, blk_up(ex, nx.e));
     }
     __syncthreads();
-    gu_finish(red[1], R - 1, it, row0 + 16 * (R - 1), I, h);
+    gu_finish<Q>(red[1], R - 1, it, row0 + 16 * (R - 1), I, h);
     if (!more) break;
     item = next;
     it = nx;
@@ -311,11 +344,11 @@ __device__ inline floatx4_t dn_tile(const WRow<NBL>& wd, const _Float16* hrow, i
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) xf[kk] = *reinterpret_cast<const half8_t*>(hrow + 32 * (kb0 + b) + 8 * kk);
     if constexpr (Q == 3) {
-      const WSplit sd = wsplit_block(wd.c[2 * b], wd.c[2 * b + 1], wd.hi[b], wd.dm[b]);
 #pragma unroll
-      for (int kk = 0; kk < 4; kk += 2) {
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(sd, kk), xf[kk], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_split(sd, kk + 1), xf[kk + 1], acc1, 0, 0, 0);
+      for (int w = 0; w < 2; ++w) {
+        const WByteWord sd = wbyte_word(wd.c[2 * b + w], wd.hi[b], wd.dm[b], w);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_byte(sd, 0), xf[2 * w], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_byte(sd, 1), xf[2 * w + 1], acc1, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     } else {

@@ -68,16 +68,6 @@ __device__ inline half2_t fp4x2_to_f16(uint32_t w, int j) {
   }
 }
 
-// The same times 8 (E2M1 0.5 becomes 4).
-__device__ inline half2_t fp4x2_to_f16_x8(uint32_t w, int j) {
-  switch (j) {
-    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, 0);
-    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, 1);
-    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, 2);
-    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 8.0f, 3);
-  }
-}
-
 // Weights 8 kk .. 8 kk + 7 of the block (in the K order above) as an MFMA operand.
 template <int Q>
 __device__ inline half8_t wfrag(const WStage& w, int kk) {
@@ -110,89 +100,50 @@ __device__ inline half8_t wfrag(const WStage& w, int kk) {
   return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-// --- Q3 through the FP4 conversion ----------------------------------------
-// A 3-bit code is q = q_lo + 4 q_hi. The two low bits take the Q2 path above
-// (an FP4 conversion with scale 2 gives q_lo exactly); the third bits, spread
-// to the same nibble positions (byte j of a word's e plane holds codes 4j,
-// 4j + 2 in its two nibbles, the o plane codes 4j + 1, 4j + 3), go through the
-// FP4 conversion with scale 8, which turns nibble 0b0001 (E2M1 0.5) into an
-// exact 4. One exact fp16 add gives q, then one fused d*q + m rounds once, as
-// in wfrag<3>, for far fewer VALU instructions than assembling 3-bit fields.
-struct WSplit {
-  uint32_t e0, o0, e1, o1;      // low bits of code words 0, 1 as E2M1 nibbles (Q2 planes)
-  uint32_t he0, ho0, he1, ho1;  // third bits at the same nibble positions
+// --- Q3 through the FP8 conversion ----------------------------------------
+// A byte holding a code q <= 15 is the OCP E4M3 value q * 2^-9 (subnormal
+// below 8, exponent 1 from 8 on), so the scaled FP8 -> fp16 conversion with
+// scale 2^9 (a power of two) gives q exactly, two bytes per instruction. One
+// code word (16 codes, 2 bits each) and its half of the third-bit plane make
+// four byte words: byte b of word s holds code 4 b + s, its two low bits
+// shifted down from the code word and its third bit taken from a copy of the
+// plane spread one nibble per byte. One fused d*q + m per pair then rounds
+// once. About two VALU instructions per weight, against three and a half for
+// separate FP4 conversions of the low and third bits.
+//
+// K order of this form (both operands follow it): position i of operand half
+// h of a word holds weight 4 (i & 3) + 2 h + (i >> 2), i.e. weights
+// 0, 4, 8, 12, 1, 5, 9, 13 for h = 0 and 2, 6, 10, 14, 3, 7, 11, 15 for h = 1.
+struct WByteWord {
+  uint32_t b[4];
   half2_t d2, m2;
 };
 
-// Bits 2i of x (i = 0..7) in the bytes sel picks, moved to bit 4i of the
-// result: a byte permute, then two shift-or-mask steps.
-__device__ inline uint32_t spread_even(uint32_t x, uint32_t sel) {
-  x = __builtin_amdgcn_perm(x, x, sel);
+__device__ inline WByteWord wbyte_word(uint32_t c, uint32_t hi, uint32_t dm, int w) {
+  // third bits of codes 16 w .. 16 w + 15: nibble b into byte b
+  uint32_t x = __builtin_amdgcn_perm(hi, hi, w ? 0x0C030C02u : 0x0C010C00u);
   x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  return (x | (x << 2)) & 0x33333333u;
+  WByteWord r;
+  r.b[0] = (c & 0x03030303u) | ((x << 2) & 0x04040404u);
+  r.b[1] = ((c >> 2) & 0x03030303u) | ((x << 1) & 0x04040404u);
+  r.b[2] = ((c >> 4) & 0x03030303u) | (x & 0x04040404u);
+  r.b[3] = ((c >> 6) & 0x03030303u) | ((x >> 1) & 0x04040404u);
+  r.d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
+  r.m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
+  return r;
 }
 
-__device__ inline WSplit wsplit_block(uint32_t c0, uint32_t c1, uint32_t hi, uint32_t dm) {
-  WSplit st;
-  st.e0 = c0 & 0x33333333u;
-  st.o0 = (c0 >> 2) & 0x33333333u;
-  st.e1 = c1 & 0x33333333u;
-  st.o1 = (c1 >> 2) & 0x33333333u;
-  const uint32_t ev = hi & 0x55555555u, od = (hi >> 1) & 0x55555555u;
-  st.he0 = spread_even(ev, 0x0C010C00u);  // third bits of codes 0 .. 15
-  st.ho0 = spread_even(od, 0x0C010C00u);
-  st.he1 = spread_even(ev, 0x0C030C02u);  // codes 16 .. 31
-  st.ho1 = spread_even(od, 0x0C030C02u);
-  st.d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
-  st.m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
-  return st;
-}
-
-// The planes of one code word w (0: codes 0 .. 15, 1: codes 16 .. 31), for
-// callers short of registers: weights 8 kk .. 8 kk + 7 for kk = 2 w, 2 w + 1.
-struct WSplitWord {
-  uint32_t e, o, he, ho;
-  half2_t d2, m2;
-};
-
-__device__ inline WSplitWord wsplit_word(uint32_t c, uint32_t hi, uint32_t dm, int w) {
-  WSplitWord st;
-  st.e = c & 0x33333333u;
-  st.o = (c >> 2) & 0x33333333u;
-  const uint32_t sel = w ? 0x0C030C02u : 0x0C010C00u;
-  st.he = spread_even(hi & 0x55555555u, sel);
-  st.ho = spread_even((hi >> 1) & 0x55555555u, sel);
-  st.d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
-  st.m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
-  return st;
-}
-
-// Weights 8 kk .. 8 kk + 7 of the block, kk = 2 w + half.
-__device__ inline half8_t wfrag_word(const WSplitWord& w, int half) {
+// Operand half h of the word: byte words 2 h and 2 h + 1, low bytes (codes s,
+// s + 4) then high bytes (s + 8, s + 12) of each.
+__device__ inline half8_t wfrag_byte(const WByteWord& w, int h) {
   uint32_t o[4];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int j = 2 * half + u;
-    const half2_t qa = fp4x2_to_f16(w.e, j) + fp4x2_to_f16_x8(w.he, j);
-    const half2_t qb = fp4x2_to_f16(w.o, j) + fp4x2_to_f16_x8(w.ho, j);
-    o[2 * u] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qa, w.d2, w.m2));
-    o[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qb, w.d2, w.m2));
-  }
-  return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
-}
-
-// Weights 8 kk .. 8 kk + 7 of the block in the K order above.
-__device__ inline half8_t wfrag_split(const WSplit& w, int kk) {
-  const uint32_t e = kk < 2 ? w.e0 : w.e1, od = kk < 2 ? w.o0 : w.o1;
-  const uint32_t he = kk < 2 ? w.he0 : w.he1, ho = kk < 2 ? w.ho0 : w.ho1;
-  uint32_t o[4];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int j = 2 * (kk & 1) + u;
-    const half2_t qa = fp4x2_to_f16(e, j) + fp4x2_to_f16_x8(he, j);
-    const half2_t qb = fp4x2_to_f16(od, j) + fp4x2_to_f16_x8(ho, j);
-    o[2 * u] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qa, w.d2, w.m2));
-    o[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qb, w.d2, w.m2));
+    const uint32_t bw = w.b[2 * h + u];
+    const half2_t ql = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bw, 512.0f, false);
+    const half2_t qh = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bw, 512.0f, true);
+    o[2 * u] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(ql, w.d2, w.m2));
+    o[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qh, w.d2, w.m2));
   }
   return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
