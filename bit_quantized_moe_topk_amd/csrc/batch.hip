@@ -27,9 +27,12 @@
 //
 // Both grids are persistent (gate/up: two workgroups per CU, down: three):
 // every workgroup builds a map of the grouping in LDS (token groups per
-// expert, slot offsets, and the token id or gate of every slot) and takes
-// items dealt round-robin; an expert's consecutive items, which read the same
-// weights, go to workgroups of one XCD.
+// expert, slot offsets, and the token id or gate of every slot). Gate/up
+// workgroups take runs of consecutive items in (expert, token group, chunk)
+// order, so the activations of a token group are loaded once per run; down
+// items are dealt round-robin in (expert, chunk, token group) order. Either
+// way the items of one expert, which read the same weights, go to workgroups
+// of one XCD.
 #include "common.h"
 #include "deq16.h"
 #include "gemv.h"
@@ -98,9 +101,25 @@ __device__ inline BatItem bat_item(const int* base, const int* off, int E_tot, i
   return it;
 }
 
+// Gate/up items in (expert, token group, chunk) order: the chunks of one
+// token group follow each other, so a workgroup that takes a run of them
+// keeps the group's activations in registers.
+__device__ inline BatItem bat_item_seq(const int* base, const int* off, int E_tot, int NC, int item) {
+  const int gi = item / NC;
+  const int e = workmap_find(base, E_tot, gi);
+  BatItem it;
+  it.e = __builtin_amdgcn_readfirstlane(e);
+  it.chunk = __builtin_amdgcn_readfirstlane(item - NC * gi);
+  it.tg = __builtin_amdgcn_readfirstlane(gi - base[e]);
+  it.slot0 = __builtin_amdgcn_readfirstlane(off[e]);
+  it.M = __builtin_amdgcn_readfirstlane(off[e + 1] - off[e]);
+  return it;
+}
+
 // First item of this workgroup; later ones follow every gridDim.x. Consecutive
 // item numbers go to workgroups of one XCD (workgroup g runs on XCD g % 8)
-// when the grid is a multiple of 8.
+// when the grid is a multiple of 8. The gate/up kernel uses the same number
+// as its column: it takes items column * rows .. column * rows + rows - 1.
 __device__ inline int bat_first() {
   const int g = blockIdx.x, G = gridDim.x;
   return (G % 8) ? g : (g % 8) * (G / 8) + g / 8;
@@ -260,8 +279,13 @@ void bat_gateup(Experts ex, FfnArgs a) {
   });
   const int NC = I / (16 * R);
   const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
-  int item = bat_first();
-  if (item >= n_items) return;
+  // a run of consecutive items per workgroup (runs of neighbouring workgroup
+  // numbers on one XCD, so the token groups of one expert, which read the
+  // same weights, meet in its L2)
+  const int rows = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
+  int item = bat_first() * rows;
+  const int item_end = min(n_items, item + rows);
+  if (item >= item_end) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int kb0 = wave * (H / 256) + NBL * (lane >> 4);  // the lane's first block of its rows
@@ -271,12 +295,13 @@ void bat_gateup(Experts ex, FfnArgs a) {
     return load_wrow_at<Q, NBL>(ex, mat0 + (size_t)(16 * (R * it.chunk + j)) * (H / 32), lane_blk);
   };
 
-  BatItem it = bat_item(base, off, E_tot, NC, item);
+  BatItem it = bat_item_seq(base, off, E_tot, NC, item);
   WRow<NBL> ga = wrow(it, 0, blk_gate(ex, it.e)), ua = wrow(it, 0, blk_up(ex, it.e));
   WRow<NBL> gb = wrow(it, 1, blk_gate(ex, it.e)), ub = wrow(it, 1, blk_up(ex, it.e));
+  half8_t xf[NBL][4];
+  bool new_group = true;
   for (;;) {
-    half8_t xf[NBL][4];
-    {
+    if (new_group) {
       const int m = 16 * it.tg + r16, slot = it.slot0 + m;
       const bool live = m < it.M;
       int t = 0;
@@ -290,10 +315,10 @@ void bat_gateup(Experts ex, FfnArgs a) {
       }
       load_xop<Q, NBL, XBF16>(a, H, t, live, kb0, xf);
     }
-    const int next = item + gridDim.x;
-    const bool more = next < n_items;
+    const int next = item + 1;
+    const bool more = next < item_end;
     BatItem nx = it;
-    if (more) nx = bat_item(base, off, E_tot, NC, next);
+    if (more) nx = bat_item_seq(base, off, E_tot, NC, next);
     const int row0 = 16 * R * it.chunk;
     if constexpr (R == 4) {
       // row group 0 (set a), then its weights make way for row group 2
@@ -326,6 +351,7 @@ void bat_gateup(Experts ex, FfnArgs a) {
     __syncthreads();
     gu_finish<Q>(red[1], R - 1, it, row0 + 16 * (R - 1), I, h);
     if (!more) break;
+    new_group = nx.e != it.e || nx.tg != it.tg;
     item = next;
     it = nx;
   }
