@@ -65,18 +65,38 @@ struct BatItem {
   int e, chunk, tg, M, slot0;
 };
 
-// Fills the map, and tab[s] = fill(s) for every slot when the table is used;
-// all threads of the block call it.
-template <typename Fill>
+// Fills the map, and with kTab calls fill(s, perm[s]) for every slot when the
+// table is used (A <= kBTab); all kBThreads threads of the block call it.
+// Every global load is issued (at a clamped, in-bounds index) before the
+// first one is used: the map costs one memory round trip.
+template <bool kTab, typename Fill>
 __device__ inline void batmap_init(BatMap& bm, int* base, int* off, const FfnArgs& a, int E_tot,
                                    bool use_tab, int A, Fill&& fill) {
-  for (int e = threadIdx.x; e <= E_tot; e += blockDim.x) {
-    const int o = a.offsets[e];
-    off[e] = o;
-    if (e < E_tot) base[e] = (a.counts[e] + 15) >> 4;
+  constexpr int kEPer = (MOE_MAX_E_DEV + 2 + kBThreads - 1) / kBThreads;
+  constexpr int kSPer = kBTab / kBThreads;
+  const int tid = threadIdx.x;
+  int ov[kEPer], cv[kEPer], pv[kSPer];
+#pragma unroll
+  for (int u = 0; u < kEPer; ++u) {
+    const int e = tid + kBThreads * u;
+    ov[u] = a.offsets[min(e, E_tot)];
+    cv[u] = a.counts[min(e, E_tot - 1)];
   }
-  if (use_tab)
-    for (int s = threadIdx.x; s < A; s += blockDim.x) fill(s);
+#pragma unroll
+  for (int u = 0; u < kSPer; ++u) pv[u] = kTab ? a.perm[min(tid + kBThreads * u, A - 1)] : 0;
+#pragma unroll
+  for (int u = 0; u < kEPer; ++u) {
+    const int e = tid + kBThreads * u;
+    if (e <= E_tot) off[e] = ov[u];
+    if (e < E_tot) base[e] = (cv[u] + 15) >> 4;
+  }
+  if (kTab && use_tab) {
+#pragma unroll
+    for (int u = 0; u < kSPer; ++u) {
+      const int sl = tid + kBThreads * u;
+      if (sl < A) fill(sl, pv[u]);
+    }
+  }
   __syncthreads();
   const int n = block_exclusive_scan(base, E_tot, bm.wsum);
   if (threadIdx.x == 0) {
@@ -273,8 +293,8 @@ void bat_gateup(Experts ex, FfnArgs a) {
   const bool use_tab = A <= kBTab;
   int* base = bat_dyn;
   int* off = bat_dyn + E_tot + 2;
-  batmap_init(bm, base, off, a, E_tot, use_tab, A, [&](int s) {
-    const int t = token_of(a.perm[s], a.T, a.k);
+  batmap_init<true>(bm, base, off, a, E_tot, use_tab, A, [&](int s, int asg) {
+    const int t = token_of(asg, a.T, a.k);
     tok[s] = (unsigned)t < (unsigned)a.T ? t : 0;
   });
   const int NC = I / (16 * R);
@@ -421,7 +441,7 @@ void bat_down(Experts ex, FfnArgs a) {
   int* base = bat_dyn;
   int* off = bat_dyn + E_tot + 2;
   // the gate table is filled after the first item's loads are in flight (below)
-  batmap_init(bm, base, off, a, E_tot, false, A, [](int) {});
+  batmap_init<false>(bm, base, off, a, E_tot, false, A, [](int, int) {});
   const int NC = H / (16 * kDnRows * kBWaves);
   const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
   int item = bat_first();
