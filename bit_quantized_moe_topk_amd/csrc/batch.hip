@@ -27,12 +27,12 @@
 //
 // Both grids are persistent (gate/up: two workgroups per CU, down: three):
 // every workgroup builds a map of the grouping in LDS (token groups per
-// expert, slot offsets, and the token id or gate of every slot). Gate/up
-// workgroups take runs of consecutive items in (expert, token group, chunk)
-// order, so the activations of a token group are loaded once per run; down
-// items are dealt round-robin in (expert, chunk, token group) order. Either
-// way the items of one expert, which read the same weights, go to workgroups
-// of one XCD.
+// expert, slot offsets, and the token id or gate of every slot) and takes a
+// run of consecutive items in (expert, token group, chunk) order, so a token
+// group's activations (h rows for down) are loaded once per run; the items of
+// one expert, which read the same weights, go to workgroups of one XCD. Waves
+// raise their issue priority by the workgroup's progress, so the workgroups
+// sharing a CU move together instead of the youngest finishing alone.
 #include "common.h"
 #include "deq16.h"
 #include "gemv.h"
@@ -106,24 +106,9 @@ __device__ inline void batmap_init(BatMap& bm, int* base, int* off, const FfnArg
   __syncthreads();
 }
 
-// Items of expert e are NC * G_e consecutive numbers from NC * base[e], in
-// (chunk, token group) order.
-__device__ inline BatItem bat_item(const int* base, const int* off, int E_tot, int NC, int item) {
-  const int e = workmap_find(base, E_tot, item / NC);
-  const int g0 = base[e], G = base[e + 1] - g0;
-  const int local = item - NC * g0;
-  BatItem it;
-  it.e = __builtin_amdgcn_readfirstlane(e);
-  it.chunk = __builtin_amdgcn_readfirstlane(local / G);
-  it.tg = __builtin_amdgcn_readfirstlane(local % G);
-  it.slot0 = __builtin_amdgcn_readfirstlane(off[e]);
-  it.M = __builtin_amdgcn_readfirstlane(off[e + 1] - off[e]);
-  return it;
-}
-
-// Gate/up items in (expert, token group, chunk) order: the chunks of one
-// token group follow each other, so a workgroup that takes a run of them
-// keeps the group's activations in registers.
+// Items in (expert, token group, chunk) order: the chunks of one token group
+// follow each other, so a workgroup that takes a run of them keeps the
+// group's activations (gate/up: registers; down: h rows in LDS).
 __device__ inline BatItem bat_item_seq(const int* base, const int* off, int E_tot, int NC, int item) {
   const int gi = item / NC;
   const int e = workmap_find(base, E_tot, gi);
@@ -136,16 +121,26 @@ __device__ inline BatItem bat_item_seq(const int* base, const int* off, int E_to
   return it;
 }
 
-// First item of this workgroup; later ones follow every gridDim.x. Consecutive
-// item numbers go to workgroups of one XCD (workgroup g runs on XCD g % 8)
-// when the grid is a multiple of 8. The gate/up kernel uses the same number
-// as its column: it takes items column * rows .. column * rows + rows - 1.
+// Column of this workgroup: it takes items column * rows .. column * rows +
+// rows - 1. Neighbouring columns go to workgroups of one XCD (workgroup g runs
+// on XCD g % 8) when the grid is a multiple of 8, so the token groups of one
+// expert, which read the same weights, meet in that XCD's L2.
 __device__ inline int bat_first() {
   const int g = blockIdx.x, G = gridDim.x;
   return (G % 8) ? g : (g % 8) * (G / 8) + g / 8;
 }
 
 // --- gate/up ----------------------------------------------------------------
+
+// Waves issue by priority, then age: the workgroup that has finished fewer
+// items goes first, so the workgroups on a CU progress together instead of
+// the youngest one running alone at the end.
+__device__ inline void set_prio_by_progress(int done) {
+  if (done == 0) __builtin_amdgcn_s_setprio(3);
+  else if (done == 1) __builtin_amdgcn_s_setprio(2);
+  else if (done == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
 
 // The lane's token operand: the activations of its NBL blocks, fp16, in the
 // weight operand's K order. Q2: operand kk holds weights 8 kk .. 8 kk + 7,
@@ -299,9 +294,7 @@ void bat_gateup(Experts ex, FfnArgs a) {
   });
   const int NC = I / (16 * R);
   const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
-  // a run of consecutive items per workgroup (runs of neighbouring workgroup
-  // numbers on one XCD, so the token groups of one expert, which read the
-  // same weights, meet in its L2)
+  // a run of consecutive items per workgroup
   const int rows = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
   int item = bat_first() * rows;
   const int item_end = min(n_items, item + rows);
@@ -320,7 +313,9 @@ void bat_gateup(Experts ex, FfnArgs a) {
   WRow<NBL> gb = wrow(it, 1, blk_gate(ex, it.e)), ub = wrow(it, 1, blk_up(ex, it.e));
   half8_t xf[NBL][4];
   bool new_group = true;
+  int done = 0;
   for (;;) {
+    set_prio_by_progress(done++);
     if (new_group) {
       const int m = 16 * it.tg + r16, slot = it.slot0 + m;
       const bool live = m < it.M;
@@ -444,8 +439,12 @@ void bat_down(Experts ex, FfnArgs a) {
   batmap_init<false>(bm, base, off, a, E_tot, false, A, [](int, int) {});
   const int NC = H / (16 * kDnRows * kBWaves);
   const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
-  int item = bat_first();
-  if (item >= n_items) return;
+  // runs of consecutive items in (expert, token group, chunk) order, as in
+  // the gate/up kernel: a token group's h rows stay in LDS for its run
+  const int rows = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
+  int item = bat_first() * rows;
+  const int item_end = min(n_items, item + rows);
+  if (item >= item_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane >> 4, r16 = lane & 15;
   const int kb0 = NBL * c;
@@ -466,7 +465,7 @@ void bat_down(Experts ex, FfnArgs a) {
     }
   };
 
-  BatItem it = bat_item(base, off, E_tot, NC, item);
+  BatItem it = bat_item_seq(base, off, E_tot, NC, item);
   WRow<NBL> w0 = wrow(it, 0), w1;
   if constexpr (kDnRows == 2) w1 = wrow(it, 1);
   uint4 hv[HC];
@@ -476,21 +475,24 @@ void bat_down(Experts ex, FfnArgs a) {
   // publishes it
   if (use_tab)
     for (int s = tid; s < A; s += kBThreads) gtab[s] = gate_of(a, s);
-  int buf = 0;
+  int buf = 0, done = 0;
+  bool new_group = true;
   for (;;) {
+    set_prio_by_progress(done++);
+    if (new_group) {
 #pragma unroll
-    for (int u = 0; u < HC; ++u) {
-      const int q = tid + kBThreads * u, r = q / (I_ / 8), col = q % (I_ / 8);
-      *reinterpret_cast<uint4*>(&hs[buf][r * kRow + 8 * col]) = hv[u];
+      for (int u = 0; u < HC; ++u) {
+        const int q = tid + kBThreads * u, r = q / (I_ / 8), col = q % (I_ / 8);
+        *reinterpret_cast<uint4*>(&hs[buf][r * kRow + 8 * col]) = hv[u];
+      }
+      __syncthreads();  // hs[buf] complete; hs[buf ^ 1] no longer read
     }
-    __syncthreads();  // hs[buf] complete; hs[buf ^ 1] no longer read
-    const int next = item + gridDim.x;
-    const bool more = next < n_items;
+    const int next = item + 1;
+    const bool more = next < item_end;
     BatItem nx = it;
-    if (more) {
-      nx = bat_item(base, off, E_tot, NC, next);
-      hload(nx, hv);
-    }
+    if (more) nx = bat_item_seq(base, off, E_tot, NC, next);
+    const bool next_group = more && (nx.e != it.e || nx.tg != it.tg);
+    if (next_group) hload(nx, hv);
     const int m = 16 * it.tg + r16, slot = it.slot0 + m;
     const bool live = m < it.M;
     const float g = live ? (use_tab ? gtab[slot] : gate_of(a, slot)) : 0.f;
@@ -505,9 +507,10 @@ void bat_down(Experts ex, FfnArgs a) {
     }
     if (live) dn_store(a, H, slot, row0, g, o0);
     if (!more) break;
+    if (next_group) buf ^= 1;
+    new_group = next_group;
     item = next;
     it = nx;
-    buf ^= 1;
   }
 }
 
