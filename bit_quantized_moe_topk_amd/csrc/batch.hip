@@ -142,30 +142,35 @@ __device__ inline void set_prio_by_progress(int done) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-// The lane's token operand: the activations of its NBL blocks, fp16, in the
-// weight operand's K order. Q2: operand kk holds weights 8 kk .. 8 kk + 7,
+// The lane's token operand holds the activations of its NBL blocks, fp16, in
+// the weight operand's K order. Q2: operand kk holds weights 8 kk .. 8 kk + 7,
 // each group of four as 0, 2, 1, 3 (the order of the fp16 copy). Q3: operand
 // 2 w + h holds weights 16 w + 4 (i & 3) + 2 h + (i >> 2) at position i (the
 // FP8 form's order). XBF16: converted from the bf16 activations (round to
 // nearest even); else taken from the fp16 copy.
-template <int Q, int NBL, bool XBF16>
-__device__ inline void load_xop(const FfnArgs& a, int H, int t, bool live, int kb0,
-                                half8_t (&xf)[NBL][4]) {
-  if (!live) {
-#pragma unroll
-    for (int b = 0; b < NBL; ++b)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) xf[b][kk] = half8_t{};
-    return;
-  }
+// Raw activations of token t for the lane's NBL blocks (bf16 or the fp16
+// copy), requested without waiting for them. A padding column of the tile
+// loads some valid token's row: the matrix product keeps columns apart and
+// padding columns are never stored.
+template <int NBL, bool XBF16>
+__device__ inline void load_xraw(const FfnArgs& a, int H, int t, int kb0, uint4 (&xr)[NBL][4]) {
   const uint16_t* row = (XBF16 ? static_cast<const uint16_t*>(a.x) : a.x16) + (uint32_t)(t * H + 32 * kb0);
   const uint4* src = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+  for (int b = 0; b < NBL; ++b)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xr[b][q] = src[4 * b + q];
+}
+
+// The raw activations as the token operand.
+template <int Q, int NBL, bool XBF16>
+__device__ inline void xop_of(const uint4 (&xr)[NBL][4], half8_t (&xf)[NBL][4]) {
   if constexpr (Q == 3) {
 #pragma unroll
     for (int b = 0; b < NBL; ++b)
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        const uint4 v0 = src[4 * b + 2 * w], v1 = src[4 * b + 2 * w + 1];
+        const uint4 v0 = xr[b][2 * w], v1 = xr[b][2 * w + 1];
         if (XBF16) {
           // v0: weights 0 .. 7 of the word (two per dword, low half first), v1: 8 .. 15
           xf[b][2 * w] = __builtin_bit_cast(
@@ -191,7 +196,7 @@ __device__ inline void load_xop(const FfnArgs& a, int H, int t, bool live, int k
   for (int b = 0; b < NBL; ++b)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint4 v = src[4 * b + kk];
+      const uint4 v = xr[b][kk];
       xf[b][kk] = XBF16 ? __builtin_bit_cast(half8_t, make_uint4(pack_half2(bf16_lo(v.x), bf16_lo(v.y)),
                                                                  pack_half2(bf16_hi(v.x), bf16_hi(v.y)),
                                                                  pack_half2(bf16_lo(v.z), bf16_lo(v.w)),
@@ -308,27 +313,42 @@ void bat_gateup(Experts ex, FfnArgs a) {
     return load_wrow_at<Q, NBL>(ex, mat0 + (size_t)(16 * (R * it.chunk + j)) * (H / 32), lane_blk);
   };
 
+  // raw activations of the item's token group for the lane's token
+  auto load_x = [&](const BatItem& it, uint4 (&xr)[NBL][4]) {
+    const int m = min(16 * it.tg + r16, it.M - 1), slot = it.slot0 + m;  // padding: the last token
+    int t;
+    if (use_tab) {
+      t = tok[slot];
+    } else {
+      t = token_of(a.perm[slot], a.T, a.k);
+      t = (unsigned)t < (unsigned)a.T ? t : 0;
+    }
+    load_xraw<NBL, XBF16>(a, H, t, kb0, xr);
+  };
+
+  // first item: activations requested first, so its first row group can start
+  // while the second one's weights are still in flight
   BatItem it = bat_item_seq(base, off, E_tot, NC, item);
-  WRow<NBL> ga = wrow(it, 0, blk_gate(ex, it.e)), ua = wrow(it, 0, blk_up(ex, it.e));
-  WRow<NBL> gb = wrow(it, 1, blk_gate(ex, it.e)), ub = wrow(it, 1, blk_up(ex, it.e));
   half8_t xf[NBL][4];
-  bool new_group = true;
+  WRow<NBL> ga, ua, gb, ub;
+  {
+    uint4 xr[NBL][4];
+    load_x(it, xr);
+    ga = wrow(it, 0, blk_gate(ex, it.e));
+    ua = wrow(it, 0, blk_up(ex, it.e));
+    gb = wrow(it, 1, blk_gate(ex, it.e));
+    ub = wrow(it, 1, blk_up(ex, it.e));
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
+    xop_of<Q, NBL, XBF16>(xr, xf);
+  }
+  bool new_group = false;
   int done = 0;
   for (;;) {
     set_prio_by_progress(done++);
     if (new_group) {
-      const int m = 16 * it.tg + r16, slot = it.slot0 + m;
-      const bool live = m < it.M;
-      int t = 0;
-      if (live) {
-        if (use_tab) {
-          t = tok[slot];
-        } else {
-          t = token_of(a.perm[slot], a.T, a.k);
-          t = (unsigned)t < (unsigned)a.T ? t : 0;
-        }
-      }
-      load_xop<Q, NBL, XBF16>(a, H, t, live, kb0, xf);
+      uint4 xr[NBL][4];
+      load_x(it, xr);
+      xop_of<Q, NBL, XBF16>(xr, xf);
     }
     const int next = item + 1;
     const bool more = next < item_end;
