@@ -4,6 +4,7 @@
 
 #include "../../include/moe.h"
 #include "common.h"
+#include "batch_x.h"
 
 using moe::Experts;
 
@@ -187,10 +188,21 @@ size_t moe_ffn_q_workspace_size(const moe_experts* ex, int32_t T, int32_t k, int
   return ffn_layout(ex->d, T, k, mode).total;
 }
 
-int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, const int32_t* idx,
-              const float* gates, int32_t k, const int32_t* counts, const int32_t* offsets,
-              const int32_t* perm, const int32_t* slot_of, void* y, int32_t mode, void* ws,
-              size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Fast mode below 256 tokens on shapes the small-batch kernels cover.
+inline bool batch_path(const Experts& d, int T, int mode) {
+  return mode == MOE_FAST && T < moe::kGemvBatchLimit && moe::batch_supported(d.H, d.I);
+}
+
+// moe_ffn_q; xs_ready: the workspace's x16 already holds the small-batch
+// activation layout (written by the caller's grouping launch).
+int ffn_q_impl(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, const int32_t* idx,
+               const float* gates, int32_t k, const int32_t* counts, const int32_t* offsets,
+               const int32_t* perm, const int32_t* slot_of, void* y, int32_t mode, void* ws,
+               size_t ws_bytes, void* stream, bool xs_ready) {
   if (!ex || T < 0 || k < 1 || k > ex->d.E) return MOE_ERR_INVALID_ARG;
   if (xdtype != MOE_F32 && xdtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (mode != MOE_FAST && mode != MOE_CHECK_F32) return MOE_ERR_INVALID_ARG;
@@ -215,6 +227,7 @@ int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, c
   a.y = y;
   a.h = at(ws, L.h);
   a.x16 = reinterpret_cast<uint16_t*>(at(ws, L.x16));
+  a.xs_ready = xs_ready;
   if (given == 4) {
     a.counts = counts;
     a.offsets = offsets;
@@ -225,8 +238,13 @@ int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, c
     int32_t* o = reinterpret_cast<int32_t*>(at(ws, L.offsets));
     int32_t* p = reinterpret_cast<int32_t*>(at(ws, L.perm));
     int32_t* so = reinterpret_cast<int32_t*>(at(ws, L.slot_of));
-    hipError_t e = moe::launch_group(idx, T, k, d.E, d.has_shared, c, o, p, so, at(ws, L.group), s);
+    // the small-batch activation layout rides in the one-workgroup grouping launch
+    const moe::XsJob xj = moe::batch_xs_job(d, x, xdtype, T, a.x16);
+    bool xs_done = false;
+    hipError_t e = moe::launch_group(idx, T, k, d.E, d.has_shared, c, o, p, so, at(ws, L.group), s,
+                                     batch_path(d, T, mode) ? &xj : nullptr, &xs_done);
     if (e != hipSuccess) return MOE_ERR_HIP;
+    a.xs_ready = xs_done;
     a.counts = c;
     a.offsets = o;
     a.perm = p;
@@ -242,7 +260,7 @@ int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, c
     // From a few hundred tokens on, experts with few assignments ride in the
     // persistent matrix-core grid, where their weight reads overlap the other
     // tiles' arithmetic; a separate GEMV pass would run on its own.
-    if (T < moe::kGemvBatchLimit && moe::batch_supported(d.H, d.I)) {
+    if (batch_path(d, T, mode)) {
       e = moe::launch_batch(d, a, s);
     } else {
       const bool small_batch = T < moe::kGemvBatchLimit || !moe::mfma_supported(d.H, d.I);
@@ -252,6 +270,18 @@ int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, c
   }
   if (e == hipSuccess) e = moe::launch_combine(d, a, s);
   return status_of(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_q(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, const int32_t* idx,
+              const float* gates, int32_t k, const int32_t* counts, const int32_t* offsets,
+              const int32_t* perm, const int32_t* slot_of, void* y, int32_t mode, void* ws,
+              size_t ws_bytes, void* stream) {
+  return ffn_q_impl(x, xdtype, T, ex, idx, gates, k, counts, offsets, perm, slot_of, y, mode, ws,
+                    ws_bytes, stream, false);
 }
 
 // ---- whole layer -----------------------------------------------------------
@@ -311,11 +341,17 @@ int moe_layer(const float* logits, const void* x, int32_t xdtype, int32_t T, con
   int32_t* o = reinterpret_cast<int32_t*>(at(ws, L.offsets));
   int32_t* p = reinterpret_cast<int32_t*>(at(ws, L.perm));
   int32_t* so = reinterpret_cast<int32_t*>(at(ws, L.slot_of));
-  int st = moe_route_group(logits, T, d.E, k, d.has_shared, idx, gates, c, o, p, so,
-                           at(ws, L.group), moe::group_scratch_bytes(T, k, d.E), stream);
-  if (st != MOE_OK) return st;
-  return moe_ffn_q(x, xdtype, T, ex, idx, gates, k, c, o, p, so, y, mode, at(ws, L.ffn),
-                   ws_bytes - L.ffn, stream);
+  // the small-batch activation layout rides in the routing's one-workgroup
+  // grouping launch when there is one
+  const FfnLayout F = ffn_layout(d, T, k, mode);
+  const moe::XsJob xj = moe::batch_xs_job(d, x, xdtype, T, reinterpret_cast<uint16_t*>(at(ws, L.ffn + F.x16)));
+  bool xs_done = false;
+  const hipError_t e = moe::launch_route_group(logits, T, d.E, k, d.has_shared, idx, gates, c, o, p, so,
+                                               at(ws, L.group), s, batch_path(d, T, mode) ? &xj : nullptr,
+                                               &xs_done);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return ffn_q_impl(x, xdtype, T, ex, idx, gates, k, c, o, p, so, y, mode, at(ws, L.ffn),
+                    ws_bytes - L.ffn, stream, xs_done);
 }
 
 }  // extern "C"

@@ -37,6 +37,7 @@
 #include "deq16.h"
 #include "gemv.h"
 #include "sched.h"
+#include "batch_x.h"
 
 namespace moe {
 namespace {
@@ -142,67 +143,21 @@ __device__ inline void set_prio_by_progress(int done) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-// The lane's token operand holds the activations of its NBL blocks, fp16, in
-// the weight operand's K order. Q2: operand kk holds weights 8 kk .. 8 kk + 7,
-// each group of four as 0, 2, 1, 3 (the order of the fp16 copy). Q3: operand
-// 2 w + h holds weights 16 w + 4 (i & 3) + 2 h + (i >> 2) at position i (the
-// FP8 form's order). XBF16: converted from the bf16 activations (round to
-// nearest even); else taken from the fp16 copy.
-// Raw activations of token t for the lane's NBL blocks (bf16 or the fp16
-// copy), requested without waiting for them. A padding column of the tile
-// loads some valid token's row: the matrix product keeps columns apart and
-// padding columns are never stored.
-template <int NBL, bool XBF16>
-__device__ inline void load_xraw(const FfnArgs& a, int H, int t, int kb0, uint4 (&xr)[NBL][4]) {
-  const uint16_t* row = (XBF16 ? static_cast<const uint16_t*>(a.x) : a.x16) + (uint32_t)(t * H + 32 * kb0);
-  const uint4* src = reinterpret_cast<const uint4*>(row);
-#pragma unroll
-  for (int b = 0; b < NBL; ++b)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xr[b][q] = src[4 * b + q];
+__global__ __launch_bounds__(256) void bat_xs(XsJob xj) {
+  xs_write(xj.x, xj.xbf16, xj.q, xj.H, blockIdx.x * 256L + threadIdx.x, (long)xj.T * xj.H / 8,
+           (long)gridDim.x * 256, xj.xs);
 }
 
-// The raw activations as the token operand.
-template <int Q, int NBL, bool XBF16>
-__device__ inline void xop_of(const uint4 (&xr)[NBL][4], half8_t (&xf)[NBL][4]) {
-  if constexpr (Q == 3) {
-#pragma unroll
-    for (int b = 0; b < NBL; ++b)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint4 v0 = xr[b][2 * w], v1 = xr[b][2 * w + 1];
-        if (XBF16) {
-          // v0: weights 0 .. 7 of the word (two per dword, low half first), v1: 8 .. 15
-          xf[b][2 * w] = __builtin_bit_cast(
-              half8_t, make_uint4(pack_half2(bf16_lo(v0.x), bf16_lo(v0.z)), pack_half2(bf16_lo(v1.x), bf16_lo(v1.z)),
-                                  pack_half2(bf16_hi(v0.x), bf16_hi(v0.z)), pack_half2(bf16_hi(v1.x), bf16_hi(v1.z))));
-          xf[b][2 * w + 1] = __builtin_bit_cast(
-              half8_t, make_uint4(pack_half2(bf16_lo(v0.y), bf16_lo(v0.w)), pack_half2(bf16_lo(v1.y), bf16_lo(v1.w)),
-                                  pack_half2(bf16_hi(v0.y), bf16_hi(v0.w)), pack_half2(bf16_hi(v1.y), bf16_hi(v1.w))));
-        } else {
-          // fp16 copy: dwords hold weights (0, 2), (1, 3), (4, 6), (5, 7) of each eight
-          constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;
-          xf[b][2 * w] = __builtin_bit_cast(
-              half8_t, make_uint4(__builtin_amdgcn_perm(v0.z, v0.x, kLo), __builtin_amdgcn_perm(v1.z, v1.x, kLo),
-                                  __builtin_amdgcn_perm(v0.w, v0.y, kLo), __builtin_amdgcn_perm(v1.w, v1.y, kLo)));
-          xf[b][2 * w + 1] = __builtin_bit_cast(
-              half8_t, make_uint4(__builtin_amdgcn_perm(v0.z, v0.x, kHi), __builtin_amdgcn_perm(v1.z, v1.x, kHi),
-                                  __builtin_amdgcn_perm(v0.w, v0.y, kHi), __builtin_amdgcn_perm(v1.w, v1.y, kHi)));
-        }
-      }
-    return;
-  }
+// The lane's token operand for token t (a padding column of the tile takes
+// some valid token's row: the matrix product keeps columns apart and padding
+// columns are never stored).
+template <int NBL>
+__device__ inline void load_xop(const uint16_t* xs, int H, int t, int wave, int c, half8_t (&xf)[NBL][4]) {
+  const uint4* row = reinterpret_cast<const uint4*>(xs) + (uint32_t)(t * (H / 8) + wave * (H / 64) + c);
 #pragma unroll
   for (int b = 0; b < NBL; ++b)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint4 v = xr[b][kk];
-      xf[b][kk] = XBF16 ? __builtin_bit_cast(half8_t, make_uint4(pack_half2(bf16_lo(v.x), bf16_lo(v.y)),
-                                                                 pack_half2(bf16_hi(v.x), bf16_hi(v.y)),
-                                                                 pack_half2(bf16_lo(v.z), bf16_lo(v.w)),
-                                                                 pack_half2(bf16_hi(v.z), bf16_hi(v.w))))
-                        : __builtin_bit_cast(half8_t, v);
-    }
+    for (int kk = 0; kk < 4; ++kk) xf[b][kk] = __builtin_bit_cast(half8_t, row[4 * (4 * b + kk)]);
 }
 
 // One row group: the wave's partial gate and up tiles into red (gate, then
@@ -279,7 +234,7 @@ __device__ inline void gu_finish(const float (&red)[kBWaves][2][16][17], int j, 
   *dst = pack_half2(silu_mul(ga, ua), silu_mul(gb, ub));
 }
 
-template <int Q, int NBL, bool XBF16>
+template <int Q, int NBL>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void bat_gateup(Experts ex, FfnArgs a) {
   constexpr int R = kGuRows;
@@ -313,8 +268,8 @@ void bat_gateup(Experts ex, FfnArgs a) {
     return load_wrow_at<Q, NBL>(ex, mat0 + (size_t)(16 * (R * it.chunk + j)) * (H / 32), lane_blk);
   };
 
-  // raw activations of the item's token group for the lane's token
-  auto load_x = [&](const BatItem& it, uint4 (&xr)[NBL][4]) {
+  // the token operand of the item's token group
+  auto load_x = [&](const BatItem& it, half8_t (&xf)[NBL][4]) {
     const int m = min(16 * it.tg + r16, it.M - 1), slot = it.slot0 + m;  // padding: the last token
     int t;
     if (use_tab) {
@@ -323,33 +278,21 @@ void bat_gateup(Experts ex, FfnArgs a) {
       t = token_of(a.perm[slot], a.T, a.k);
       t = (unsigned)t < (unsigned)a.T ? t : 0;
     }
-    load_xraw<NBL, XBF16>(a, H, t, kb0, xr);
+    load_xop<NBL>(a.x16, H, t, wave, lane >> 4, xf);
   };
 
   // first item: activations requested first, so its first row group can start
   // while the second one's weights are still in flight
   BatItem it = bat_item_seq(base, off, E_tot, NC, item);
   half8_t xf[NBL][4];
-  WRow<NBL> ga, ua, gb, ub;
-  {
-    uint4 xr[NBL][4];
-    load_x(it, xr);
-    ga = wrow(it, 0, blk_gate(ex, it.e));
-    ua = wrow(it, 0, blk_up(ex, it.e));
-    gb = wrow(it, 1, blk_gate(ex, it.e));
-    ub = wrow(it, 1, blk_up(ex, it.e));
-    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
-    xop_of<Q, NBL, XBF16>(xr, xf);
-  }
+  load_x(it, xf);
+  WRow<NBL> ga = wrow(it, 0, blk_gate(ex, it.e)), ua = wrow(it, 0, blk_up(ex, it.e));
+  WRow<NBL> gb = wrow(it, 1, blk_gate(ex, it.e)), ub = wrow(it, 1, blk_up(ex, it.e));
   bool new_group = false;
   int done = 0;
   for (;;) {
     set_prio_by_progress(done++);
-    if (new_group) {
-      uint4 xr[NBL][4];
-      load_x(it, xr);
-      xop_of<Q, NBL, XBF16>(xr, xf);
-    }
+    if (new_group) load_x(it, xf);
     const int next = item + 1;
     const bool more = next < item_end;
     BatItem nx = it;
@@ -561,22 +504,16 @@ hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   const dim3 ggu((unsigned)(gu_items < cap_gu ? gu_items : cap_gu));
   const dim3 gdn((unsigned)(dn_items < cap_dn ? dn_items : cap_dn));
   const size_t map = bat_map_bytes(ex.E_tot);
-  const bool xbf16 = a.xdtype != 0;
-  if (!xbf16) {
-    const hipError_t e = launch_x16(ex, a, s);
-    if (e != hipSuccess) return e;
+  if (!a.xs_ready) {
+    const long n = (long)a.T * ex.H / 8;
+    const int xg = (int)(n / 256 + 1 < 1024 ? n / 256 + 1 : 1024);
+    MOE_LAUNCH("bat_xs", s, bat_xs, dim3(xg), dim3(256), 0, s, batch_xs_job(ex, a.x, a.xdtype, a.T, a.x16));
   }
-#define MOE_BAT_GU(NBL)                                                                              \
-  do {                                                                                             \
-    if (xbf16) MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, NBL, true>), ggu, dim3(kBThreads), map, s, ex, a); \
-    else MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, NBL, false>), ggu, dim3(kBThreads), map, s, ex, a);     \
-  } while (0)
   switch (ex.H / 1024) {
-    case 1: MOE_BAT_GU(1); break;
-    case 2: MOE_BAT_GU(2); break;
+    case 1: MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, 1>), ggu, dim3(kBThreads), map, s, ex, a); break;
+    case 2: MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, 2>), ggu, dim3(kBThreads), map, s, ex, a); break;
     default: return hipErrorInvalidValue;
   }
-#undef MOE_BAT_GU
   switch (ex.I / 128) {
     case 2: MOE_LAUNCH("bat_down", s, (bat_down<Q, 2>), gdn, dim3(kBThreads), map, s, ex, a); break;
     case 4: MOE_LAUNCH("bat_down", s, (bat_down<Q, 4>), gdn, dim3(kBThreads), map, s, ex, a); break;
@@ -590,6 +527,10 @@ hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
 bool batch_supported(int H, int I) {
   return (H == 1024 || H == 2048) && (I == 256 || I == 512) && H % (16 * kDnRows * kBWaves) == 0 &&
          I % (16 * kGuRows) == 0 && I <= kBMaxI;
+}
+
+XsJob batch_xs_job(const Experts& ex, const void* x, int xdtype, int T, uint16_t* x16) {
+  return XsJob{x, xdtype != 0, ex.qtype, ex.H, T, reinterpret_cast<uint4*>(x16)};
 }
 
 hipError_t launch_batch(const Experts& ex, const FfnArgs& a, hipStream_t s) {

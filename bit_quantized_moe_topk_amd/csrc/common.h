@@ -84,12 +84,16 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, f
                        hipStream_t s);
 
 size_t group_scratch_bytes(int T, int k, int E);
+// xj (optional): the small-batch activation layout to write in the same
+// launch when the grouping runs in one workgroup; *xs_done tells whether it did.
+struct XsJob;
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared, int32_t* counts,
                         int32_t* offsets, int32_t* perm, int32_t* slot_of, void* scratch,
-                        hipStream_t s);
+                        hipStream_t s, const XsJob* xj = nullptr, bool* xs_done = nullptr);
 hipError_t launch_route_group(const float* logits, int T, int E, int k, int has_shared, int32_t* idx,
                               float* gates, int32_t* counts, int32_t* offsets, int32_t* perm,
-                              int32_t* slot_of, void* scratch, hipStream_t s);
+                              int32_t* slot_of, void* scratch, hipStream_t s,
+                              const XsJob* xj = nullptr, bool* xs_done = nullptr);
 
 // FFN: check mode (fp32) and fast mode; both read a grouping and write y.
 struct FfnArgs {
@@ -106,7 +110,8 @@ struct FfnArgs {
   int out_f32;     // y is float32
   int gmax;        // GEMV token limit (0: every expert takes the MFMA tiles)
   void* h;         // [A][I] intermediate (fp32 check; bf16 GEMV / fp16 MFMA rows fast)
-  uint16_t* x16;   // [T][H] fp16 copy of x (fast mode, MFMA tiles)
+  uint16_t* x16;   // [T][H] fp16 copy of x (fast mode: MFMA tiles; small-batch layout below 256 tokens)
+  int xs_ready;    // x16 already holds the small-batch layout
   float* o;        // [A][H] fp32 gate-scaled expert outputs (check mode; fast, few tokens)
   uint16_t* ob;    // [A][H] bf16 gate-scaled expert outputs (fast, many tokens)
 };
@@ -138,6 +143,8 @@ hipError_t launch_x16(const Experts& ex, const FfnArgs& a, hipStream_t s);
 // per-slot outputs.
 bool batch_supported(int H, int I);
 hipError_t launch_batch(const Experts& ex, const FfnArgs& a, hipStream_t s);
+// The layout request for the small-batch kernels' activations (into x16).
+XsJob batch_xs_job(const Experts& ex, const void* x, int xdtype, int T, uint16_t* x16);
 // Writes the tiled copy of ex's planes (t_codes, t_dm, t_hi must be set).
 hipError_t launch_tile_weights(const Experts& ex, hipStream_t s);
 hipError_t launch_combine(const Experts& ex, const FfnArgs& a, hipStream_t s);

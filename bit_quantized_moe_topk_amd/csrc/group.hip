@@ -13,6 +13,7 @@
 // Order inside an expert is therefore ascending id, identical on every run.
 // Small inputs run all three steps in one workgroup; large ones in 3 launches.
 #include "common.h"
+#include "batch_x.h"
 #include "sched.h"
 #include "topk.h"
 
@@ -112,11 +113,17 @@ __device__ inline void write_shared(int T, int k, int has_shared, int32_t* perm,
 }
 
 // All three steps in one workgroup: one wave per segment of seg_len ids
-// (nseg <= 16 segments).
+// (nseg <= 16 segments). Workgroups past the first, when the launch has them,
+// write the small-batch activation layout (xj) meanwhile.
 __global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ idx, int T, int k,
                                                     int E, int has_shared, int nseg, int seg_len,
                                                     int32_t* counts, int32_t* offsets,
-                                                    int32_t* perm, int32_t* slot_of) {
+                                                    int32_t* perm, int32_t* slot_of, XsJob xj) {
+  if (blockIdx.x > 0) {
+    xs_write(xj.x, xj.xbf16, xj.q, xj.H, (long)(blockIdx.x - 1) * blockDim.x + threadIdx.x,
+             (long)xj.T * xj.H / 8, (long)(gridDim.x - 1) * blockDim.x, xj.xs);
+    return;
+  }
   extern __shared__ int lds[];  // [E * nseg] bases, then [16] wave totals
   int* hist = lds;
   int* tmp = lds + E * nseg;
@@ -331,15 +338,25 @@ size_t group_scratch_bytes(int T, int k, int E) {
 
 hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared, int32_t* counts,
                         int32_t* offsets, int32_t* perm, int32_t* slot_of, void* scratch,
-                        hipStream_t s) {
+                        hipStream_t s, const XsJob* xj, bool* xs_done) {
   const int nseg = nseg_of(T, k);
+  if (xs_done) *xs_done = false;
   if (use_fused(T, k, E)) {
     int seg_len = kSeg;
     const int nf = small_segments(T * k, E, 16, 16384 - 16, seg_len);
     const size_t lds = ((size_t)E * nf + 16) * sizeof(int);
     const int threads = 64 * (nf > 0 ? nf : 1);
-    MOE_LAUNCH("group_fused", s, group_fused, dim3(1), dim3(threads), lds, s, idx, T, k, E, has_shared, nf,
-               seg_len, counts, offsets, perm, slot_of);
+    XsJob job{};
+    int grid = 1;
+    if (xj && xj->xs && xj->T > 0) {
+      job = *xj;
+      const long n = (long)xj->T * xj->H / 8;
+      const long g = (n + threads - 1) / threads;
+      grid = 1 + (int)(g < 256 ? g : 256);
+      if (xs_done) *xs_done = true;
+    }
+    MOE_LAUNCH("group_fused", s, group_fused, dim3(grid), dim3(threads), lds, s, idx, T, k, E, has_shared, nf,
+               seg_len, counts, offsets, perm, slot_of, job);
     return hipGetLastError();
   }
   int* hist = static_cast<int*>(scratch);
@@ -356,7 +373,9 @@ hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared,
 
 hipError_t launch_route_group(const float* logits, int T, int E, int k, int has_shared, int32_t* idx,
                               float* gates, int32_t* counts, int32_t* offsets, int32_t* perm,
-                              int32_t* slot_of, void* scratch, hipStream_t s) {
+                              int32_t* slot_of, void* scratch, hipStream_t s, const XsJob* xj,
+                              bool* xs_done) {
+  if (xs_done) *xs_done = false;
   if (small_route_group(T, k, E)) {
     const int per = (E + 63) / 64;
     if (per <= 1) return launch_rg<1>(logits, T, E, k, has_shared, idx, gates, counts, offsets, perm, slot_of, s);
@@ -368,7 +387,7 @@ hipError_t launch_route_group(const float* logits, int T, int E, int k, int has_
   }
   hipError_t e = launch_topk(logits, T, E, k, idx, gates, s);
   if (e != hipSuccess) return e;
-  return launch_group(idx, T, k, E, has_shared, counts, offsets, perm, slot_of, scratch, s);
+  return launch_group(idx, T, k, E, has_shared, counts, offsets, perm, slot_of, scratch, s, xj, xs_done);
 }
 
 }  // namespace moe
