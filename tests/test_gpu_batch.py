@@ -7,7 +7,10 @@ per expert and more than 64 tokens of one expert (h staged in chunks), both
 quantisations, H = 1024 / I = 256, float32 activations, no shared expert, a
 single token, a ragged batch and more slots than the LDS tables hold; two
 shapes outside those kernels run the GEMV kernels (experts with 1..4
-assignments) beside the matrix-core tiles.
+assignments) beside the matrix-core tiles. The activation layout of the
+small-batch kernels is written in three ways, each checked: by the FFN
+call's own grouping launch, by the whole-layer call's routing launch, and by
+a separate kernel when the caller brings the grouping.
 """
 import numpy as np
 import pytest
@@ -60,5 +63,39 @@ def test_batch_ffn_parity(name, kw, hot):
     assert torch.equal(y1, y2), "two runs differ"
     err = rel_l2_rows(y_to_f64(y1), oracle_rows(lay, idx_np, gates_np))
     log(f"[batch] {name}: max rel-L2 {err.max():.3e}  mean {err.mean():.3e}")
+    assert err.max() <= TOL_FAST
+    ex.close()
+
+
+LAYOUT_CASES = [
+    ("Q3 T=64 layer", dict(), "layer"),
+    ("Q2 T=37 f32 layer", dict(T=37, qtype=2, xdtype="f32"), "layer"),
+    ("Q3 T=9 layer (one-workgroup routing: separate layout kernel)", dict(T=9), "layer"),
+    ("Q3 T=64 caller grouping", dict(), "grouping"),
+    ("Q2 H=1024 I=256 T=20 f32 caller grouping", dict(T=20, H=1024, I=256, E=32, k=4, qtype=2, xdtype="f32"),
+     "grouping"),
+]
+
+
+@pytest.mark.parametrize("name,kw,how", LAYOUT_CASES, ids=[c[0] for c in LAYOUT_CASES])
+def test_batch_activation_layout_paths(name, kw, how):
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfg = CONFIGS[4].with_(**kw)
+    lay = make_layer(cfg, seed=37)
+    dev = upload(lay)
+    ex = experts_of(lay, dev)
+    idx_np, gates_np = oracle.route(lay["logits"], cfg.k)
+    log(f"[batch-layout] {name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} Q{cfg.qtype}")
+    if how == "layer":
+        idx, gates, y = moe.layer(dev["logits"], dev["x"], ex, cfg.k)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), idx_np)
+    else:
+        idx, gates, grp = moe.route_group(dev["logits"], cfg.k, bool(cfg.shared))
+        y = moe.ffn_q(dev["x"], ex, idx, gates, grouping=grp)
+        torch.cuda.synchronize()
+    err = rel_l2_rows(y_to_f64(y), oracle_rows(lay, idx_np, gates_np))
+    log(f"[batch-layout] {name}: max rel-L2 {err.max():.3e}")
     assert err.max() <= TOL_FAST
     ex.close()
