@@ -103,28 +103,23 @@ __device__ inline void write_offsets(const int* base, int nseg, int E, int T, in
   }
 }
 
-__device__ inline void write_shared(int T, int k, int has_shared, int32_t* perm, int32_t* slot_of) {
+// Identity slots of the shared expert, tokens t0, t0 + ts, ... (the caller's
+// threads split them).
+__device__ inline void write_shared(int T, int k, int has_shared, int32_t* perm, int32_t* slot_of,
+                                    int t0, int ts) {
   if (!has_shared) return;
   const int AR = T * k;
-  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
+  for (int t = t0; t < T; t += ts) {
     perm[AR + t] = AR + t;
     slot_of[AR + t] = AR + t;
   }
 }
 
 // All three steps in one workgroup: one wave per segment of seg_len ids
-// (nseg <= 16 segments). Workgroups past the first, when the launch has them,
-// write the small-batch activation layout (xj) meanwhile.
-__global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ idx, int T, int k,
-                                                    int E, int has_shared, int nseg, int seg_len,
-                                                    int32_t* counts, int32_t* offsets,
-                                                    int32_t* perm, int32_t* slot_of, XsJob xj) {
-  if (blockIdx.x > 0) {
-    xs_write(xj.x, xj.xbf16, xj.q, xj.H, (long)(blockIdx.x - 1) * blockDim.x + threadIdx.x,
-             (long)xj.T * xj.H / 8, (long)(gridDim.x - 1) * blockDim.x, xj.xs);
-    return;
-  }
-  extern __shared__ int lds[];  // [E * nseg] bases, then [16] wave totals
+// (nseg <= 16 segments; lds holds E * nseg + 16 ints).
+__device__ inline void group_one_wg(const int32_t* __restrict__ idx, int T, int k, int E, int has_shared,
+                                    int nseg, int seg_len, int32_t* counts, int32_t* offsets,
+                                    int32_t* perm, int32_t* slot_of, int* lds) {
   int* hist = lds;
   int* tmp = lds + E * nseg;
   const int AR = T * k;
@@ -138,7 +133,22 @@ __global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ 
   write_offsets(hist, nseg, E, T, k, has_shared, counts, offsets);
   __syncthreads();  // the bases are read above before the scatter advances them
   if (seg < nseg) wave_scatter<kBatchSmall>(idx, f0, f1, E, hist + seg, nseg, perm, slot_of);
-  write_shared(T, k, has_shared, perm, slot_of);
+  write_shared(T, k, has_shared, perm, slot_of, threadIdx.x, blockDim.x);
+}
+
+// group_one_wg in the first workgroup; workgroups past the first, when the
+// launch has them, write the small-batch activation layout (xj) meanwhile.
+__global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ idx, int T, int k,
+                                                    int E, int has_shared, int nseg, int seg_len,
+                                                    int32_t* counts, int32_t* offsets,
+                                                    int32_t* perm, int32_t* slot_of, XsJob xj) {
+  if (blockIdx.x > 0) {
+    xs_write(xj.x, xj.xbf16, xj.q, xj.H, (long)(blockIdx.x - 1) * blockDim.x + threadIdx.x,
+             (long)xj.T * xj.H / 8, (long)(gridDim.x - 1) * blockDim.x, xj.xs);
+    return;
+  }
+  extern __shared__ int lds[];  // [E * nseg] bases, then [16] wave totals
+  group_one_wg(idx, T, k, E, has_shared, nseg, seg_len, counts, offsets, perm, slot_of, lds);
 }
 
 // Top-k and grouping in one workgroup for small batches (a decode verify
@@ -170,7 +180,7 @@ __global__ __launch_bounds__(1024) void route_group_small(const float* __restric
   write_offsets(hist, nseg, E, T, k, has_shared, counts, offsets);
   __syncthreads();  // the bases are read above before the scatter advances them
   if (wv < nseg) wave_scatter<1>(lidx, f0, f1, E, hist + wv, nseg, perm, slot_of);
-  write_shared(T, k, has_shared, perm, slot_of);
+  write_shared(T, k, has_shared, perm, slot_of, threadIdx.x, blockDim.x);
 }
 
 // Large inputs, step 1: per-segment counts into hist[seg * E + e] (global,
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(256) void group_count(const int32_t* __restrict__ i
   __syncthreads();
   if (seg < nseg)
     for (int e = lane; e < E; e += 64) hist[(size_t)seg * E + e] = h[e];
-  write_shared(T, k, has_shared, perm, slot_of);
+  write_shared(T, k, has_shared, perm, slot_of, blockIdx.x * blockDim.x + threadIdx.x, gridDim.x * blockDim.x);
 }
 
 // Step 2: one workgroup turns hist into exclusive bases in (expert, segment)
