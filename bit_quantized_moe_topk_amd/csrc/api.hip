@@ -197,6 +197,24 @@ inline bool batch_path(const Experts& d, int T, int mode) {
   return mode == MOE_FAST && T < moe::kGemvBatchLimit && moe::batch_supported(d.H, d.I);
 }
 
+// GEMV token limit of fast mode outside the small-batch path: from a few
+// hundred tokens on, experts with few assignments ride in the persistent
+// matrix-core grid, where their weight reads overlap the other tiles'
+// arithmetic; a separate GEMV pass would run on its own.
+inline int gemv_max(const Experts& d, int T) {
+  const bool small_batch = T < moe::kGemvBatchLimit || !moe::mfma_supported(d.H, d.I);
+  return moe::gemv_supported(d.H, d.I) && small_batch ? moe::kGemvMaxTokens : 0;
+}
+
+// The fp16 activation copy the FFN's matrix-core kernels read, as the Q of an
+// XsJob: the small-batch layout (2, 3), the prefill tiles' copy (0), or none
+// (-1: check mode, or GEMV kernels only).
+inline int x16_kind(const Experts& d, int T, int mode) {
+  if (mode != MOE_FAST) return -1;
+  if (batch_path(d, T, mode)) return d.qtype;
+  return T > gemv_max(d, T) ? 0 : -1;
+}
+
 // moe_ffn_q; xs_ready: the workspace's x16 already holds the small-batch
 // activation layout (written by the caller's grouping launch).
 int ffn_q_impl(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, const int32_t* idx,
@@ -238,11 +256,12 @@ int ffn_q_impl(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, 
     int32_t* o = reinterpret_cast<int32_t*>(at(ws, L.offsets));
     int32_t* p = reinterpret_cast<int32_t*>(at(ws, L.perm));
     int32_t* so = reinterpret_cast<int32_t*>(at(ws, L.slot_of));
-    // the small-batch activation layout rides in the one-workgroup grouping launch
-    const moe::XsJob xj = moe::batch_xs_job(d, x, xdtype, T, a.x16);
+    // the fp16 activation copy rides in the grouping launch
+    const int kind = x16_kind(d, T, mode);
+    const moe::XsJob xj = moe::xs_job(kind, d.H, x, xdtype, T, a.x16);
     bool xs_done = false;
     hipError_t e = moe::launch_group(idx, T, k, d.E, d.has_shared, c, o, p, so, at(ws, L.group), s,
-                                     batch_path(d, T, mode) ? &xj : nullptr, &xs_done);
+                                     kind >= 0 ? &xj : nullptr, &xs_done);
     if (e != hipSuccess) return MOE_ERR_HIP;
     a.xs_ready = xs_done;
     a.counts = c;
@@ -257,14 +276,10 @@ int ffn_q_impl(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, 
   if (mode == MOE_CHECK_F32) {
     e = moe::launch_ffn_check(d, a, s);
   } else {
-    // From a few hundred tokens on, experts with few assignments ride in the
-    // persistent matrix-core grid, where their weight reads overlap the other
-    // tiles' arithmetic; a separate GEMV pass would run on its own.
     if (batch_path(d, T, mode)) {
       e = moe::launch_batch(d, a, s);
     } else {
-      const bool small_batch = T < moe::kGemvBatchLimit || !moe::mfma_supported(d.H, d.I);
-      a.gmax = moe::gemv_supported(d.H, d.I) && small_batch ? moe::kGemvMaxTokens : 0;
+      a.gmax = gemv_max(d, T);
       e = moe::launch_ffn_fast(d, a, s);
     }
   }
@@ -341,13 +356,13 @@ int moe_layer(const float* logits, const void* x, int32_t xdtype, int32_t T, con
   int32_t* o = reinterpret_cast<int32_t*>(at(ws, L.offsets));
   int32_t* p = reinterpret_cast<int32_t*>(at(ws, L.perm));
   int32_t* so = reinterpret_cast<int32_t*>(at(ws, L.slot_of));
-  // the small-batch activation layout rides in the routing's one-workgroup
-  // grouping launch when there is one
+  // the FFN's fp16 activation copy rides in the routing's grouping launch
   const FfnLayout F = ffn_layout(d, T, k, mode);
-  const moe::XsJob xj = moe::batch_xs_job(d, x, xdtype, T, reinterpret_cast<uint16_t*>(at(ws, L.ffn + F.x16)));
+  const int kind = x16_kind(d, T, mode);
+  const moe::XsJob xj = moe::xs_job(kind, d.H, x, xdtype, T, reinterpret_cast<uint16_t*>(at(ws, L.ffn + F.x16)));
   bool xs_done = false;
   const hipError_t e = moe::launch_route_group(logits, T, d.E, k, d.has_shared, idx, gates, c, o, p, so,
-                                               at(ws, L.group), s, batch_path(d, T, mode) ? &xj : nullptr,
+                                               at(ws, L.group), s, kind >= 0 ? &xj : nullptr,
                                                &xs_done);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return ffn_q_impl(x, xdtype, T, ex, idx, gates, k, c, o, p, so, y, mode, at(ws, L.ffn),

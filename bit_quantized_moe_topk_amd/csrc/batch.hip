@@ -507,7 +507,7 @@ hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   if (!a.xs_ready) {
     const long n = (long)a.T * ex.H / 8;
     const int xg = (int)(n / 256 + 1 < 1024 ? n / 256 + 1 : 1024);
-    MOE_LAUNCH("bat_xs", s, bat_xs, dim3(xg), dim3(256), 0, s, batch_xs_job(ex, a.x, a.xdtype, a.T, a.x16));
+    MOE_LAUNCH("bat_xs", s, bat_xs, dim3(xg), dim3(256), 0, s, xs_job(ex.qtype, ex.H, a.x, a.xdtype, a.T, a.x16));
   }
   switch (ex.H / 1024) {
     case 1: MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, 1>), ggu, dim3(kBThreads), map, s, ex, a); break;
@@ -529,8 +529,8 @@ bool batch_supported(int H, int I) {
          I % (16 * kGuRows) == 0 && I <= kBMaxI;
 }
 
-XsJob batch_xs_job(const Experts& ex, const void* x, int xdtype, int T, uint16_t* x16) {
-  return XsJob{x, xdtype != 0, ex.qtype, ex.H, T, reinterpret_cast<uint4*>(x16)};
+XsJob xs_job(int q, int H, const void* x, int xdtype, int T, uint16_t* x16) {
+  return XsJob{x, xdtype != 0, q, H, T, q < 0 ? nullptr : reinterpret_cast<uint4*>(x16)};
 }
 
 hipError_t launch_batch(const Experts& ex, const FfnArgs& a, hipStream_t s) {

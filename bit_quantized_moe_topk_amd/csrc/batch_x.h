@@ -1,5 +1,7 @@
-// Activation layout of the small-batch gate/up kernel (header-only; batch.hip
-// reads it, and the grouping launch can write it beside its own work).
+// fp16 activation copies (header-only): the small-batch gate/up kernel's lane
+// layout, and the row-major copy of the prefill tiles; batch.hip and
+// mfma.hip read them, and the grouping launches can write them beside their
+// own work.
 #pragma once
 
 #include "common.h"
@@ -80,7 +82,25 @@ __device__ inline uint4 xs_chunk(const void* x, int H, int t, int j) {
                     pack_half2(f[6], f[7]));
 }
 
-// Chunks [j0, n) step js of the layout for T rows (n = T H / 8), written to xs.
+// Row-major fp16 copy of the prefill tiles: 16-byte chunk i holds elements
+// 8 i .. 8 i + 7 of the flat [T][H] activations, each group of four as
+// 0, 2, 1, 3 (their K order).
+template <bool XBF16>
+__device__ inline uint4 x16_chunk(const void* x, long i) {
+  if constexpr (XBF16) {
+    const uint4 v = static_cast<const uint4*>(x)[i];
+    return make_uint4(pack_half2(bf16_lo(v.x), bf16_lo(v.y)), pack_half2(bf16_hi(v.x), bf16_hi(v.y)),
+                      pack_half2(bf16_lo(v.z), bf16_lo(v.w)), pack_half2(bf16_hi(v.z), bf16_hi(v.w)));
+  } else {
+    const float4* src = static_cast<const float4*>(x) + 2 * i;
+    const float4 f0 = src[0], f1 = src[1];
+    return make_uint4(pack_half2(f0.x, f0.z), pack_half2(f0.y, f0.w), pack_half2(f1.x, f1.z),
+                      pack_half2(f1.y, f1.w));
+  }
+}
+
+// Chunks [j0, n) step js (n = T H / 8) of the copy named by Q, written to xs:
+// Q = 2, 3 the small-batch layout for that code width, Q = 0 the prefill copy.
 __device__ inline void xs_write(const void* x, int xbf16, int Q, int H, long j0, long n, long js,
                                 uint4* xs) {
   const int per_row = H / 8;
@@ -88,12 +108,13 @@ __device__ inline void xs_write(const void* x, int xbf16, int Q, int H, long j0,
     const int t = (int)(i / per_row), j = (int)(i % per_row);
     uint4 v;
     if (Q == 3) v = xbf16 ? xs_chunk<3, true>(x, H, t, j) : xs_chunk<3, false>(x, H, t, j);
-    else v = xbf16 ? xs_chunk<2, true>(x, H, t, j) : xs_chunk<2, false>(x, H, t, j);
+    else if (Q == 2) v = xbf16 ? xs_chunk<2, true>(x, H, t, j) : xs_chunk<2, false>(x, H, t, j);
+    else v = xbf16 ? x16_chunk<true>(x, i) : x16_chunk<false>(x, i);
     xs[i] = v;
   }
 }
 
-// A request to write the layout (xs == nullptr: none).
+// A request to write one of the copies (xs == nullptr: none).
 struct XsJob {
   const void* x;
   int xbf16, q, H, T;

@@ -111,7 +111,7 @@ struct FfnArgs {
   int gmax;        // GEMV token limit (0: every expert takes the MFMA tiles)
   void* h;         // [A][I] intermediate (fp32 check; bf16 GEMV / fp16 MFMA rows fast)
   uint16_t* x16;   // [T][H] fp16 copy of x (fast mode: MFMA tiles; small-batch layout below 256 tokens)
-  int xs_ready;    // x16 already holds the small-batch layout
+  int xs_ready;    // x16 already holds the copy the FFN's matrix-core kernels read
   float* o;        // [A][H] fp32 gate-scaled expert outputs (check mode; fast, few tokens)
   uint16_t* ob;    // [A][H] bf16 gate-scaled expert outputs (fast, many tokens)
 };
@@ -143,8 +143,9 @@ hipError_t launch_x16(const Experts& ex, const FfnArgs& a, hipStream_t s);
 // per-slot outputs.
 bool batch_supported(int H, int I);
 hipError_t launch_batch(const Experts& ex, const FfnArgs& a, hipStream_t s);
-// The layout request for the small-batch kernels' activations (into x16).
-XsJob batch_xs_job(const Experts& ex, const void* x, int xdtype, int T, uint16_t* x16);
+// A request for the fp16 activation copy into x16: q = 2, 3 the small-batch
+// layout for that code width, 0 the prefill tiles' copy, -1 none.
+XsJob xs_job(int q, int H, const void* x, int xdtype, int T, uint16_t* x16);
 // Writes the tiled copy of ex's planes (t_codes, t_dm, t_hi must be set).
 hipError_t launch_tile_weights(const Experts& ex, hipStream_t s);
 hipError_t launch_combine(const Experts& ex, const FfnArgs& a, hipStream_t s);

@@ -185,9 +185,15 @@ __global__ __launch_bounds__(1024) void route_group_small(const float* __restric
 
 // Large inputs, step 1: per-segment counts into hist[seg * E + e] (global,
 // segment-major so that every step's accesses are coalesced).
+// Workgroups from nb on write the activation copy (xj) meanwhile.
 __global__ __launch_bounds__(256) void group_count(const int32_t* __restrict__ idx, int T, int k,
                                                    int E, int has_shared, int nseg, int* hist,
-                                                   int32_t* perm, int32_t* slot_of) {
+                                                   int32_t* perm, int32_t* slot_of, int nb, XsJob xj) {
+  if ((int)blockIdx.x >= nb) {
+    xs_write(xj.x, xj.xbf16, xj.q, xj.H, (long)(blockIdx.x - nb) * 256 + threadIdx.x,
+             (long)xj.T * xj.H / 8, (long)(gridDim.x - nb) * 256, xj.xs);
+    return;
+  }
   extern __shared__ int lds[];  // [4][E]
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int* h = lds + w * E;
@@ -202,7 +208,7 @@ __global__ __launch_bounds__(256) void group_count(const int32_t* __restrict__ i
   __syncthreads();
   if (seg < nseg)
     for (int e = lane; e < E; e += 64) hist[(size_t)seg * E + e] = h[e];
-  write_shared(T, k, has_shared, perm, slot_of, blockIdx.x * blockDim.x + threadIdx.x, gridDim.x * blockDim.x);
+  write_shared(T, k, has_shared, perm, slot_of, blockIdx.x * blockDim.x + threadIdx.x, nb * blockDim.x);
 }
 
 // Step 2: one workgroup turns hist into exclusive bases in (expert, segment)
@@ -372,8 +378,17 @@ hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared,
   int* hist = static_cast<int*>(scratch);
   const int blocks = (nseg + 3) / 4;
   const size_t lds = (size_t)4 * E * sizeof(int);
-  MOE_LAUNCH("group_count", s, group_count, dim3(blocks), dim3(256), lds, s, idx, T, k, E, has_shared, nseg,
-                     hist, perm, slot_of);
+  XsJob job{};
+  int grid = blocks;
+  if (xj && xj->xs && xj->T > 0) {
+    job = *xj;
+    const long n = (long)xj->T * xj->H / 8;
+    const long g = (n + 255) / 256;
+    grid += (int)(g < 1024 ? g : 1024);
+    if (xs_done) *xs_done = true;
+  }
+  MOE_LAUNCH("group_count", s, group_count, dim3(grid), dim3(256), lds, s, idx, T, k, E, has_shared, nseg,
+                     hist, perm, slot_of, blocks, job);
   MOE_LAUNCH("group_scan", s, group_scan, dim3(1), dim3(1024), 0, s, T, k, E, has_shared, nseg, hist,
                      counts, offsets);
   MOE_LAUNCH("group_scatter", s, group_scatter, dim3(nseg), dim3(256), lds, s, idx, T, k, E, nseg, hist,

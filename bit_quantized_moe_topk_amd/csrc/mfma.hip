@@ -515,8 +515,10 @@ __global__ __launch_bounds__(256) void tile_weights(Experts ex, long n) {
 
 template <int Q>
 hipError_t launch_q(const Experts& ex, const FfnArgs& a, int grid, hipStream_t s) {
-  const hipError_t xe = launch_x16(ex, a, s);
-  if (xe != hipSuccess) return xe;
+  if (!a.xs_ready) {
+    const hipError_t xe = launch_x16(ex, a, s);
+    if (xe != hipSuccess) return xe;
+  }
   const bool g8 = ex.I % tile_rows<false, 8>() == 0, d8 = ex.H % tile_rows<true, 8>() == 0;
 #define MOE_TILES(NAME, DOWN, NW)                                                              \
   do {                                                                                         \
