@@ -99,3 +99,31 @@ def test_batch_activation_layout_paths(name, kw, how):
     log(f"[batch-layout] {name}: max rel-L2 {err.max():.3e}")
     assert err.max() <= TOL_FAST
     ex.close()
+
+
+def test_batch_layer_workspace_reuse():
+    """One workspace through layer calls of different batches, then the first
+    again: every call matches the oracle and the repeat is bit-identical
+    (nothing of an earlier call's copy, grouping or counters leaks)."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfgs = [CONFIGS[4], CONFIGS[4].with_(T=37, qtype=3), CONFIGS[4].with_(T=9)]
+    lays = [make_layer(c, seed=41 + i) for i, c in enumerate(cfgs)]
+    devs = [upload(l) for l in lays]
+    exs = [experts_of(l, d) for l, d in zip(lays, devs)]
+    nbytes = max(int(moe.lib().moe_layer_workspace_size(ex.handle, c.T, c.k, 0)) for ex, c in zip(exs, cfgs))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    outs = []
+    for i in [0, 1, 2, 0]:
+        c = cfgs[i]
+        log(f"[batch-reuse] call T={c.T} Q{c.qtype}")
+        idx, gates, y = moe.layer(devs[i]["logits"], devs[i]["x"], exs[i], c.k, workspace=ws)
+        torch.cuda.synchronize()
+        idx_np, gates_np = oracle.route(lays[i]["logits"], c.k)
+        assert np.array_equal(idx.cpu().numpy(), idx_np)
+        err = rel_l2_rows(y_to_f64(y), oracle_rows(lays[i], idx_np, gates_np))
+        assert err.max() <= TOL_FAST, (c.T, err.max())
+        outs.append(y.clone())
+    assert torch.equal(outs[0], outs[3]), "repeat of the first call differs"
+    for ex in exs:
+        ex.close()
