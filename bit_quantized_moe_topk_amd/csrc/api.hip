@@ -22,11 +22,14 @@ inline int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_H
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Byte layout of the moe_ffn_q workspace.
-//   grouping (used when the caller passes none) | h [A][I] | o [A][H]
-// h: fp32 in check mode, 16-bit in fast mode. o: gate-scaled expert outputs
-// per assignment, fp32 in check mode and for few tokens, bf16 otherwise.
+//   grouping (used when the caller passes none) | h [A][I] | x16 [T][H] |
+//   xe [T] | o [A][H]
+// h: fp32 in check mode, bf16 in fast mode. x16: the fp16 activation copy of
+// the matrix-core kernels, xe its per-token exponents. o: gate-scaled expert
+// outputs per assignment, fp32 in check mode and for few tokens, bf16
+// otherwise.
 struct FfnLayout {
-  size_t counts, offsets, perm, slot_of, group, h, x16, o, total;
+  size_t counts, offsets, perm, slot_of, group, h, x16, xe, o, total;
   bool o_f32;
 };
 
@@ -41,6 +44,7 @@ FfnLayout ffn_layout(const Experts& ex, int T, int k, int mode) {
   L.group = off;   off = align_up(off + moe::group_scratch_bytes(T, k, ex.E));
   L.h = off;       off = align_up(off + (mode == MOE_CHECK_F32 ? 4 : 2) * A * (size_t)ex.I);
   L.x16 = off;     off = align_up(off + (mode == MOE_CHECK_F32 ? 0 : 2) * (size_t)T * ex.H);
+  L.xe = off;      off = align_up(off + (mode == MOE_CHECK_F32 ? 0 : sizeof(int32_t)) * (size_t)T);
   L.o_f32 = mode == MOE_CHECK_F32 || T <= moe::kF32SlotMaxTokens;
   L.o = off;       off = align_up(off + (L.o_f32 ? 4 : 2) * A * (size_t)ex.H);
   L.total = off;
@@ -245,6 +249,7 @@ int ffn_q_impl(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, 
   a.y = y;
   a.h = at(ws, L.h);
   a.x16 = reinterpret_cast<uint16_t*>(at(ws, L.x16));
+  a.xe = reinterpret_cast<int32_t*>(at(ws, L.xe));
   a.xs_ready = xs_ready;
   if (given == 4) {
     a.counts = counts;
@@ -258,7 +263,7 @@ int ffn_q_impl(const void* x, int32_t xdtype, int32_t T, const moe_experts* ex, 
     int32_t* so = reinterpret_cast<int32_t*>(at(ws, L.slot_of));
     // the fp16 activation copy rides in the grouping launch
     const int kind = x16_kind(d, T, mode);
-    const moe::XsJob xj = moe::xs_job(kind, d.H, x, xdtype, T, a.x16);
+    const moe::XsJob xj = moe::xs_job(kind, d.H, x, xdtype, T, a.x16, a.xe);
     bool xs_done = false;
     hipError_t e = moe::launch_group(idx, T, k, d.E, d.has_shared, c, o, p, so, at(ws, L.group), s,
                                      kind >= 0 ? &xj : nullptr, &xs_done);
@@ -359,7 +364,8 @@ int moe_layer(const float* logits, const void* x, int32_t xdtype, int32_t T, con
   // the FFN's fp16 activation copy rides in the routing's grouping launch
   const FfnLayout F = ffn_layout(d, T, k, mode);
   const int kind = x16_kind(d, T, mode);
-  const moe::XsJob xj = moe::xs_job(kind, d.H, x, xdtype, T, reinterpret_cast<uint16_t*>(at(ws, L.ffn + F.x16)));
+  const moe::XsJob xj = moe::xs_job(kind, d.H, x, xdtype, T, reinterpret_cast<uint16_t*>(at(ws, L.ffn + F.x16)),
+                                    reinterpret_cast<int32_t*>(at(ws, L.ffn + F.xe)));
   bool xs_done = false;
   const hipError_t e = moe::launch_route_group(logits, T, d.E, k, d.has_shared, idx, gates, c, o, p, so,
                                                at(ws, L.group), s, kind >= 0 ? &xj : nullptr,

@@ -17,10 +17,12 @@
 //               (deq16.h); the next item's first weights are requested while
 //               the last row groups compute (Q3 operands: deq16.h, "Q3
 //               through the FP8 conversion"). Each row group's eight partial
-//               tiles are summed in LDS in wave order, then SwiGLU; h is
-//               stored as fp16 in the MFMA K order.
+//               tiles are summed in LDS in wave order, then SwiGLU (each
+//               token's activation copy is scaled by 2^-e, xe, which the
+//               epilogue undoes); h is stored as bf16 in the MFMA K order.
 //   bat_down  : chunk = 128 rows of H (wave w: one group of 16 rows over all
-//               of K = I). The item's 16 h rows come into LDS (double-buffered
+//               of K = I), on bf16 operands (weights dequantised to bf16,
+//               bf16 h). The item's 16 h rows come into LDS (double-buffered
 //               across items, the next item's rows requested early); outputs
 //               are scaled by the routing gate and stored per assignment slot
 //               for the combine.
@@ -144,8 +146,7 @@ __device__ inline void set_prio_by_progress(int done) {
 }
 
 __global__ __launch_bounds__(256) void bat_xs(XsJob xj) {
-  xs_write(xj.x, xj.xbf16, xj.q, xj.H, blockIdx.x * 256L + threadIdx.x, (long)xj.T * xj.H / 8,
-           (long)gridDim.x * 256, xj.xs);
+  xs_write_rows(xj, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4);
 }
 
 // The lane's token operand for token t (a padding column of the tile takes
@@ -214,12 +215,21 @@ __device__ inline void gu_partial(const WRow<NBL>& wg, const WRow<NBL>& wu, cons
 // row group mod 4), so the extra work rotates over the waves.
 template <int Q>
 __device__ inline void gu_finish(const float (&red)[kBWaves][2][16][17], int j, const BatItem& it,
-                                 int row0, int I, uint16_t* h) {
+                                 int row0, int I, uint16_t* h, const int* tok, bool use_tab,
+                                 const FfnArgs& a, const int* xe_s) {
   const int rt = (int)threadIdx.x - 128 * (j & 3);
   if (rt < 0 || rt >= 128) return;
   const int pr = rt >> 4, t = rt & 15;
   const int m = 16 * it.tg + t;
   if (m >= it.M) return;
+  int tk;  // the slot's token: its activation row's exponent restores g and u
+  if (use_tab) {
+    tk = tok[it.slot0 + m];
+  } else {
+    tk = token_of(a.perm[it.slot0 + m], a.T, a.k);
+    tk = (unsigned)tk < (unsigned)a.T ? tk : 0;
+  }
+  const int e = xe_s[tk];
   const int ra = Q == 3 ? (pr >> 1) + 8 * (pr & 1) : 4 * (pr >> 1) + (pr & 1);
   const int rb = ra + (Q == 3 ? 4 : 2);
   float ga = 0.f, ua = 0.f, gb = 0.f, ub = 0.f;
@@ -231,7 +241,7 @@ __device__ inline void gu_finish(const float (&red)[kBWaves][2][16][17], int j, 
     ub += red[w][1][rb][t];
   }
   uint32_t* dst = reinterpret_cast<uint32_t*>(h + (size_t)(it.slot0 + m) * I + row0 + 2 * pr);
-  *dst = pack_half2(silu_mul(ga, ua), silu_mul(gb, ub));
+  *dst = pack_bf16x2(silu_mul_x(ga, ua, e), silu_mul_x(gb, ub, e));
 }
 
 template <int Q, int NBL>
@@ -242,16 +252,19 @@ void bat_gateup(Experts ex, FfnArgs a) {
   __shared__ BatMap bm;
   extern __shared__ int bat_dyn[];  // base, off (bat_map_bytes)
   __shared__ int tok[kBTab];
+  __shared__ int xe_s[kGemvBatchLimit];  // per-token exponents of the activation copy
   __shared__ float red[2][kBWaves][2][16][17];  // two buffers: wave, gate/up, row, token
   const int H = ex.H, I = ex.I, E_tot = ex.E_tot;
   const int A = a.T * (a.k + ex.has_shared);
   const bool use_tab = A <= kBTab;
   int* base = bat_dyn;
   int* off = bat_dyn + E_tot + 2;
+  const int xev = (int)threadIdx.x < a.T ? a.xe[threadIdx.x] : 0;  // T < kBThreads
   batmap_init<true>(bm, base, off, a, E_tot, use_tab, A, [&](int s, int asg) {
     const int t = token_of(asg, a.T, a.k);
     tok[s] = (unsigned)t < (unsigned)a.T ? t : 0;
   });
+  if ((int)threadIdx.x < a.T) xe_s[threadIdx.x] = xev;  // published by the loop's first barrier
   const int NC = I / (16 * R);
   const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
   // a run of consecutive items per workgroup
@@ -304,13 +317,13 @@ void bat_gateup(Experts ex, FfnArgs a) {
       ga = wrow(it, 2, blk_gate(ex, it.e));
       ua = wrow(it, 2, blk_up(ex, it.e));
       __syncthreads();
-      gu_finish<Q>(red[0], 0, it, row0, I, h);
+      gu_finish<Q>(red[0], 0, it, row0, I, h, tok, use_tab, a, xe_s);
       // row group 1 (set b) -> row group 3
       gu_partial<Q, NBL>(gb, ub, xf, red[1]);
       gb = wrow(it, 3, blk_gate(ex, it.e));
       ub = wrow(it, 3, blk_up(ex, it.e));
       __syncthreads();
-      gu_finish<Q>(red[1], 1, it, row0 + 16, I, h);
+      gu_finish<Q>(red[1], 1, it, row0 + 16, I, h, tok, use_tab, a, xe_s);
     }
     // row group R - 2 (set a) -> the next item's row group 0
     gu_partial<Q, NBL>(ga, ua, xf, red[0]);
@@ -319,7 +332,7 @@ void bat_gateup(Experts ex, FfnArgs a) {
       ua = wrow(nx, 0, blk_up(ex, nx.e));
     }
     __syncthreads();
-    gu_finish<Q>(red[0], R - 2, it, row0 + 16 * (R - 2), I, h);
+    gu_finish<Q>(red[0], R - 2, it, row0 + 16 * (R - 2), I, h, tok, use_tab, a, xe_s);
     // row group R - 1 (set b) -> the next item's row group 1
     gu_partial<Q, NBL>(gb, ub, xf, red[1]);
     if (more) {
@@ -327,7 +340,7 @@ void bat_gateup(Experts ex, FfnArgs a) {
       ub = wrow(nx, 1, blk_up(ex, nx.e));
     }
     __syncthreads();
-    gu_finish<Q>(red[1], R - 1, it, row0 + 16 * (R - 1), I, h);
+    gu_finish<Q>(red[1], R - 1, it, row0 + 16 * (R - 1), I, h, tok, use_tab, a, xe_s);
     if (!more) break;
     new_group = nx.e != it.e || nx.tg != it.tg;
     item = next;
@@ -337,30 +350,30 @@ void bat_gateup(Experts ex, FfnArgs a) {
 
 // --- down -------------------------------------------------------------------
 
-// One 16-row x 16-token down tile over all of K; two accumulators (step
-// parity) keep consecutive MFMAs independent.
+// One 16-row x 16-token down tile over all of K on bf16 operands (h is
+// bf16); two accumulators (step parity) keep consecutive MFMAs independent.
 template <int Q, int NBL>
-__device__ inline floatx4_t dn_tile(const WRow<NBL>& wd, const _Float16* hrow, int kb0) {
+__device__ inline floatx4_t dn_tile(const WRow<NBL>& wd, const uint16_t* hrow, int kb0) {
   floatx4_t acc0 = {}, acc1 = {};
 #pragma unroll
   for (int b = 0; b < NBL; ++b) {
-    half8_t xf[4];
+    bf16x8_t xf[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) xf[kk] = *reinterpret_cast<const half8_t*>(hrow + 32 * (kb0 + b) + 8 * kk);
+    for (int kk = 0; kk < 4; ++kk) xf[kk] = *reinterpret_cast<const bf16x8_t*>(hrow + 32 * (kb0 + b) + 8 * kk);
     if constexpr (Q == 3) {
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         const WByteWord sd = wbyte_word(wd.c[2 * b + w], wd.hi[b], wd.dm[b], w);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_byte(sd, 0), xf[2 * w], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag_byte(sd, 1), xf[2 * w + 1], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag_byte_bf(sd, 0), xf[2 * w], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag_byte_bf(sd, 1), xf[2 * w + 1], acc1, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     } else {
       const WStage sd = wstage_block<Q>(wd.c[2 * b], wd.c[2 * b + 1], wd.hi[b], wd.dm[b]);
 #pragma unroll
       for (int kk = 0; kk < 4; kk += 2) {
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sd, kk), xf[kk], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sd, kk + 1), xf[kk + 1], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag_bf<Q>(sd, kk), xf[kk], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag_bf<Q>(sd, kk + 1), xf[kk + 1], acc1, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -392,7 +405,7 @@ void bat_down(Experts ex, FfnArgs a) {
   __shared__ BatMap bm;
   extern __shared__ int bat_dyn[];  // base, off (bat_map_bytes)
   __shared__ float gtab[kBTabDn];
-  __shared__ __attribute__((aligned(16))) _Float16 hs[2][16 * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[2][16 * kRow];
   const int H = ex.H, E_tot = ex.E_tot;
   const int A = a.T * (a.k + ex.has_shared);
   const bool use_tab = A <= kBTabDn;
@@ -459,7 +472,7 @@ void bat_down(Experts ex, FfnArgs a) {
     const int m = 16 * it.tg + r16, slot = it.slot0 + m;
     const bool live = m < it.M;
     const float g = live ? (use_tab ? gtab[slot] : gate_of(a, slot)) : 0.f;
-    const _Float16* hrow = &hs[buf][r16 * kRow];
+    const uint16_t* hrow = &hs[buf][r16 * kRow];
     const int row0 = 16 * kDnRows * (kBWaves * it.chunk + wave) + 4 * c;
     const floatx4_t o0 = dn_tile<Q, NBL>(w0, hrow, kb0);
     if (more) w0 = wrow(nx, 0);
@@ -505,9 +518,9 @@ hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
   const dim3 gdn((unsigned)(dn_items < cap_dn ? dn_items : cap_dn));
   const size_t map = bat_map_bytes(ex.E_tot);
   if (!a.xs_ready) {
-    const long n = (long)a.T * ex.H / 8;
-    const int xg = (int)(n / 256 + 1 < 1024 ? n / 256 + 1 : 1024);
-    MOE_LAUNCH("bat_xs", s, bat_xs, dim3(xg), dim3(256), 0, s, xs_job(ex.qtype, ex.H, a.x, a.xdtype, a.T, a.x16));
+    const int xg = (a.T + 3) / 4 < 1024 ? (a.T + 3) / 4 : 1024;  // a wave per token row
+    MOE_LAUNCH("bat_xs", s, bat_xs, dim3(xg), dim3(256), 0, s,
+               xs_job(ex.qtype, ex.H, a.x, a.xdtype, a.T, a.x16, a.xe));
   }
   switch (ex.H / 1024) {
     case 1: MOE_LAUNCH("bat_gateup", s, (bat_gateup<Q, 1>), ggu, dim3(kBThreads), map, s, ex, a); break;
@@ -529,8 +542,8 @@ bool batch_supported(int H, int I) {
          I % (16 * kGuRows) == 0 && I <= kBMaxI;
 }
 
-XsJob xs_job(int q, int H, const void* x, int xdtype, int T, uint16_t* x16) {
-  return XsJob{x, xdtype != 0, q, H, T, q < 0 ? nullptr : reinterpret_cast<uint4*>(x16)};
+XsJob xs_job(int q, int H, const void* x, int xdtype, int T, uint16_t* x16, int32_t* xe) {
+  return XsJob{x, xdtype != 0, q, H, T, q < 0 ? nullptr : reinterpret_cast<uint4*>(x16), xe};
 }
 
 hipError_t launch_batch(const Experts& ex, const FfnArgs& a, hipStream_t s) {

@@ -34,6 +34,7 @@ __device__ inline uint32_t deq_pair(uint32_t t, half2_t d2, half2_t m2) {
 struct WStage {
   uint32_t w0, w1, w2, w3;  // Q2: e, o of code words 0, 1; Q3: codes 0, 1, third bits
   half2_t d2, m2;
+  float d, m;               // the same scales for the bf16 operands
 };
 
 // Per-row operand state of one block: its two code words (Q2: as e, o
@@ -54,6 +55,8 @@ __device__ inline WStage wstage_block(uint32_t c0, uint32_t c1, uint32_t hi, uin
   }
   st.d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
   st.m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
+  st.d = half_lo(dm);
+  st.m = half_hi(dm);
   return st;
 }
 
@@ -100,6 +103,54 @@ __device__ inline half8_t wfrag(const WStage& w, int kk) {
   return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
+// --- bf16 operands (the down projection) ----------------------------------
+// The same weights, positions and K order as wfrag, as bf16: each code comes
+// out of the FP4 conversion (Q2) or as a small integer (Q3) in fp32, d*q + m
+// is one fp32 fma (d*q is exact), and the pair is rounded once to bf16.
+__device__ inline float2v_t fp4x2_to_f32(uint32_t w, int j) {
+  switch (j) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, 3);
+  }
+}
+
+__device__ inline uint32_t deq_bf16x2(float qa, float qb, float d, float m) {
+  return pack_bf16x2(__builtin_fmaf(qa, d, m), __builtin_fmaf(qb, d, m));
+}
+
+template <int Q>
+__device__ inline bf16x8_t wfrag_bf(const WStage& w, int kk) {
+  uint32_t o[4];
+  if (Q == 2) {
+    const uint32_t e = kk < 2 ? w.w0 : w.w2, od = kk < 2 ? w.w1 : w.w3;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * (kk & 1) + u;
+      const float2v_t qa = fp4x2_to_f32(e, j), qb = fp4x2_to_f32(od, j);
+      o[2 * u] = deq_bf16x2(qa.x, qa.y, w.d, w.m);
+      o[2 * u + 1] = deq_bf16x2(qb.x, qb.y, w.d, w.m);
+    }
+  } else {
+    const uint32_t cw = kk < 2 ? w.w0 : w.w1, hq = kk < 2 ? w.w2 : w.w2 >> 16;
+    const uint32_t s = cw >> 2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t j = 2 * (kk & 1) + u;
+      const uint32_t r = __builtin_amdgcn_perm(s, cw, 0x0C000C00u | ((4u + j) << 16) | j);
+      uint32_t t0 = r & 0x00030003u, t1 = (r >> 4) & 0x00030003u;
+      const uint32_t hb = hq >> (4 * j);
+      t0 |= ((hb & 1u) << 2) | ((hb & 2u) << 17);
+      t1 |= (hb & 4u) | ((hb & 8u) << 15);
+      // t0: codes 4j, 4j + 1 in its two halves; t1: codes 4j + 2, 4j + 3
+      o[2 * u] = deq_bf16x2((float)(t0 & 0xFFu), (float)(t1 & 0xFFu), w.d, w.m);      // weights 0, 2
+      o[2 * u + 1] = deq_bf16x2((float)(t0 >> 16), (float)(t1 >> 16), w.d, w.m);      // weights 1, 3
+    }
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
 // --- Q3 through the FP8 conversion ----------------------------------------
 // A byte holding a code q <= 15 is the OCP E4M3 value q * 2^-9 (subnormal
 // below 8, exponent 1 from 8 on), so the scaled FP8 -> fp16 conversion with
@@ -117,6 +168,7 @@ __device__ inline half8_t wfrag(const WStage& w, int kk) {
 struct WByteWord {
   uint32_t b[4];
   half2_t d2, m2;
+  float d, m;
 };
 
 __device__ inline WByteWord wbyte_word(uint32_t c, uint32_t hi, uint32_t dm, int w) {
@@ -130,6 +182,8 @@ __device__ inline WByteWord wbyte_word(uint32_t c, uint32_t hi, uint32_t dm, int
   r.b[3] = ((c >> 6) & 0x03030303u) | ((x >> 1) & 0x04040404u);
   r.d2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x01000100u));
   r.m2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dm, dm, 0x03020302u));
+  r.d = half_lo(dm);
+  r.m = half_hi(dm);
   return r;
 }
 
@@ -146,6 +200,22 @@ __device__ inline half8_t wfrag_byte(const WByteWord& w, int h) {
     o[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qh, w.d2, w.m2));
   }
   return __builtin_bit_cast(half8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// The same as bf16 (positions as wfrag_byte): the scaled FP8 -> fp32
+// conversion gives two exact codes, then one fp32 fma each and one bf16
+// rounding per pair.
+__device__ inline bf16x8_t wfrag_byte_bf(const WByteWord& w, int h) {
+  uint32_t o[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t bw = w.b[2 * h + u];
+    const float2v_t ql = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bw, 512.0f, false);
+    const float2v_t qh = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bw, 512.0f, true);
+    o[2 * u] = deq_bf16x2(ql.x, ql.y, w.d, w.m);
+    o[2 * u + 1] = deq_bf16x2(qh.x, qh.y, w.d, w.m);
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
 // --- raw weight rows -------------------------------------------------------

@@ -15,6 +15,7 @@ namespace moe {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
@@ -40,6 +41,30 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
 __device__ inline int token_of(int asg, int T, int k) { return asg < T * k ? asg / k : asg - T * k; }
 
 __device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// SwiGLU of a token whose activations entered the matrix cores scaled by
+// 2^-e (row_exp): the true g = 2^e gs and u = 2^e us are exact in fp32.
+__device__ inline float silu_mul_x(float gs, float us, int e) {
+  return silu_mul(__builtin_ldexpf(gs, e), __builtin_ldexpf(us, e));
+}
+
+// Power-of-two exponent that brings a token row into fp16 for the matrix
+// cores: with amax its largest |x|, amax * 2^-e lies in [4, 8), so every bf16
+// value of the row converts exactly (bf16's 8-bit significand fits fp16's 11)
+// unless it is below 2^-12 of the row's largest, where fp16 turns subnormal;
+// fp32 rows round once, as any fp16 conversion does. All-zero and non-finite
+// rows keep e = 0.
+__device__ inline int row_exp(float amax) {
+  if (!(amax > 0.f) || !(amax <= 3.4028235e38f)) return 0;
+  return __builtin_amdgcn_frexp_expf(amax) - 3;  // amax = f 2^E, f in [0.5, 1)
+}
+
+// Largest value of v over the 64 lanes of the wave (every lane gets it).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
 
 // ---------------------------------------------------------------------------
 // Activations of one 32-wide block, as 16 bf16 pairs in code-pair order:
@@ -191,6 +216,13 @@ struct LaneReduce {
 __device__ inline uint32_t pack_half2(float lo, float hi) {
   const half2_t v = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+typedef float float2v_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> a bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v_t){lo, hi}, bf16x2_t));
 }
 
 // Gate-scaled expert output of one assignment slot and output row.

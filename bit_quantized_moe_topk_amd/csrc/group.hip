@@ -143,8 +143,8 @@ __global__ __launch_bounds__(1024) void group_fused(const int32_t* __restrict__ 
                                                     int32_t* counts, int32_t* offsets,
                                                     int32_t* perm, int32_t* slot_of, XsJob xj) {
   if (blockIdx.x > 0) {
-    xs_write(xj.x, xj.xbf16, xj.q, xj.H, (long)(blockIdx.x - 1) * blockDim.x + threadIdx.x,
-             (long)xj.T * xj.H / 8, (long)(gridDim.x - 1) * blockDim.x, xj.xs);
+    const int wpb = blockDim.x >> 6;
+    xs_write_rows(xj, (blockIdx.x - 1) * wpb + (threadIdx.x >> 6), (gridDim.x - 1) * wpb);
     return;
   }
   extern __shared__ int lds[];  // [E * nseg] bases, then [16] wave totals
@@ -190,8 +190,7 @@ __global__ __launch_bounds__(256) void group_count(const int32_t* __restrict__ i
                                                    int E, int has_shared, int nseg, int* hist,
                                                    int32_t* perm, int32_t* slot_of, int nb, XsJob xj) {
   if ((int)blockIdx.x >= nb) {
-    xs_write(xj.x, xj.xbf16, xj.q, xj.H, (long)(blockIdx.x - nb) * 256 + threadIdx.x,
-             (long)xj.T * xj.H / 8, (long)(gridDim.x - nb) * 256, xj.xs);
+    xs_write_rows(xj, (blockIdx.x - nb) * 4 + (threadIdx.x >> 6), (gridDim.x - nb) * 4);
     return;
   }
   extern __shared__ int lds[];  // [4][E]
@@ -366,8 +365,7 @@ hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared,
     int grid = 1;
     if (xj && xj->xs && xj->T > 0) {
       job = *xj;
-      const long n = (long)xj->T * xj->H / 8;
-      const long g = (n + threads - 1) / threads;
+      const long g = (xj->T + threads / 64 - 1) / (threads / 64);  // a wave per token row
       grid = 1 + (int)(g < 256 ? g : 256);
       if (xs_done) *xs_done = true;
     }
@@ -382,8 +380,7 @@ hipError_t launch_group(const int32_t* idx, int T, int k, int E, int has_shared,
   int grid = blocks;
   if (xj && xj->xs && xj->T > 0) {
     job = *xj;
-    const long n = (long)xj->T * xj->H / 8;
-    const long g = (n + 255) / 256;
+    const long g = (xj->T + 3) / 4;  // a wave per token row
     grid += (int)(g < 1024 ? g : 1024);
     if (xs_done) *xs_done = true;
   }

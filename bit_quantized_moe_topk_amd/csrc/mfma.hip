@@ -6,13 +6,15 @@
 // gate into its epilogue. The pages' prompt path likewise multiplies quantised
 // experts in large chunks without first expanding them to FP16 in memory
 // ("Strata - the details", "Faster prompts"). Here weights are expanded only
-// in registers, right before v_mfma_f32_32x32x16_f16 consumes them.
+// in registers, right before v_mfma_f32_32x32x16_f16 (gate/up: fp16 weights
+// and activations, each token row scaled by a power of two into fp16 range)
+// or v_mfma_f32_32x32x16_bf16 (down: bf16 weights and h) consumes them.
 //
 // Workgroup tile: kBM = 128 assignments x NW * 64 weight rows, K in stages of
 // 64 (two quantisation blocks), NW = 8 waves (4 for narrow matrices), two
 // per SIMD. Each wave owns 64 weight rows for all 128 assignments: it loads
 // its own weight blocks and dequantises them straight into MFMA operand
-// registers (w = d*q + m, one fp16 rounding), so weights never touch LDS. The
+// registers (w = d*q + m, one fp16 or bf16 rounding), so weights never touch LDS. The
 // activation tile is gathered through the grouping permutation by all waves
 // into double-buffered LDS and read by every wave.
 // K order: stage s of S = K/64 holds blocks s (lane half 0) and S + s (lane
@@ -30,6 +32,7 @@
 #include "deq16.h"
 #include "gemv.h"
 #include "sched.h"
+#include "batch_x.h"
 
 namespace moe {
 namespace {
@@ -44,7 +47,6 @@ constexpr int kRow = 64;
 // Epilogue staging per wave (16-bit outputs): down, 64 assignments x 64 rows
 // (stride 72); gate/up, 128 assignments x 32 rows (stride 40).
 constexpr int kStage = 128 * 40;
-__device__ inline half8_t frag(const _Float16* p) { return *reinterpret_cast<const half8_t*>(p); }
 
 // Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at
 // lds_wave + 16 l (lds_wave must be the same for the whole wave).
@@ -77,33 +79,46 @@ __device__ inline WStage wstage(const WPair& w, int b) {
 
 // One stage of an MFMA wave over NI 32-row activation groups: activation
 // fragments are read one MFMA step ahead and each step's weight operands are
-// dequantised while the previous step's MFMAs run.
-template <int NI, int Q>
+// dequantised while the previous step's MFMAs run. BF: bf16 operands (the
+// down projection, whose activation operand h is bf16), else fp16.
+template <int Q, bool BF>
+__device__ inline auto wop(const WStage& w, int kk) {
+  if constexpr (BF) return wfrag_bf<Q>(w, kk);
+  else return wfrag<Q>(w, kk);
+}
+
+template <int NI, int Q, bool BF>
 __device__ inline void stage_mma(const _Float16* xb, const WStage (&w)[2],
                                  float16_t (&acc)[4][2]) {
+  typedef typename std::conditional<BF, bf16x8_t, half8_t>::type op_t;
   const int lane = threadIdx.x & 63;
   // row 32 i + lane % 32, logical chunk 4 h + kk (h = lane / 32), swizzled
   const _Float16* ap = xb + (lane & 31) * kRow;
   const int hq = 4 * (lane >> 5), sw = lane & 7;
-  half8_t af[2][NI], bf[2][2];
+  auto afrag = [](const _Float16* p) { return *reinterpret_cast<const op_t*>(p); };
+  op_t af[2][NI], bf[2][2];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) af[0][i] = frag(ap + 32 * i * kRow + 8 * (hq ^ sw));
+  for (int i = 0; i < NI; ++i) af[0][i] = afrag(ap + 32 * i * kRow + 8 * (hq ^ sw));
 #pragma unroll
-  for (int j = 0; j < 2; ++j) bf[0][j] = wfrag<Q>(w[j], 0);
+  for (int j = 0; j < 2; ++j) bf[0][j] = wop<Q, BF>(w[j], 0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const int c = kk & 1, n = c ^ 1;
     if (kk < 3) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) af[n][i] = frag(ap + 32 * i * kRow + 8 * ((hq + kk + 1) ^ sw));
+      for (int i = 0; i < NI; ++i) af[n][i] = afrag(ap + 32 * i * kRow + 8 * ((hq + kk + 1) ^ sw));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[n][j] = wfrag<Q>(w[j], kk + 1);
+      for (int j = 0; j < 2; ++j) bf[n][j] = wop<Q, BF>(w[j], kk + 1);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[c][j], af[c][i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (BF)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[c][j], af[c][i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[c][j], af[c][i], acc[i][j], 0, 0, 0);
+      }
   }
 }
 
@@ -204,9 +219,10 @@ __device__ inline TileInfo tile_info(const TileMap& tm, const int* offs, int E_t
 template <bool DOWN, int NW>
 constexpr int tile_rows() { return DOWN ? 64 * NW : 32 * NW; }
 
-// DOWN = false: gate/up + SwiGLU -> h (fp16, grouped order, [A][I], each
-//               group of four rows of I in the MFMA K order).
-// DOWN = true : gate * (W_d h) -> per-slot outputs.
+// DOWN = false: gate/up + SwiGLU -> h (bf16, grouped order, [A][I], each
+//               group of four rows of I in the MFMA K order); fp16 operands,
+//               each token's activations scaled by 2^-e (xe).
+// DOWN = true : gate * (W_d h) -> per-slot outputs; bf16 operands.
 //
 // NW waves, each owning 64 weight rows (gate/up: 32 gate + 32 up rows, so
 // SwiGLU is local) for all kBM activation rows of the tile. Every wave also
@@ -342,11 +358,19 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
   auto tile = [&](auto live_c, const TileInfo& t) {
     constexpr int LIVE = decltype(live_c)::value;
     const int wrow0 = t.nt * tile_rows<DOWN, NW>() + (DOWN ? 64 : 32) * wave;
-    float gpre[LIVE];  // routing gates of this lane's assignments, fetched early
+    // per assignment of this lane: the routing gate (down) or the exponent
+    // of its token's activation row (gate/up), fetched early
+    float gpre[LIVE];
+    int epre[LIVE];
 #pragma unroll
     for (int i = 0; i < LIVE; ++i) {
       const int mm = 32 * i + (lane & 31);
       gpre[i] = DOWN && mm < t.M ? gate_of(a, t.slot0 + mm) : 0.f;
+      epre[i] = 0;
+      if (!DOWN && mm < t.M) {
+        const int tk = token_of(a.perm[t.slot0 + mm], a.T, a.k);
+        epre[i] = (unsigned)tk < (unsigned)a.T ? a.xe[tk] : 0;
+      }
     }
     float16_t acc[4][2];
 #pragma unroll
@@ -360,7 +384,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) w[j] = wstage<Q>(wq[j], 0);
       xdma(xs1);                     // stage g + 1 (total is even)
-      stage_mma<LIVE, Q>(xs0, w, acc);
+      stage_mma<LIVE, Q, DOWN>(xs0, w, acc);
       __syncthreads();               // also waits for stage g + 1's LDS writes
       // odd stage g + 1: xs1, weight block 1
 #pragma unroll
@@ -369,7 +393,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
         wload(wq);                   // stage pair g + 2, g + 3
         xdma(xs0);                   // stage g + 2
       }
-      stage_mma<LIVE, Q>(xs1, w, acc);
+      stage_mma<LIVE, Q, DOWN>(xs1, w, acc);
       if (s + 2 < S) __syncthreads();
     }
     // ---- epilogue ----
@@ -425,16 +449,17 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
         __builtin_amdgcn_wave_barrier();
       }
     } else {
-      // 128 assignments x 32 rows of h (fp16, row stride 40)
+      // 128 assignments x 32 rows of h (bf16, row stride 40): the token's
+      // exponent restores the true g and u before SwiGLU
 #pragma unroll
       for (int i = 0; i < LIVE; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float v[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = silu_mul(acc[i][0][4 * q + u], acc[i][1][4 * q + u]);
+          for (int u = 0; u < 4; ++u) v[u] = silu_mul_x(acc[i][0][4 * q + u], acc[i][1][4 * q + u], epre[i]);
           *reinterpret_cast<uint2*>(stg + (32 * i + (lane & 31)) * 40 + 8 * q + 4 * h) =
-              make_uint2(pack_half2(v[0], v[2]), pack_half2(v[1], v[3]));  // K order 0, 2, 1, 3
+              make_uint2(pack_bf16x2(v[0], v[2]), pack_bf16x2(v[1], v[3]));  // K order 0, 2, 1, 3
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -443,7 +468,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
         const int mm = (lane >> 2) + 16 * it;
         if (mm < t.M) {
           const uint4 v = *reinterpret_cast<const uint4*>(stg + mm * 40 + 8 * (lane & 3));
-          *reinterpret_cast<uint4*>(static_cast<_Float16*>(a.h) + (size_t)(t.slot0 + mm) * ex.I +
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.h) + (size_t)(t.slot0 + mm) * ex.I +
                                     wrow0 + 8 * (lane & 3)) = v;
         }
       }
@@ -462,28 +487,10 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
 }
 
 // x -> fp16 copy, the activation operand of the gate/up tiles, in the MFMA K
-// order (each group of four stored as 0, 2, 1, 3).
-template <bool XF32>
-__global__ __launch_bounds__(256) void x_to_f16(const void* __restrict__ x, long n8,
-                                                uint16_t* __restrict__ x16) {
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
-    uint32_t o[4];
-    if (XF32) {
-      const float4* src = static_cast<const float4*>(x) + 2 * i;
-      const float4 f0 = src[0], f1 = src[1];
-      o[0] = pack_half2(f0.x, f0.z);
-      o[1] = pack_half2(f0.y, f0.w);
-      o[2] = pack_half2(f1.x, f1.z);
-      o[3] = pack_half2(f1.y, f1.w);
-    } else {
-      const uint4 v = static_cast<const uint4*>(x)[i];
-      o[0] = pack_half2(bf16_lo(v.x), bf16_lo(v.y));
-      o[1] = pack_half2(bf16_hi(v.x), bf16_hi(v.y));
-      o[2] = pack_half2(bf16_lo(v.z), bf16_lo(v.w));
-      o[3] = pack_half2(bf16_hi(v.z), bf16_hi(v.w));
-    }
-    reinterpret_cast<uint4*>(x16)[i] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+// order (each group of four stored as 0, 2, 1, 3), each token row scaled by
+// 2^-e with its exponent e in xe.
+__global__ __launch_bounds__(256) void x_to_f16(XsJob xj) {
+  xs_write_rows(xj, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4);
 }
 
 // Writes the tiled copy: one thread per (expert, matrix, record, lane).
@@ -540,12 +547,9 @@ hipError_t launch_q(const Experts& ex, const FfnArgs& a, int grid, hipStream_t s
 }  // namespace
 
 hipError_t launch_x16(const Experts& ex, const FfnArgs& a, hipStream_t s) {
-  const long n8 = (long)a.T * ex.H / 8;
-  const int xg = (int)(n8 / 256 + 1 < 2048 ? n8 / 256 + 1 : 2048);
-  if (a.xdtype == 0)
-    MOE_LAUNCH("x_to_f16", s, x_to_f16<true>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
-  else
-    MOE_LAUNCH("x_to_f16", s, x_to_f16<false>, dim3(xg), dim3(256), 0, s, a.x, n8, a.x16);
+  const int xg = (a.T + 3) / 4 < 2048 ? (a.T + 3) / 4 : 2048;  // a wave per token row
+  MOE_LAUNCH("x_to_f16", s, x_to_f16, dim3(xg), dim3(256), 0, s,
+             xs_job(0, ex.H, a.x, a.xdtype, a.T, a.x16, a.xe));
   return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@
 #include "gemv.h"
 #include "sched.h"
 #include "topk.h"
+#include "batch_x.h"
 
 namespace moe {
 
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(kWinThreads) void win_down(int T, Experts ex, const
 // order). Ends after the last h store of the role, behind a barrier.
 template <int Q, int NBL>
 __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T, const Experts& ex,
-                                   const _Float16* xs,
+                                   const _Float16* xs, const int* xe,
                                    float (&red)[kWinWaves][kMmaBatch][2][16][kWinT],
                                    uint16_t* hwin) {
   // experts per round (at H = 4096 the activation operand alone takes 64
@@ -501,8 +502,8 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
         }
         uint32_t* dst = reinterpret_cast<uint32_t*>(hwin + ((size_t)p * kWinT + t) * ex.I + 16 * rgrp +
                                                     4 * (pr >> 1) + 2 * (pr & 1));
-        __hip_atomic_store(dst, pack_half2(silu_mul(ga, ua), silu_mul(gb, ub)), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst, pack_bf16x2(silu_mul_x(ga, ua, xe[t]), silu_mul_x(gb, ub, xe[t])),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();
@@ -528,7 +529,7 @@ constexpr int kHsBytes = 64 * 1024;   // LDS for h: 16 experts at I = 512, 32 at
 
 template <int Q, int NBL, typename Wait>
 __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, const Experts& ex,
-                                 const uint16_t* hwin, void* y, int out_f32, _Float16* hs,
+                                 const uint16_t* hwin, void* y, int out_f32, uint16_t* hs,
                                  float (&red)[kWinWaves][16][kWinT], Wait&& wait) {
   constexpr int kDnBatch = dn_batch<Q>();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -572,19 +573,19 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
       if (p >= n_act) continue;
       // columns past T read token 0's row (finite; their gate is 0): no
       // branch, so all eight LDS reads of the expert issue together
-      const _Float16* hp = hs + ((size_t)(p - r0) * kWinT + (tok ? r16 : 0)) * I;
-      half8_t hv[NBL][4];
+      const uint16_t* hp = hs + ((size_t)(p - r0) * kWinT + (tok ? r16 : 0)) * I;
+      bf16x8_t hv[NBL][4];
 #pragma unroll
       for (int b = 0; b < NBL; ++b)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) hv[b][t] = *reinterpret_cast<const half8_t*>(hp + 32 * (kb0 + b) + 8 * t);
+        for (int t = 0; t < 4; ++t) hv[b][t] = *reinterpret_cast<const bf16x8_t*>(hp + 32 * (kb0 + b) + 8 * t);
       floatx4_t o = {};
 #pragma unroll
       for (int b = 0; b < NBL; ++b) {
         const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          o = __builtin_amdgcn_mfma_f32_16x16x32_f16(wfrag<Q>(sw, t), hv[b][t], o, 0, 0, 0);
+          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag_bf<Q>(sw, t), hv[b][t], o, 0, 0, 0);
       }
       const float ga = wl.act_gate[p][r16 & (kWinT - 1)];
       const float g = tok ? ga : 0.f;  // o[v]: row 4 c + v, token r16
@@ -664,6 +665,7 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
   auto& red = *reinterpret_cast<float(*)[kWinWaves][kMmaBatch][2][16][kWinT]>(buf + kWinT * kMmaMaxH * 2);
   __shared__ uint32_t guard_s;
   __shared__ int bad_s;
+  __shared__ int xe_w[kWinT];  // per-token exponents of the fp16 activations
   const int tid = threadIdx.x;
   const int H = ex.H;
   const int G = ex.I / 16 * kMmaSlices, D = H / 16;
@@ -671,20 +673,29 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
 
   win_topk<kLayerPer>(R, logits, T, ex.E, k);
   // the window's activations -> LDS fp16 in the MFMA K order (tokens >= T
-  // zero), by the waves that do not select experts
-  for (int i = tid - 64 * kWinT; i >= 0 && i < kWinT * H / 4; i += kWinThreads - 64 * kWinT) {
-    const int t = i / (H / 4), q = i % (H / 4);
-    float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-    if (t < T) {
-      if (XF32) {
-        const float4 f = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)t * H)[q];
-        v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
-      } else {
-        const uint2 u = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)t * H)[q];
-        v0 = bf16_lo(u.x); v1 = bf16_hi(u.x); v2 = bf16_lo(u.y); v3 = bf16_hi(u.y);
+  // zero), by the waves that do not select experts, one token row per wave:
+  // the row is scaled by 2^-e (row_exp of its largest |x|), e kept in xe_w
+  {
+    const int t = (tid >> 6) - kWinT, lane = tid & 63;
+    if (t >= 0 && t < kWinT) {
+      const int e = t < T ? row_exp(row_absmax(x, !XF32, H, t)) : 0;
+      if (lane == 0) xe_w[t] = e;
+      for (int q = lane; q < H / 4; q += 64) {
+        float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+        if (t < T) {
+          if (XF32) {
+            const float4 f = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)t * H)[q];
+            v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
+          } else {
+            const uint2 u = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)t * H)[q];
+            v0 = bf16_lo(u.x); v1 = bf16_hi(u.x); v2 = bf16_lo(u.y); v3 = bf16_hi(u.y);
+          }
+          v0 = __builtin_ldexpf(v0, -e); v1 = __builtin_ldexpf(v1, -e);
+          v2 = __builtin_ldexpf(v2, -e); v3 = __builtin_ldexpf(v3, -e);
+        }
+        *reinterpret_cast<uint2*>(xs + t * H + 4 * q) = make_uint2(pack_half2(v0, v2), pack_half2(v1, v3));
       }
     }
-    *reinterpret_cast<uint2*>(xs + t * H + 4 * q) = make_uint2(pack_half2(v0, v2), pack_half2(v1, v3));
   }
   if (tid == kWinThreads - 64) guard_s = sync_load(sync->guard);
   const int n_act = win_list(R, ex, T, k, false, nullptr, nullptr, nullptr);  // ends with a barrier
@@ -702,7 +713,7 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
       gates_out[a] = R.lgate[a];
     }
   if (role < G) {
-    gateup_role<Q, NBG>(R.wl, n_act, role, T, ex, xs, red, hwin);
+    gateup_role<Q, NBG>(R.wl, n_act, role, T, ex, xs, xe_w, red, hwin);
     // The h stores are agent-coherent; a wave's store count reaching zero means
     // they are performed chip-wide, so once every wave has waited for that,
     // the role's count orders them before the down roles' reads (which are
@@ -729,7 +740,7 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
     return bad_s == 0;
   };
   const int grp = role - G;
-  down_role<Q, NBD>(R.wl, n_act, grp, T, ex, hwin, y, out_f32, reinterpret_cast<_Float16*>(buf),
+  down_role<Q, NBD>(R.wl, n_act, grp, T, ex, hwin, y, out_f32, reinterpret_cast<uint16_t*>(buf),
                     red_dn, wait);
   if (tid == 0 && bad_s == 0 && sync_add(sync->dn[grp / kSyncGroup]) == kSyncGroup - 1 &&
       sync_add(sync->dn_all) == (uint32_t)(D / kSyncGroup - 1)) {

@@ -53,11 +53,18 @@ extern "C" {
 #define MOE_Q3 3 /* 3-bit codes, w = d*q + m, q in 0..7, 32-weight blocks */
 
 /* FFN compute modes.
- * MOE_FAST: dequantised weights and activations enter the matrix cores as fp16
- *   (decode experts: exact codes, bf16 activations, fp32 block scaling), fp32
- *   accumulation, intermediate h rounded to fp16/bf16, y rounded to the
- *   activation dtype. Expected agreement with an exact evaluation: about 1e-3
- *   relative L2 per token row. Requires |x|, |h| < 65504 (fp16 range).
+ * MOE_FAST: matrix cores with fp32 accumulation. Gate/up: weights dequantised
+ *   to fp16 (one rounding of d*q + m) times the activations in fp16, each token
+ *   row first scaled by its own power of two 2^-e (its largest |x| lands in
+ *   [4, 8)), which is exact for bf16 rows; the epilogue multiplies g and u by
+ *   2^e again before SwiGLU. h = silu(g) * u is rounded to bf16. Down: weights
+ *   dequantised to bf16 times bf16 h. y is rounded to the activation dtype.
+ *   So neither x nor h is limited to fp16's range: every finite bf16 or fp32
+ *   activation row is handled at its own scale (values below 2^-12 of their
+ *   row's largest turn fp16-subnormal and lose low bits). Some experts of
+ *   batches of up to 256 tokens run an exact-code dot on bf16 activations
+ *   instead. Expected agreement with an exact evaluation: a few 1e-3 relative
+ *   L2 per token row.
  * MOE_CHECK_F32: every step in fp32 on the vector ALUs (parity mode); y is
  *   always float32. Agreement about 1e-6. */
 #define MOE_FAST 0

@@ -75,3 +75,80 @@ def test_subnormal_block_scales(T, mode):
     assert far.min() > 10 * TOL[mode]
     assert err.max() <= TOL[mode]
     ex.close()
+
+
+# Row scales of the activation-range cases: rows past fp16's range (65,504),
+# rows of tiny values (fp16 would flush them), and ordinary rows, mixed in one
+# batch so that every row's scaling is its own.
+ROW_SCALES = (1e5, 3e-9, 1.0, 2.5e4, 1e-6, 7e5, 1e-10, 0.5)
+
+
+def scaled_rows_layer(cfg, seed):
+    lay = make_layer(cfg, seed=seed)
+    sc = np.array([ROW_SCALES[t % len(ROW_SCALES)] for t in range(cfg.T)], np.float64)
+    if cfg.xdtype == "f32":
+        x = (lay["x"].astype(np.float64) * sc[:, None]).astype(np.float32)
+    else:
+        x = f32_to_bf16_bits((bf16_bits_to_f32(lay["x"]).astype(np.float64) * sc[:, None]).astype(np.float32))
+    return dict(lay, x=x)
+
+
+@pytest.mark.parametrize("name,kw,mode", [
+    ("window T=4", dict(T=4), "fast"),
+    ("window T=3 f32", dict(T=3, xdtype="f32"), "fast"),
+    ("two-kernel window k=20", dict(T=4, k=20), "fast"),
+    ("small batch T=64 Q3", dict(T=64, qtype=3), "fast"),
+    ("small batch T=37", dict(T=37), "fast"),
+    ("tiles T=300", dict(T=300), "fast"),
+    ("GEMV + tiles H=4096 I=256", dict(T=24, H=4096, I=256, E=64, k=4), "fast"),
+    ("check T=64", dict(T=64), "check"),
+])
+def test_activation_range(name, kw, mode):
+    """bf16 activations are honoured over their whole range: each token row
+    enters the fp16 matrix cores scaled by its own power of two and h stays in
+    bf16, so rows of 1e5 (past fp16's largest value) and of 1e-10 (below its
+    smallest) agree with the oracle like ordinary rows."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfg = CONFIGS[1].with_(**kw)
+    lay = scaled_rows_layer(cfg, seed=61)
+    dev = upload(lay)
+    ex = experts_of(lay, dev)
+    log(f"[activation range] {name} mode={mode}")
+    idx, gates, y = moe.layer(dev["logits"], dev["x"], ex, cfg.k, mode=mode)
+    torch.cuda.synchronize()
+    idx_o, g_o = oracle.route(lay["logits"], cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_o)
+    ref = oracle_rows(lay, idx_o, g_o)
+    got = y_to_f64(y)
+    assert np.isfinite(got).all(), f"{name}: non-finite outputs"
+    err = rel_l2_rows(got, ref)
+    log(f"[activation range] {name}: max rel-L2 {err.max():.3e} (row norms "
+        f"{np.linalg.norm(ref, axis=1).min():.1e} .. {np.linalg.norm(ref, axis=1).max():.1e})")
+    assert err.max() <= TOL[mode], name
+    ex.close()
+
+
+def test_activation_range_prefill_1k_tiled():
+    """The same at the 1,024-token chunk through the benchmark's call form
+    (grouping launch writes the scaled copy; tiled weights)."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfg = CONFIGS[2]
+    lay = scaled_rows_layer(cfg, seed=62)
+    dev = upload(lay)
+    ex = experts_of(lay, dev)
+    ex.attach_tiled()
+    log("[activation range] prefill 1K tiled")
+    idx, gates, y = moe.layer(dev["logits"], dev["x"], ex, cfg.k)
+    torch.cuda.synchronize()
+    idx_o, g_o = oracle.route(lay["logits"], cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_o)
+    rows = np.concatenate([np.arange(16), np.random.default_rng(62).choice(cfg.T, 240, replace=False)])
+    rows = np.unique(rows).astype(np.int32)
+    got = y_to_f64(y)
+    assert np.isfinite(got).all()
+    err = rel_l2_rows(got[rows], oracle_rows(lay, idx_o, g_o, rows=rows))
+    log(f"[activation range] prefill 1K tiled: max rel-L2 {err.max():.3e}")
+    assert err.max() <= TOL["fast"]
+    ex.close()
