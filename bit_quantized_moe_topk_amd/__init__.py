@@ -75,6 +75,8 @@ def lib() -> C.CDLL:
         L.moe_layer_workspace_size.restype = sz
         L.moe_layer.argtypes = [P, P, i32, i32, P, i32, P, P, P, i32, P, sz, P]
         L.moe_layer.restype = C.c_int
+        L.moe_layer_static.argtypes = [P, P, i32, i32, P, i32, P, P, P, i32, P]
+        L.moe_layer_static.restype = C.c_int
         L.moe_profile_begin.argtypes = [i32]
         L.moe_profile_begin.restype = C.c_int
         L.moe_profile_end.argtypes = []
@@ -331,5 +333,25 @@ def layer(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fa
     return idx, gates, y
 
 
-__all__ = ["layer", "profile_begin", "profile_end", "router_logits", "route_topk", "route_group", "group", "Grouping", "Experts", "ffn_q", "lib", "status_string",
+def layer_static(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fast"):
+    """moe_layer_static: the whole layer on the library's own per-GPU scratch
+    (no workspace argument, nothing allocated by the library): (idx, gates, y)."""
+    mode = _MODES[mode]
+    _need_cuda("logits", logits, torch.float32)
+    _need_cuda("x", x, (torch.float32, torch.bfloat16))
+    T, H = x.shape
+    if H != ex.H or logits.shape[0] != T:
+        raise ValueError("shape mismatch between logits, x and the experts")
+    dev = x.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32 if mode == CHECK_F32 else x.dtype, device=dev)
+    xdt = F32 if x.dtype == torch.float32 else BF16
+    _check("moe_layer_static", lib().moe_layer_static(_ptr(logits), _ptr(x), xdt, T, ex.handle, k,
+                                                      _ptr(idx), _ptr(gates), _ptr(y), mode,
+                                                      _stream()))
+    return idx, gates, y
+
+
+__all__ = ["layer", "layer_static", "profile_begin", "profile_end", "router_logits", "route_topk", "route_group", "group", "Grouping", "Experts", "ffn_q", "lib", "status_string",
            "MoeError", "Q2", "Q3", "F32", "BF16", "FAST", "CHECK_F32", "MAX_E", "LIB_PATH"]

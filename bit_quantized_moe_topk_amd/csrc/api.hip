@@ -1,5 +1,6 @@
 // Host implementation of the C ABI declared in include/moe.h: argument checks,
 // workspace layout and kernel dispatch. Nothing here allocates device memory.
+#include <mutex>
 #include <new>
 
 #include "../../include/moe.h"
@@ -373,6 +374,69 @@ int moe_layer(const float* logits, const void* x, int32_t xdtype, int32_t T, con
   if (e != hipSuccess) return MOE_ERR_HIP;
   return ffn_q_impl(x, xdtype, T, ex, idx, gates, k, c, o, p, so, y, mode, at(ws, L.ffn),
                     ws_bytes - L.ffn, stream, xs_done);
+}
+
+}  // extern "C"
+
+// ---- whole layer without allocation ------------------------------------------
+
+namespace {
+
+// Scratch of moe_layer_static: one array per GPU the library runs on, kept
+// until the process ends. In host code `scratch` only names the symbol; its
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticBytes = MOE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_static_once[kMaxDevices];
+void* g_static_ptr[kMaxDevices];
+hipError_t g_static_err[kMaxDevices];
+
+// Zeroes the head of the scratch (the decode window's counters) once at set-up.
+__global__ __launch_bounds__(256) void zero_head(uint32_t* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+// The calling thread's current device's scratch address, resolved (and its
+// head zeroed on `s`) on the first call for that device.
+int static_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::call_once(g_static_once[dev], [&]() {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && p) {
+      hipLaunchKernelGGL(zero_head, dim3(8), dim3(256), 0, s, static_cast<uint32_t*>(p),
+                         (int)(moe::kWinSyncBytes / sizeof(uint32_t)));
+      e = hipGetLastError();
+    } else if (e == hipSuccess) {
+      e = hipErrorInvalidSymbol;
+    }
+    g_static_err[dev] = e;
+    g_static_ptr[dev] = e == hipSuccess ? p : nullptr;
+  });
+  if (g_static_err[dev] != hipSuccess || !g_static_ptr[dev]) return MOE_ERR_HIP;
+  *out = g_static_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_static(const float* logits, const void* x, int32_t xdtype, int32_t T,
+                     const moe_experts* ex, int32_t k, int32_t* idx, float* gates, void* y,
+                     int32_t mode, void* stream) {
+  if (!ex || T < 0 || k < 1 || k > ex->d.E) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_FAST && mode != MOE_CHECK_F32) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (layer_layout(ex->d, T, k, mode).total > kStaticBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = static_scratch(static_cast<hipStream_t>(stream), &ws);
+  if (st != MOE_OK) return st;
+  return moe_layer(logits, x, xdtype, T, ex, k, idx, gates, y, mode, ws, kStaticBytes, stream);
 }
 
 }  // extern "C"

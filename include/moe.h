@@ -260,6 +260,28 @@ int moe_layer(const float *logits, const void *x, int32_t xdtype, int32_t T, con
               int32_t k, int32_t *idx, float *gates, void *y, int32_t mode, void *ws,
               size_t ws_bytes, void *stream);
 
+/* ---- whole layer without allocation --------------------------------------- */
+
+/* Bytes of the library's own scratch array per GPU (moe_layer_static). */
+#define MOE_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* moe_layer for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The same computation, results and kernels as moe_layer
+ * (same arguments without ws/ws_bytes); the workspace is a 16 MiB array inside
+ * the library, one per GPU, held until the process ends. The first call on a
+ * device resolves that device's array and enqueues a small kernel on `stream`
+ * that zeroes its first 8192 bytes; no call allocates or frees anything.
+ * Calls whose moe_layer_workspace_size exceeds MOE_STATIC_SCRATCH_BYTES return
+ * MOE_ERR_WORKSPACE before launching anything (decode windows and batches of a
+ * few dozen tokens fit; 1,024-token prefill chunks do not). Every call on a GPU
+ * uses that GPU's one array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give undefined results; serialise them.
+ * Returns MOE_ERR_HIP if the device's array cannot be resolved. */
+int moe_layer_static(const float *logits, const void *x, int32_t xdtype, int32_t T,
+                     const moe_experts *ex, int32_t k, int32_t *idx, float *gates, void *y,
+                     int32_t mode, void *stream);
+
 /* ---- launch profiling ------------------------------------------------------ */
 
 /* A measurement aid for the caller's own timing (per-kernel GPU durations).
