@@ -311,7 +311,8 @@ def layer(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fa
     """The whole layer (route, group, expert FFN, combine): returns (idx, gates, y).
 
     A caller-provided `workspace` (uint8, at least moe_layer_workspace_size
-    bytes) must start zero-filled; the calls keep its first 8192 bytes zero."""
+    bytes) must start zero-filled; the calls keep the counters in its first
+    8192 bytes consistent from call to call."""
     mode = _MODES[mode]
     _need_cuda("logits", logits, torch.float32)
     _need_cuda("x", x, (torch.float32, torch.bfloat16))

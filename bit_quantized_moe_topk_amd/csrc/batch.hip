@@ -490,18 +490,6 @@ void bat_down(Experts ex, FfnArgs a) {
   }
 }
 
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
 
 template <int Q>
 hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
@@ -536,6 +524,19 @@ hipError_t launch_bat_q(const Experts& ex, const FfnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 bool batch_supported(int H, int I) {
   return (H == 1024 || H == 2048) && (I == 256 || I == 512) && H % (16 * kDnRows * kBWaves) == 0 &&

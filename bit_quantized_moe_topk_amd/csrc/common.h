@@ -79,6 +79,9 @@ void prof_close();
     }                                                                                      \
   } while (0)
 
+// Compute units of the current device (read once per device).
+int device_cus();
+
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----------
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* gates,
                        hipStream_t s);

@@ -617,16 +617,28 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
 
 // Counters of the one-launch window, at the head of the workspace, each on a
 // 128-byte line of its own (atomics on one address serialise, so every counter
-// is shared by at most 16 workgroups). Zero when a launch starts; the launch's
-// last down workgroup zeroes them again. `guard` is never written: non-zero
-// means the head was not zeroed.
+// is shared by at most 16 workgroups). up[] and up_all count over all launches
+// on the workspace (mod 2^32), kSyncGroup per launch each, whatever the layer's
+// shape: the 16 gate/up roles of group g add one each to up[g] (the role that
+// sees the old count at 15 mod 16 closes the group and adds 16 / (groups) to
+// up_all), and the launch's last down role adds kSyncGroup to every up[g] past
+// the launch's groups. So after n complete launches up[g] = up_all = 16 n and
+// epoch = n, and a launch finds them consistent whatever happened in earlier
+// ones, including waits that timed out (late gate/up roles still finish
+// before their launch ends). dn[] and dn_all count the down roles of the
+// running launch; its last down role sets them back to zero and raises epoch.
+// `guard` is never written: non-zero means the head was not zeroed. `spin`:
+// 0, or a bound in wall-clock ticks on each wait (a testing aid).
 constexpr int kSyncGroup = 16;   // workgroups per counter
 constexpr int kSyncLine = 32;    // uint32 per 128-byte line
 struct WinSync {
   uint32_t guard[kSyncLine];
+  uint32_t spin[kSyncLine];
+  uint32_t epoch[kSyncLine];     // launches completed
+  uint32_t up_all[kSyncLine];    // gate/up groups completed, 16 per launch
   uint32_t up[16][kSyncLine];    // gate/up roles of group g whose h is released
-  uint32_t dn[16][kSyncLine];    // down roles of group g finished
-  uint32_t dn_all[kSyncLine];    // down groups finished
+  uint32_t dn[16][kSyncLine];    // down roles of group g finished (this launch)
+  uint32_t dn_all[kSyncLine];    // down groups finished (this launch)
 };
 static_assert(sizeof(WinSync) <= kWinSyncBytes, "the window counters fit the workspace head");
 
@@ -636,8 +648,8 @@ constexpr long long kWinSpinTicks = 1ll << 24;  // wall-clock ticks a down role 
 __device__ inline uint32_t sync_load(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline uint32_t sync_add(uint32_t* p) {
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ inline uint32_t sync_add(uint32_t* p, uint32_t v = 1u) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline void sync_zero(uint32_t* p) {
   __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -663,7 +675,7 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
   static_assert(kWinT * kMmaMaxH * 2 + kWinWaves * kMmaBatch * 2 * 16 * kWinT * 4 <= kHsBytes, "");
   _Float16* xs = reinterpret_cast<_Float16*>(buf);
   auto& red = *reinterpret_cast<float(*)[kWinWaves][kMmaBatch][2][16][kWinT]>(buf + kWinT * kMmaMaxH * 2);
-  __shared__ uint32_t guard_s;
+  __shared__ uint32_t head_s[3];  // guard, spin, epoch
   __shared__ int bad_s;
   __shared__ int xe_w[kWinT];  // per-token exponents of the fp16 activations
   const int tid = threadIdx.x;
@@ -697,10 +709,14 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
       }
     }
   }
-  if (tid == kWinThreads - 64) guard_s = sync_load(sync->guard);
+  if (tid == kWinThreads - 64) {
+    head_s[0] = sync_load(sync->guard);
+    head_s[1] = sync_load(sync->spin);
+    head_s[2] = sync_load(sync->epoch);
+  }
   const int n_act = win_list(R, ex, T, k, false, nullptr, nullptr, nullptr);  // ends with a barrier
 
-  if (guard_s != 0u) {  // the head was not zeroed: y becomes NaN
+  if (head_s[0] != 0u) {  // the head was not zeroed: y becomes NaN
     for (int i = tid; i < T * H; i += kWinThreads) {
       if (out_f32) static_cast<float*>(y)[i] = __uint_as_float(0x7FC00000u);
       else static_cast<uint16_t*>(y)[i] = 0x7FC0u;
@@ -720,20 +736,25 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
     // agent-coherent too). No cache write-back is needed.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (tid == 0) sync_add(sync->up[role / kSyncGroup]);
+    if (tid == 0 && (sync_add(sync->up[role / kSyncGroup]) % kSyncGroup) == kSyncGroup - 1)
+      sync_add(sync->up_all, (uint32_t)(kSyncGroup / (G / kSyncGroup)));  // the group is complete
     return;
   }
+  // One lane watches up_all, with a pause between reads (the counters' lines
+  // stay quiet for the gate/up roles' stores and atomics), until this launch's
+  // groups are all complete; bounded in time, past which the rows become NaN.
+  const uint32_t target = (uint32_t)kSyncGroup * (head_s[2] + 1u);
+  const long long spin = head_s[1] ? (long long)head_s[1] : kWinSpinTicks;
   auto wait = [&]() -> bool {
-    if (tid == 0) bad_s = 0;
-    __syncthreads();
-    if (tid < G / kSyncGroup) {  // lanes of wave 0, one counter each
+    if (tid == 0) {
+      bad_s = 0;
       const long long t0 = wall_clock64();
-      while (sync_load(sync->up[tid]) != (uint32_t)kSyncGroup) {
-        __builtin_amdgcn_s_sleep(1);
-        if (wall_clock64() - t0 > kWinSpinTicks) {
+      while (sync_load(sync->up_all) != target) {
+        if (wall_clock64() - t0 > spin) {
           bad_s = 1;
           break;
         }
+        __builtin_amdgcn_s_sleep(4);
       }
     }
     __syncthreads();
@@ -742,12 +763,15 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
   const int grp = role - G;
   down_role<Q, NBD>(R.wl, n_act, grp, T, ex, hwin, y, out_f32, reinterpret_cast<uint16_t*>(buf),
                     red_dn, wait);
-  if (tid == 0 && bad_s == 0 && sync_add(sync->dn[grp / kSyncGroup]) == kSyncGroup - 1 &&
+  if (tid == 0 && sync_add(sync->dn[grp / kSyncGroup]) == kSyncGroup - 1 &&
       sync_add(sync->dn_all) == (uint32_t)(D / kSyncGroup - 1)) {
-    // every gate/up role has released h and every down role has passed its wait
-    for (int g = 0; g < G / kSyncGroup; ++g) sync_zero(sync->up[g]);
+    // the launch's last down role (timed-out roles count too): top up the
+    // groups this launch's shape has none of, reset the down counts, close
+    // the launch
+    for (int g = G / kSyncGroup; g < 16; ++g) sync_add(sync->up[g], (uint32_t)kSyncGroup);
     for (int g = 0; g < D / kSyncGroup; ++g) sync_zero(sync->dn[g]);
     sync_zero(sync->dn_all);
+    sync_add(sync->epoch);
   }
 }
 
@@ -811,9 +835,8 @@ bool window_supported(const Experts& ex, int T, int k) {
   return ex.H % rows == 0 && ex.I % (64 / (ex.H / 32) > 2 ? 64 / (ex.H / 32) : 2) == 0;
 }
 
-// Window workspace: counters (kWinSyncBytes, zero between calls) | active list |
-// h [n_act][kWinT][I] (fp16 in the MFMA K order for the one-launch form, bf16
-// otherwise).
+// Window workspace: counters (kWinSyncBytes; see WinSync) | active list |
+// h [n_act][kWinT][I] (bf16; in the MFMA K order for the one-launch form).
 namespace {
 struct WinLayout {
   size_t sync, meta, h, total;

@@ -250,12 +250,16 @@ size_t moe_layer_workspace_size(const moe_experts *ex, int32_t T, int32_t k, int
  * down); other calls run moe_route_group then moe_ffn_q inside the workspace.
  *
  * ws: at least moe_layer_workspace_size(ex, T, k, mode) bytes. Its first 8192
- * bytes must be zero before the first call that uses it (a zero-filled
- * allocation); every moe_layer call leaves them zero, and no form of the call
- * other than the one-kernel window writes them, so one zeroed workspace serves
- * every shape. Calls that overlap in time must not share a workspace. A head
- * that was not zeroed shows as NaN in the window's y (the first 128 bytes are
- * checked; a down row also gives up waiting after about 0.2 s). */
+ * bytes (the head) must be zero before the first call that uses it (a
+ * zero-filled allocation). The one-kernel window keeps counters there that
+ * count over all calls on the workspace; every call leaves them in a state the
+ * next call can start from, also when a wait timed out; no other form of the
+ * call writes the head, so one zeroed workspace serves every shape. Calls that
+ * overlap in time must not share a workspace. A head whose first 128 bytes are
+ * not zero shows as NaN in the window's y; a down row that waits longer than
+ * about 0.2 s for the gate/up rows gives up and becomes NaN. Bytes 128..131 of
+ * the head may hold a shorter bound on that wait, in ticks of the 100 MHz wall
+ * clock (0 = the default); this exists for testing the timeout path. */
 int moe_layer(const float *logits, const void *x, int32_t xdtype, int32_t T, const moe_experts *ex,
               int32_t k, int32_t *idx, float *gates, void *y, int32_t mode, void *ws,
               size_t ws_bytes, void *stream);
