@@ -512,26 +512,29 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
 
 // Down role: rows 16 grp .. 16 grp + 15 of H for every active expert; wave w
 // takes K half w & 1 and the experts w / 2, w / 2 + 4, ...: per expert a
-// 16-row x 16-token tile (tokens past T zero) with h (fp16, MFMA K order) as
-// the token operand, scaled by the routing gates and summed in registers; the
-// eight partial tiles are added in LDS in wave order and the role writes its
-// rows of y. The first round's weights are requested before wait(), which
-// returns once h is complete (false: it never was; the rows become NaN). h
-// then comes into LDS (hs, kHsBytes) a phase of experts at a time, every load
-// of a phase in flight at once.
-// experts per wave whose weights are in registers (Q3 rows carry a third-bit
-// plane, so fewer of them fit)
-template <int Q>
+// 16-row x 16-token tile (tokens past T zero) on v_mfma_f32_16x16x32_bf16
+// (bf16 weights, bf16 h in the MFMA K order), scaled by the routing gates and
+// summed in registers; the eight partial tiles are added in LDS in wave order
+// and the role writes its rows of y. The first round's weights are requested
+// before wait(), which returns once h is complete (false: it never was; the
+// rows become NaN). h then comes into LDS a round of experts at a time into
+// the two halves of hs in turn: the next round's h (and weights) are in flight
+// while the current round computes.
+// experts per wave and round: a round's h fills half of hs
+template <int NBL>
 constexpr int dn_batch() {
-  return Q == 3 ? 3 : 4;
+  return 4 / NBL;
 }
-constexpr int kHsBytes = 64 * 1024;   // LDS for h: 16 experts at I = 512, 32 at I = 256
+constexpr int kHsBytes = 64 * 1024;   // LDS for h: two rounds of 8 experts at I = 512, 16 at I = 256
+constexpr int kHsHalf = kHsBytes / 2;
 
 template <int Q, int NBL, typename Wait>
 __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, const Experts& ex,
                                  const uint16_t* hwin, void* y, int out_f32, uint16_t* hs,
                                  float (&red)[kWinWaves][16][kWinT], Wait&& wait) {
-  constexpr int kDnBatch = dn_batch<Q>();
+  constexpr int kDnBatch = dn_batch<NBL>();
+  constexpr int RS = 4 * kDnBatch;  // experts per round
+  static_assert(RS * kWinT * (256 * NBL) * 2 <= kHsHalf, "h of one round fits half of hs");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int I = ex.I;
   const int c = lane >> 4, r16 = lane & 15;
@@ -546,34 +549,37 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
     if (p < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[p]) + roff);
   }
   const bool ok = wait();
-  floatx4_t acc = {};
-  static_assert(kHsBytes / (kWinT * 512 * 2) >= 4 * kDnBatch, "h of one round fits hs (I <= 512)");
-  for (int r0 = 0; r0 < n_act; r0 += 4 * kDnBatch) {  // rounds of 4 kDnBatch experts
-    const int n16 = min(4 * kDnBatch, n_act - r0) * kWinT * I / 8;
-    const uint4* src = reinterpret_cast<const uint4*>(hwin) + (size_t)r0 * kWinT * I / 8;
-    // h of the round straight into LDS (each lane's 16 bytes land at the
-    // wave's base + 16 lane), no registers held; every load in flight at once,
-    // agent-coherent (h was written in this launch on other CUs)
-    constexpr int kCopy = kHsBytes / 16 / kWinThreads;
+  // h of the round at r0 into half `half` of hs, straight into LDS (each
+  // lane's 16 bytes land at the wave's base + 16 lane), no registers held;
+  // every load in flight at once, agent-coherent (h was written in this
+  // launch on other CUs)
+  auto copy = [&](int r0, int half) {
+    constexpr int kCopy = kHsHalf / 16 / kWinThreads;
     constexpr int kCoherent = 16;  // cache policy: agent scope
-    __syncthreads();  // the previous round's reads of hs are done
+    const int n16 = min(RS, n_act - r0) * kWinT * I / 8;
+    const uint4* src = reinterpret_cast<const uint4*>(hwin) + (size_t)r0 * kWinT * I / 8;
+    uint4* dst = reinterpret_cast<uint4*>(hs) + half * (kHsHalf / 16);
 #pragma unroll
     for (int u = 0; u < kCopy; ++u)
       if (tid + u * kWinThreads < n16)
-        __builtin_amdgcn_global_load_lds(
-            src + tid + u * kWinThreads,
-            (__attribute__((address_space(3))) void*)(reinterpret_cast<uint4*>(hs) + u * kWinThreads +
-                                                      64 * wave),
-            16, 0, kCoherent);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the LDS writes have landed
-    __syncthreads();
+        __builtin_amdgcn_global_load_lds(src + tid + u * kWinThreads,
+                                         (__attribute__((address_space(3))) void*)(dst + u * kWinThreads + 64 * wave),
+                                         16, 0, kCoherent);
+  };
+  copy(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the LDS writes have landed
+  __syncthreads();
+  floatx4_t acc = {};
+  for (int r0 = 0, half = 0; r0 < n_act; r0 += RS, half ^= 1) {
+    if (r0 + RS < n_act) copy(r0 + RS, half ^ 1);  // the next round, in flight during this one
+    const uint16_t* hb = hs + half * (kHsHalf / 2);
 #pragma unroll
     for (int j = 0; j < kDnBatch; ++j) {
       const int p = r0 + eq + 4 * j;
       if (p >= n_act) continue;
       // columns past T read token 0's row (finite; their gate is 0): no
       // branch, so all eight LDS reads of the expert issue together
-      const uint16_t* hp = hs + ((size_t)(p - r0) * kWinT + (tok ? r16 : 0)) * I;
+      const uint16_t* hp = hb + ((size_t)(p - r0) * kWinT + (tok ? r16 : 0)) * I;
       bf16x8_t hv[NBL][4];
 #pragma unroll
       for (int b = 0; b < NBL; ++b)
@@ -592,9 +598,11 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
 #pragma unroll
       for (int v2 = 0; v2 < 4; ++v2) acc[v2] += g * o[v2];
       // this slot's weights for the next round, in flight during the rest of this one
-      const int pn = p + 4 * kDnBatch;
+      const int pn = p + RS;
       if (pn < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[pn]) + roff);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the next round's h and weights have landed
+    __syncthreads();                     // and every wave is done with this half
   }
   if (r16 < kWinT) {
 #pragma unroll
@@ -616,29 +624,26 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
 }
 
 // Counters of the one-launch window, at the head of the workspace, each on a
-// 128-byte line of its own (atomics on one address serialise, so every counter
-// is shared by at most 16 workgroups). up[] and up_all count over all launches
-// on the workspace (mod 2^32), kSyncGroup per launch each, whatever the layer's
-// shape: the 16 gate/up roles of group g add one each to up[g] (the role that
-// sees the old count at 15 mod 16 closes the group and adds 16 / (groups) to
-// up_all), and the launch's last down role adds kSyncGroup to every up[g] past
-// the launch's groups. So after n complete launches up[g] = up_all = 16 n and
+// 128-byte line of its own (atomics on one address serialise, so every up
+// counter is shared by at most 16 workgroups). up[] counts over all launches
+// on the workspace (mod 2^32), kSyncGroup per launch each, whatever the
+// layer's shape: the 16 gate/up roles of group g add one each to up[g], and
+// the launch's last down role adds kSyncGroup to every up[g] past the
+// launch's groups. So after n complete launches every up[g] = 16 n and
 // epoch = n, and a launch finds them consistent whatever happened in earlier
 // ones, including waits that timed out (late gate/up roles still finish
-// before their launch ends). dn[] and dn_all count the down roles of the
-// running launch; its last down role sets them back to zero and raises epoch.
-// `guard` is never written: non-zero means the head was not zeroed. `spin`:
-// 0, or a bound in wall-clock ticks on each wait (a testing aid).
+// before their launch ends). dn_all counts the down roles of the running
+// launch; its last down role sets it back to zero and raises epoch. `guard`
+// is never written: non-zero means the head was not zeroed. `spin`: 0, or a
+// bound in wall-clock ticks on the down roles' wait (a testing aid).
 constexpr int kSyncGroup = 16;   // workgroups per counter
 constexpr int kSyncLine = 32;    // uint32 per 128-byte line
 struct WinSync {
   uint32_t guard[kSyncLine];
   uint32_t spin[kSyncLine];
   uint32_t epoch[kSyncLine];     // launches completed
-  uint32_t up_all[kSyncLine];    // gate/up groups completed, 16 per launch
+  uint32_t dn_all[kSyncLine];    // down roles finished (this launch)
   uint32_t up[16][kSyncLine];    // gate/up roles of group g whose h is released
-  uint32_t dn[16][kSyncLine];    // down roles of group g finished (this launch)
-  uint32_t dn_all[kSyncLine];    // down groups finished (this launch)
 };
 static_assert(sizeof(WinSync) <= kWinSyncBytes, "the window counters fit the workspace head");
 
@@ -689,7 +694,33 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
   // the row is scaled by 2^-e (row_exp of its largest |x|), e kept in xe_w
   {
     const int t = (tid >> 6) - kWinT, lane = tid & 63;
-    if (t >= 0 && t < kWinT) {
+    if (!XF32 && t >= 0 && t < kWinT) {
+      // bf16 rows: the row's quads come into registers once; their largest
+      // magnitude gives e, then they are converted from the registers
+      constexpr int kQ = kMmaMaxH / 4 / 64;
+      uint2 qv[kQ];
+      uint32_t m = 0;
+      const uint2* row = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)(t < T ? t : 0) * H);
+#pragma unroll
+      for (int i = 0; i < kQ; ++i) {
+        const int q = lane + 64 * i;
+        qv[i] = make_uint2(0u, 0u);
+        if (t < T && q < H / 4) qv[i] = row[q];
+        const uint32_t a = max(qv[i].x & 0x7FFF7FFFu, qv[i].y & 0x7FFF7FFFu);
+        m = max(m, max(a & 0xFFFFu, a >> 16));
+      }
+      const int e = row_exp(__uint_as_float(wave_max_u32(m) << 16));
+      if (lane == 0) xe_w[t] = e;
+#pragma unroll
+      for (int i = 0; i < kQ; ++i) {
+        const int q = lane + 64 * i;
+        if (q < H / 4) {
+          const float v0 = __builtin_ldexpf(bf16_lo(qv[i].x), -e), v1 = __builtin_ldexpf(bf16_hi(qv[i].x), -e);
+          const float v2 = __builtin_ldexpf(bf16_lo(qv[i].y), -e), v3 = __builtin_ldexpf(bf16_hi(qv[i].y), -e);
+          *reinterpret_cast<uint2*>(xs + t * H + 4 * q) = make_uint2(pack_half2(v0, v2), pack_half2(v1, v3));
+        }
+      }
+    } else if (t >= 0 && t < kWinT) {
       const int e = t < T ? row_exp(row_absmax(x, !XF32, H, t)) : 0;
       if (lane == 0) xe_w[t] = e;
       for (int q = lane; q < H / 4; q += 64) {
@@ -736,26 +767,30 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
     // agent-coherent too). No cache write-back is needed.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (tid == 0 && (sync_add(sync->up[role / kSyncGroup]) % kSyncGroup) == kSyncGroup - 1)
-      sync_add(sync->up_all, (uint32_t)(kSyncGroup / (G / kSyncGroup)));  // the group is complete
+    if (tid == 0) sync_add(sync->up[role / kSyncGroup]);
     return;
   }
-  // One lane watches up_all, with a pause between reads (the counters' lines
-  // stay quiet for the gate/up roles' stores and atomics), until this launch's
-  // groups are all complete; bounded in time, past which the rows become NaN.
+  // Wave 0 watches the launch's group counters (one load, a lane per group,
+  // then a pause, so the counters' lines stay quiet for the gate/up roles'
+  // atomics) until all are complete; bounded in time, past which the rows
+  // become NaN.
   const uint32_t target = (uint32_t)kSyncGroup * (head_s[2] + 1u);
   const long long spin = head_s[1] ? (long long)head_s[1] : kWinSpinTicks;
   auto wait = [&]() -> bool {
-    if (tid == 0) {
-      bad_s = 0;
+    if (tid < 64) {
+      const int lane = tid;
       const long long t0 = wall_clock64();
-      while (sync_load(sync->up_all) != target) {
+      bool bad = false;
+      for (;;) {
+        const bool done = lane >= G / kSyncGroup || sync_load(sync->up[lane]) == target;
+        if (__ballot(!done) == 0) break;
         if (wall_clock64() - t0 > spin) {
-          bad_s = 1;
+          bad = true;
           break;
         }
         __builtin_amdgcn_s_sleep(4);
       }
+      if (lane == 0) bad_s = bad;
     }
     __syncthreads();
     return bad_s == 0;
@@ -763,13 +798,11 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
   const int grp = role - G;
   down_role<Q, NBD>(R.wl, n_act, grp, T, ex, hwin, y, out_f32, reinterpret_cast<uint16_t*>(buf),
                     red_dn, wait);
-  if (tid == 0 && sync_add(sync->dn[grp / kSyncGroup]) == kSyncGroup - 1 &&
-      sync_add(sync->dn_all) == (uint32_t)(D / kSyncGroup - 1)) {
+  if (tid == 0 && sync_add(sync->dn_all) == (uint32_t)(D - 1)) {
     // the launch's last down role (timed-out roles count too): top up the
-    // groups this launch's shape has none of, reset the down counts, close
-    // the launch
+    // groups this launch's shape has none of, reset the down count, close the
+    // launch
     for (int g = G / kSyncGroup; g < 16; ++g) sync_add(sync->up[g], (uint32_t)kSyncGroup);
-    for (int g = 0; g < D / kSyncGroup; ++g) sync_zero(sync->dn[g]);
     sync_zero(sync->dn_all);
     sync_add(sync->epoch);
   }
