@@ -515,10 +515,10 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
 // 16-row x 16-token tile (tokens past T zero) on v_mfma_f32_16x16x32_bf16
 // (bf16 weights, bf16 h in the MFMA K order), scaled by the routing gates and
 // summed in registers; the eight partial tiles are added in LDS in wave order
-// and the role writes its rows of y. The first round's weights are requested
-// before wait(), which returns once h is complete (false: it never was; the
-// rows become NaN). h then comes into LDS a round of experts at a time into
-// the two halves of hs in turn: the next round's h (and weights) are in flight
+// and the role writes its rows of y. The weights of up to 4 kDnW experts are
+// requested before wait(), which returns once h is complete (false: it never
+// was; the rows become NaN). h then comes into LDS a round of experts at a
+// time into the two halves of hs in turn: the next round's h is in flight
 // while the current round computes.
 // experts per wave and round: a round's h fills half of hs
 template <int NBL>
@@ -528,12 +528,15 @@ constexpr int dn_batch() {
 constexpr int kHsBytes = 64 * 1024;   // LDS for h: two rounds of 8 experts at I = 512, 16 at I = 256
 constexpr int kHsHalf = kHsBytes / 2;
 
+constexpr int kDnW = 8;  // experts per wave whose down weights are in registers (32 experts)
+
 template <int Q, int NBL, typename Wait>
 __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, const Experts& ex,
                                  const uint16_t* hwin, void* y, int out_f32, uint16_t* hs,
                                  float (&red)[kWinWaves][16][kWinT], Wait&& wait) {
   constexpr int kDnBatch = dn_batch<NBL>();
-  constexpr int RS = 4 * kDnBatch;  // experts per round
+  constexpr int RS = 4 * kDnBatch;            // experts per round
+  constexpr int kRounds = 4 * kDnW / RS;      // rounds per chunk of 4 kDnW experts
   static_assert(RS * kWinT * (256 * NBL) * 2 <= kHsHalf, "h of one round fits half of hs");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int I = ex.I;
@@ -542,12 +545,16 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
   const int kb0 = ks * (I / 64) + NBL * c;  // this lane's first block of the wave's K half
   const size_t roff = (size_t)(16 * grp + r16) * (I / 32) + kb0;
   const bool tok = r16 < T;
-  WRow<NBL> wd[kDnBatch];
+  // the chunk's weights: experts c0 + eq + 4 j (the first chunk's before the wait)
+  WRow<NBL> wd[kDnW];
+  auto load_chunk = [&](int c0) {
 #pragma unroll
-  for (int j = 0; j < kDnBatch; ++j) {  // the first round's weights, before the wait
-    const int p = eq + 4 * j;
-    if (p < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[p]) + roff);
-  }
+    for (int j = 0; j < kDnW; ++j) {
+      const int p = c0 + eq + 4 * j;
+      if (p < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[p]) + roff);
+    }
+  };
+  load_chunk(0);
   const bool ok = wait();
   // h of the round at r0 into half `half` of hs, straight into LDS (each
   // lane's 16 bytes land at the wave's base + 16 lane), no registers held;
@@ -570,39 +577,47 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the LDS writes have landed
   __syncthreads();
   floatx4_t acc = {};
-  for (int r0 = 0, half = 0; r0 < n_act; r0 += RS, half ^= 1) {
-    if (r0 + RS < n_act) copy(r0 + RS, half ^ 1);  // the next round, in flight during this one
-    const uint16_t* hb = hs + half * (kHsHalf / 2);
-#pragma unroll
-    for (int j = 0; j < kDnBatch; ++j) {
-      const int p = r0 + eq + 4 * j;
-      if (p >= n_act) continue;
-      // columns past T read token 0's row (finite; their gate is 0): no
-      // branch, so all eight LDS reads of the expert issue together
-      const uint16_t* hp = hb + ((size_t)(p - r0) * kWinT + (tok ? r16 : 0)) * I;
-      bf16x8_t hv[NBL][4];
-#pragma unroll
-      for (int b = 0; b < NBL; ++b)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) hv[b][t] = *reinterpret_cast<const bf16x8_t*>(hp + 32 * (kb0 + b) + 8 * t);
-      floatx4_t o = {};
-#pragma unroll
-      for (int b = 0; b < NBL; ++b) {
-        const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag_bf<Q>(sw, t), hv[b][t], o, 0, 0, 0);
-      }
-      const float ga = wl.act_gate[p][r16 & (kWinT - 1)];
-      const float g = tok ? ga : 0.f;  // o[v]: row 4 c + v, token r16
-#pragma unroll
-      for (int v2 = 0; v2 < 4; ++v2) acc[v2] += g * o[v2];
-      // this slot's weights for the next round, in flight during the rest of this one
-      const int pn = p + RS;
-      if (pn < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[pn]) + roff);
+  for (int c0 = 0; c0 < n_act; c0 += 4 * kDnW) {
+    if (c0 > 0) {  // more than 4 kDnW experts: the next chunk's weights
+      load_chunk(c0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // the next round's h and weights have landed
-    __syncthreads();                     // and every wave is done with this half
+#pragma unroll
+    for (int rr = 0; rr < kRounds; ++rr) {
+      const int r0 = c0 + rr * RS;
+      if (r0 >= n_act) break;
+      const int half = (r0 / RS) & 1;
+      if (r0 + RS < n_act) copy(r0 + RS, half ^ 1);  // the next round, in flight during this one
+      const uint16_t* hb = hs + half * (kHsHalf / 2);
+#pragma unroll
+      for (int jj = 0; jj < kDnBatch; ++jj) {
+        const int j = rr * kDnBatch + jj;
+        const int p = r0 + eq + 4 * jj;
+        if (p >= n_act) continue;
+        // columns past T read token 0's row (finite; their gate is 0): no
+        // branch, so all eight LDS reads of the expert issue together
+        const uint16_t* hp = hb + ((size_t)(p - r0) * kWinT + (tok ? r16 : 0)) * I;
+        bf16x8_t hv[NBL][4];
+#pragma unroll
+        for (int b = 0; b < NBL; ++b)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) hv[b][t] = *reinterpret_cast<const bf16x8_t*>(hp + 32 * (kb0 + b) + 8 * t);
+        floatx4_t o = {};
+#pragma unroll
+        for (int b = 0; b < NBL; ++b) {
+          const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag_bf<Q>(sw, t), hv[b][t], o, 0, 0, 0);
+        }
+        const float ga = wl.act_gate[p][r16 & (kWinT - 1)];
+        const float g = tok ? ga : 0.f;  // o[v]: row 4 c + v, token r16
+#pragma unroll
+        for (int v2 = 0; v2 < 4; ++v2) acc[v2] += g * o[v2];
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // the next round's h has landed
+      __syncthreads();                     // and every wave is done with this half
+    }
   }
   if (r16 < kWinT) {
 #pragma unroll
