@@ -7,17 +7,26 @@ gate/up, SwiGLU, down, gate-weighted sum, shared expert).
 
 Default run (prints ONE JSON line):
   * decode: the 4-token verify-window layer (hidden 2048, 512 routed experts + 1
-    shared, top-10, intermediate 512, Q2). Steps rotate over --rotation distinct
-    seeded layer instances (each with its own weights and logits), so the touched
-    weights cannot stay in the 256 MB last-level cache between visits. Steps are
-    replayed from HIP graphs (one graph per pass over the rotation). `value`
-    is tokens/s.
+    shared, top-10, intermediate 512, Q2) over a stack of --rotation (48)
+    distinct seeded layers, each with its own weights, logits and x (the layers
+    are not chained: with these weight scales a chained y would fade to zero
+    within a few layers), so the touched weights cannot stay in the 256 MB
+    last-level cache between visits. One HIP graph holds a whole pass over the
+    stack and is replayed. `value` is tokens/s of one layer step; "stack"
+    gives the pass over all layers (end-to-end tokens/s of the decode window).
+  * batched decode (16 streams x 4 tokens, Q3) under both readings of its
+    logits: one Zipf ranking shared by the streams, and one per stream.
   * prefill: the 8,192-token chunk through the 48-layer stack (24,576 routed
-    experts, ~29 GB of Q2 planes resident in HBM); per-layer and end-to-end
-    tokens/s, reported under "prefill_8k".
+    experts, ~29 GB of Q2 planes resident in HBM), and the 1,024-token chunk
+    over 8 distinct layers; per-layer and end-to-end tokens/s.
   * roofline: the dominant kernel of each regime, timed with HIP events around
-    its launches (an eager pass over the same steps), against MI355X peaks.
-  * cpu_baseline: the CPU oracle timed on a bounded sample of the decode steps.
+    its launches (an eager pass over the same steps), against MI355X's
+    published peaks and against measured ones (a streaming copy and a loop of
+    matrix-core products).
+  * cpu_baseline: the CPU oracle on the decode steps, on all the host cores
+    this process may use and on one core, plus the other workloads (configs in
+    full, or bounded row samples scaled up where a full run would take minutes,
+    each labelled).
 
 Inputs are synthetic and seeded (package ``synth``); nothing is read from disk.
 """
@@ -217,6 +226,7 @@ def kernel_profile(insts, L, stream, steps: int, chunk: int = 32) -> dict:
 
 
 def run_decode(cfg, args, workload: str = "decode"):
+    """Time K layer steps over a rotation of distinct layer instances."""
     import torch
     import bit_quantized_moe_topk_amd as moe
     L = moe.lib()
@@ -294,6 +304,11 @@ def run_decode(cfg, args, workload: str = "decode"):
         "touched_experts_mean": float(np.mean([st["touched"] for st in stats])),
         "layer_weight_bytes_mean": float(touched_bytes),
         "layer_hbm_gbs": float(touched_bytes / (ms_per_step * 1e-3) / 1e9),
+        "stack": {
+            "layers": n,
+            "us_per_pass": round(ms_per_step * n * 1e3, 2),
+            "tokens_per_s_end_to_end": round(cfg.T / (ms_per_step * n * 1e-3), 1),
+        },
         "roofline": {
             "kernel": kname,
             "bound": "hbm",
@@ -343,11 +358,11 @@ def router_timing(args, reps: int = 50) -> dict:
     return out
 
 
-def run_prefill(cfg, args):
+def run_prefill(cfg, args, n_layers: int, K: int, workload: str):
+    """K passes over a stack of n_layers distinct layers of one prefill chunk."""
     import torch
     import bit_quantized_moe_topk_amd as moe
     L = moe.lib()
-    n_layers = args.prefill_layers or cfg.layers
     insts, _, keep = build_instances(cfg, n_layers, args.seed)
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
     if not args.no_tiled:  # weight copy in the matrix-core tile order, built at load time
@@ -360,7 +375,6 @@ def run_prefill(cfg, args):
         it.step(L, stream)
     torch.cuda.synchronize()
     stats = routing_stats(insts)
-    K = args.prefill_steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for _ in range(K):
@@ -375,7 +389,7 @@ def run_prefill(cfg, args):
     total_flops = sum(2.0 * 3 * cfg.I * cfg.H * cfg.A for _ in stats)
     ms_layer = ms_stack / n_layers
     res = {
-        "workload": f"prefill: {cfg.T}-token chunk through {n_layers} stacked MoE layers "
+        "workload": f"prefill: {cfg.T}-token chunk through {n_layers} distinct MoE layers "
                     f"(hidden {cfg.H}, {cfg.E} routed + {cfg.shared} shared experts, top-{cfg.k}, "
                     f"intermediate {cfg.I}, Q{cfg.qtype}, bf16 activations)",
         "layers": n_layers,
@@ -393,7 +407,7 @@ def run_prefill(cfg, args):
             "peak": MFMA_PEAK_TFLOPS_F16,
             "unit": "TFLOP/s",
             "frac": round(flops_gu / (gu_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS_F16, 4) if gu_ms else None,
-            "traffic": measured_traffic("mfma_gateup", "prefill_8k"),
+            "traffic": measured_traffic("mfma_gateup", workload),
             "launches": n_gu,
             "avg_us": round(1e3 * gu_ms / max(n_gu, 1), 1),
             "flops_per_launch": flops_gu / max(n_gu, 1),
@@ -406,37 +420,172 @@ def run_prefill(cfg, args):
     return res
 
 
-def cpu_baseline(cfg, hosts, args):
-    """The CPU oracle (fp32 build, OpenMP over tokens) on a bounded decode sample."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_share() -> int:
+    """Host cores this process may use (at most 16, the CPU share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_step(host, cfg, threads: int, rows=None) -> None:
+    """One layer step of the CPU oracle: top-k, grouping, expert FFN + combine
+    (fp32 build, OpenMP over tokens)."""
     import oracle
-    threads = max(1, min(os.cpu_count() or 1, cfg.T))
-    steps = 0
-    t0 = time.perf_counter()
+    idx, gates = oracle.route(host["logits"], cfg.k)
+    oracle.group(idx, cfg.E, bool(cfg.shared))
+    oracle.layer_rows(host, idx, gates, rows=rows, prec="f32", threads=threads)
+
+
+def time_oracle(hosts, cfg, threads: int, seconds: float, rows=None, max_steps: int = 1000):
+    """Whole oracle steps (or steps over `rows` only) until `seconds` have passed
+    (at least one): (steps, seconds, tokens per step)."""
+    steps, t0 = 0, time.perf_counter()
     while True:
-        host = hosts[steps % len(hosts)]
-        idx, gates = oracle.route(host["logits"], cfg.k)
-        oracle.group(idx, cfg.E, bool(cfg.shared))
-        oracle.layer_rows(host, idx, gates, prec="f32", threads=threads)
+        oracle_step(hosts[steps % len(hosts)], cfg, threads, rows)
         steps += 1
         el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or steps >= 1000:
+        if el >= seconds or steps >= max_steps:
             break
-    return {"value": round(steps * cfg.T / el, 2), "unit": "tokens/s", "cores": threads,
+    return steps, el, (cfg.T if rows is None else len(rows))
+
+
+def cpu_baseline(cfg, hosts, args):
+    """The CPU oracle on the decode steps (all cores, one core) and on the other
+    workloads; configs in full unless a full run would take minutes (then a row
+    sample, scaled and labelled)."""
+    from synth import CONFIGS, make_layer
+    share = cpu_share()
+    used = lambda c: max(1, min(share, c.T))  # noqa: E731  (the oracle threads over tokens)
+    out_cfgs = {}
+
+    def record(name, c, threads, steps, el, tok, note):
+        out_cfgs.setdefault(name, {})["1 core" if threads == 1 else "all cores"] = {
+            "tokens_per_s": round(steps * tok / el, 3), "threads": threads,
+            "sample": f"{steps} step(s) of {tok} token rows, {el:.1f}s wall; {note}"}
+
+    steps, el, tok = time_oracle(hosts, cfg, used(cfg), args.cpu_seconds)
+    head = {"value": round(steps * tok / el, 2), "unit": "tokens/s", "cores": used(cfg),
             "kind": "oracle",
-            "sample": f"{steps} full decode layer steps ({cfg.T} tokens each) over "
-                      f"{len(hosts)} seeded layer instances, fp32 oracle, {el:.1f}s wall; "
-                      f"host has {os.cpu_count()} logical CPUs, the oracle parallelises "
-                      f"over the {cfg.T} tokens only"}
+            "sample": f"{steps} full decode layer steps ({cfg.T} tokens each) over {len(hosts)} "
+                      f"seeded layer instances, fp32 oracle, {el:.1f}s wall; the oracle "
+                      f"parallelises over the {cfg.T} tokens only"}
+    s1, el1, tok1 = time_oracle(hosts, cfg, 1, args.cpu_seconds / 2)
+    head["single_core"] = {"value": round(s1 * tok1 / el1, 3), "unit": "tokens/s", "cores": 1,
+                           "sample": f"{s1} full decode layer steps, {el1:.1f}s wall"}
+    head["cpu_model"] = cpu_model()
+    head["host_cores_available"] = share
+
+    full = args.cpu_full
+    for cid in (0, 4, 2):
+        c = CONFIGS[cid]
+        h = [make_layer(c, seed=args.seed, layer=0, threads=share)]
+        all_core_s = 0.0
+        for threads in (used(c), 1):
+            rows, note = None, "full layer step"
+            # one core runs the whole step unless that projects to over a minute
+            if threads == 1 and not full and all_core_s * used(c) > 60.0:
+                rows = np.arange(128, dtype=np.int32)
+                note = (f"rows 0..127 of the {c.T}-token step (a full step projects to "
+                        f"{all_core_s * used(c):.0f}s on one core)")
+            secs = 1.0 if cid == 0 else 0.0
+            steps, el, tok = time_oracle(h, c, threads, secs, rows=rows)
+            if threads > 1:
+                all_core_s = el / steps
+            record(c.name, c, threads, steps, el, tok, note)
+        del h
+    # one layer of the 8K chunk, extrapolated to the 48-layer stack
+    c = CONFIGS[3]
+    h = [make_layer(c, seed=args.seed, layer=0, threads=share)]
+    n_rows = c.T if full else 2048
+    rows = np.arange(n_rows, dtype=np.int32)
+    steps, el, tok = time_oracle(h, c, used(c), 0.0, rows=rows)
+    layer_s = el / steps * c.T / n_rows
+    out_cfgs[c.name] = {"all cores": {
+        "tokens_per_s_extrapolated": round(c.T / (layer_s * c.layers), 4),
+        "threads": used(c), "layer_seconds_extrapolated": round(layer_s, 2),
+        "sample": f"EXTRAPOLATED: {n_rows} of {c.T} token rows of one layer in {el:.1f}s, "
+                  f"scaled to the whole chunk and x{c.layers} layers"}}
+    del h
+    head["configs"] = out_cfgs
+    return head
+
+
+def measured_peaks(reps: int = 5) -> dict:
+    """Measured ceilings: a streaming copy (torch's copy kernel, bytes read +
+    written) and the matrix-core loop of libmoe_peaks.so (bf16 and fp16
+    operands), each timed with events on the stream it runs on."""
+    import torch
+    path = os.path.join(ROOT, "bit_quantized_moe_topk_amd", "libmoe_peaks.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libmoe_peaks.so is not built (python -m bit_quantized_moe_topk_amd.build)")
+    P = C.CDLL(path)
+    P.peaks_mfma_loop.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    P.peaks_mfma_loop_flops.argtypes = [C.c_int, C.c_int]
+    P.peaks_mfma_loop_flops.restype = C.c_double
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 2 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * n * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+    blocks, iters = 2048, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {"copy_GBps": round(copy_gbs, 1), "copy_bytes": f"{reps} copies of 2 GiB, read + write"}
+    for bf, name in ((1, "bf16"), (0, "f16")):
+        if P.peaks_mfma_loop(bf, blocks, iters, C.c_void_p(out.data_ptr()), stream):
+            raise RuntimeError("peaks_mfma_loop failed")
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            P.peaks_mfma_loop(bf, blocks, iters, C.c_void_p(out.data_ptr()), stream)
+        ev1.record()
+        torch.cuda.synchronize()
+        fl = P.peaks_mfma_loop_flops(blocks, iters) * reps
+        res[f"mfma_loop_{name}_TFLOPs"] = round(fl / (ev0.elapsed_time(ev1) * 1e-3) / 1e12, 1)
+    res["mfma_loop"] = (f"{blocks} workgroups x 4 waves, {iters} rounds of 4 independent "
+                        "32x32x16 products on register operands")
+    return res
+
+
+def with_measured(rf: dict, peaks: dict) -> dict:
+    """A roofline object with the measured ceiling beside the published one."""
+    if not rf or peaks is None or rf.get("achieved") is None:
+        return rf
+    rf = dict(rf)
+    mp = peaks["copy_GBps"] if rf["bound"] == "hbm" else peaks["mfma_loop_f16_TFLOPs"]
+    rf["measured_peak"] = mp
+    rf["frac_of_measured"] = round(rf["achieved"] / mp, 4)
+    return rf
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--rotation", type=int, default=32,
-                    help="distinct decode layer instances the steps cycle through")
+    ap.add_argument("--rotation", type=int, default=48,
+                    help="distinct decode layers (the stack) the steps cycle through")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--separate-calls", action="store_true",
                     help="route and group with two calls instead of moe_route_group")
@@ -446,13 +595,19 @@ def main() -> int:
     ap.add_argument("--no-batched", action="store_true", help="skip the config-4 batched decode")
     ap.add_argument("--prefill-layers", type=int, default=0, help="0 = all 48")
     ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--prefill-1k-layers", type=int, default=8,
+                    help="distinct layers of the 1,024-token chunk (0 = skip it)")
+    ap.add_argument("--prefill-1k-steps", type=int, default=5)
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy/MFMA peaks")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="run every CPU oracle workload in full (no row samples; takes minutes)")
     ap.add_argument("--no-tiled", action="store_true",
                     help="prefill on the canonical weight planes only (no tiled copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first copy a buffer of this many MiB 5 times (a kernel of known "
                          "traffic for scaling hardware byte counters)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-layers", type=int, default=8)
     args = ap.parse_args()
 
@@ -492,29 +647,55 @@ def main() -> int:
     # batched decode (config 4: 16 streams x 4 tokens, Q3): reported beside the
     # headline, through the general path (route + group, GEMV and matrix-core
     # experts, combine)
-    bat = None
+    bat = bat_own = None
     if not args.no_batched:
         import copy
         bargs = copy.copy(args)
         bargs.rotation = 16
         bargs.cpu_layers = 0
-        b, _, binsts = run_decode(CONFIGS[4], bargs, workload="batched_decode")
-        for it in binsts:
-            it.ex.close()
-        del binsts
-        torch.cuda.empty_cache()
-        bat = {"workload": "batched decode: 16 streams x 4 tokens (T = 64) through one MoE layer "
-                           "(hidden 2048, 512 routed + 1 shared experts, top-10, intermediate 512, "
-                           "Q3 weights, bf16 activations); steps rotate over 16 seeded layer instances",
-               **{k: v for k, v in b.items()}}
-        log(f"batched decode: {b['tokens_per_s']:.0f} tokens/s, {b['ms_per_step'] * 1e3:.1f} us/step, "
-            f"layer {b['layer_hbm_gbs']:.0f} GB/s")
+        for reading in ("shared", "own"):
+            bcfg = CONFIGS[4] if reading == "shared" else CONFIGS[4].with_(stream_ranking=True)
+            wl = "batched_decode" if reading == "shared" else "batched_decode_stream_ranking"
+            b, _, binsts = run_decode(bcfg, bargs, workload=wl)
+            for it in binsts:
+                it.ex.close()
+            del binsts
+            torch.cuda.empty_cache()
+            rank = ("the 16 streams share the layer's Zipf ranking of the experts"
+                    if reading == "shared" else
+                    "each of the 16 streams ranks the experts by a Zipf bias of its own")
+            b = {"workload": "batched decode: 16 streams x 4 tokens (T = 64) through one MoE layer "
+                             "(hidden 2048, 512 routed + 1 shared experts, top-10, intermediate 512, "
+                             f"Q3 weights, bf16 activations); {rank}; steps rotate over 16 seeded "
+                             "layer instances", **b}
+            log(f"batched decode ({reading} ranking): {b['tokens_per_s']:.0f} tokens/s, "
+                f"{b['ms_per_step'] * 1e3:.1f} us/step, {b['touched_experts_mean']:.0f} experts, "
+                f"layer {b['layer_hbm_gbs']:.0f} GB/s")
+            if reading == "shared":
+                bat = b
+            else:
+                bat_own = b
 
-    pre = None
+    pre = pre1k = None
     if not args.no_prefill:
-        pre = run_prefill(CONFIGS[3], args)
+        pre = run_prefill(CONFIGS[3], args, args.prefill_layers or CONFIGS[3].layers,
+                          args.prefill_steps, "prefill_8k")
         log(f"prefill: {pre['tokens_per_s_end_to_end']:.0f} tokens/s end to end, "
             f"{pre['ms_per_layer']:.3f} ms/layer, mfma_gateup {pre['roofline']['achieved']} TFLOP/s")
+        if args.prefill_1k_layers:
+            pre1k = run_prefill(CONFIGS[2], args, args.prefill_1k_layers, args.prefill_1k_steps,
+                                "prefill_1k")
+            log(f"prefill 1K: {pre1k['tokens_per_s_per_layer']:.0f} tokens/s per layer, "
+                f"{pre1k['ms_per_layer'] * 1e3:.1f} us/layer, mfma_gateup "
+                f"{pre1k['roofline']['achieved']} TFLOP/s")
+
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks()
+        log(f"measured peaks: {peaks}")
+        for r in (dec, bat, bat_own, pre, pre1k):
+            if r is not None:
+                r["roofline"] = with_measured(r["roofline"], peaks)
 
     router = router_timing(args)
     log(f"router: {router}")
@@ -522,7 +703,8 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline and hosts:
         cpu = cpu_baseline(cfg, hosts, args)
-        log(f"cpu oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
+        log(f"cpu oracle: {cpu['value']} tokens/s on {cpu['cores']} threads, "
+            f"{cpu['single_core']['value']} on one core ({cpu['cpu_model']})")
 
     rf = dict(dec["roofline"])
     line = {
@@ -536,21 +718,28 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16/bf16",
+        "arithmetic": "gate/up: fp16 matrix-core operands (each x row scaled by its own power "
+                      "of two, weights dequantised to fp16), fp32 accumulation; h in bf16; "
+                      "down: bf16 matrix-core operands, fp32 accumulation; x and y bf16",
         "data": "synthetic",
         "config": {
             "workload": f"decode: one MoE layer step over a {cfg.T}-token verify window "
                         f"(hidden {cfg.H}, {cfg.E} routed + {cfg.shared} shared experts, "
                         f"top-{cfg.k}, intermediate {cfg.I}, Q{cfg.qtype} weights, bf16 "
-                        f"activations); steps rotate over {args.rotation} seeded layer instances",
+                        f"activations); steps cycle through a stack of {args.rotation} distinct "
+                        f"seeded layers",
             "tokens_per_step": cfg.T,
-            "launch": "hip graph over the layer rotation" if dec["graph"] else "eager",
+            "launch": "one hip graph per pass over the stack" if dec["graph"] else "eager",
         },
         "roofline": rf,
         "cpu_baseline": cpu,
         "decode_detail": {k: v for k, v in dec.items() if k not in ("roofline",)},
+        "measured_peaks": peaks,
         "prefill_8k": pre,
+        "prefill_1k": pre1k,
         "batched_decode_q3": bat,
+        "batched_decode_q3_stream_ranking": bat_own,
         "router": router,
     }
     print(json.dumps(line), flush=True)

@@ -307,12 +307,13 @@ def ffn_q(x: torch.Tensor, ex: Experts, idx: torch.Tensor, gates: torch.Tensor,
 
 
 def layer(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fast",
-          workspace: torch.Tensor | None = None):
+          workspace: torch.Tensor | None = None, out=None):
     """The whole layer (route, group, expert FFN, combine): returns (idx, gates, y).
 
     A caller-provided `workspace` (uint8, at least moe_layer_workspace_size
     bytes) must start zero-filled; the calls keep the counters in its first
-    8192 bytes consistent from call to call."""
+    8192 bytes consistent from call to call. `out` = (idx, gates, y) writes
+    into existing tensors (as a captured graph needs)."""
     mode = _MODES[mode]
     _need_cuda("logits", logits, torch.float32)
     _need_cuda("x", x, (torch.float32, torch.bfloat16))
@@ -320,10 +321,18 @@ def layer(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fa
     if H != ex.H or logits.shape[0] != T:
         raise ValueError("shape mismatch between logits, x and the experts")
     dev = x.device
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
     ydtype = torch.float32 if mode == CHECK_F32 else x.dtype
-    y = torch.empty((T, H), dtype=ydtype, device=dev)
+    if out is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+        y = torch.empty((T, H), dtype=ydtype, device=dev)
+    else:
+        idx, gates, y = out
+        _need_cuda("idx", idx, torch.int32)
+        _need_cuda("gates", gates, torch.float32)
+        _need_cuda("y", y, ydtype)
+        if tuple(idx.shape) != (T, k) or tuple(gates.shape) != (T, k) or tuple(y.shape) != (T, H):
+            raise ValueError("out tensors do not match (T, k) and (T, H)")
     nbytes = int(lib().moe_layer_workspace_size(ex.handle, T, k, mode))
     if workspace is None:  # zero-filled: its head holds the decode window's counters
         workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)

@@ -1,7 +1,8 @@
-"""Build libmoe.so (HIP, gfx950) in-tree from csrc/*.hip.
+"""Build libmoe.so (HIP, gfx950) in-tree from csrc/*.hip, and the benchmark's
+measuring library libmoe_peaks.so from peaks/*.hip.
 
 Every HIP translation unit is compiled with hipcc for gfx950 only, with packed
-fp32 instructions disabled, then linked into one shared library next to this
+fp32 instructions disabled, then linked into its shared library next to this
 file. Run as ``python -m bit_quantized_moe_topk_amd.build``.
 """
 import concurrent.futures as cf
@@ -13,6 +14,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
+PEAKS_SRC = os.path.join(HERE, "peaks")
+PEAKS_LIB = os.path.join(HERE, "libmoe_peaks.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
@@ -36,19 +39,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    psrcs = sorted(glob.glob(os.path.join(PEAKS_SRC, "*.hip")))
+    with cf.ThreadPoolExecutor(min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(_compile, srcs + psrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PEAKS_LIB)
     if verbose:
         print(LIB)
+        print(PEAKS_LIB)
     return LIB
 
 

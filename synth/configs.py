@@ -26,6 +26,7 @@ class LayerConfig:
     zipf: bool          # per-expert Zipf(1.1) bias added to the router logits
     layers: int = 1     # independent layers of this shape
     streams: int = 1    # concurrent decode streams (tokens are streams x window)
+    stream_ranking: bool = False  # each stream draws its own Zipf ranking of the experts
 
     @property
     def E_tot(self) -> int:

@@ -81,10 +81,25 @@ def zipf_bias(cfg: LayerConfig, seed: int, layer: int = 0) -> np.ndarray:
     return -1.1 * np.log(rank.astype(np.float64))
 
 
+def stream_zipf_bias(cfg: LayerConfig, seed: int, layer: int, stream: int) -> np.ndarray:
+    """The Zipf bias of one decode stream that ranks the experts on its own."""
+    rank = _rng(seed, cfg.cid, layer, _S_ZIPF, 1 + stream).permutation(cfg.E) + 1
+    return -1.1 * np.log(rank.astype(np.float64))
+
+
 def make_logits(cfg: LayerConfig, seed: int, layer: int = 0) -> np.ndarray:
-    """Router logits, float32 ``[T, E]``."""
+    """Router logits, float32 ``[T, E]``.
+
+    With ``stream_ranking`` the T rows are ``streams`` consecutive windows and
+    each window's rows take the Zipf bias of its own stream; otherwise every
+    row shares the layer's one ranking."""
     noise = _rng(seed, cfg.cid, layer, _S_LOGITS).standard_normal((cfg.T, cfg.E))
-    if cfg.zipf:
+    if cfg.zipf and cfg.stream_ranking and cfg.streams > 1:
+        if cfg.T % cfg.streams:
+            raise ValueError("T must be a whole number of stream windows")
+        bias = np.stack([stream_zipf_bias(cfg, seed, layer, s) for s in range(cfg.streams)])
+        noise = noise + np.repeat(bias, cfg.T // cfg.streams, axis=0)
+    elif cfg.zipf:
         noise = noise + zipf_bias(cfg, seed, layer)[None, :]
     return noise.astype(np.float32)
 

@@ -75,3 +75,24 @@ def test_bf16_activations():
     assert x.dtype == np.uint16 and x.shape == (cfg.T, cfg.H)
     xf = bf16_bits_to_f32(x)
     assert abs(xf.std() - 1.0) < 0.05
+
+
+def test_stream_ranking_reading_of_batched_decode():
+    """Two readings of the 16-stream batched decode: one Zipf ranking shared by
+    every stream (60-75 distinct experts per layer) or a ranking of its own per
+    stream (240-270). The second reading changes only the logits' bias rows."""
+    import oracle
+    shared = CONFIGS[4]
+    own = shared.with_(stream_ranking=True)
+    d_shared, d_own = [], []
+    for layer in range(6):
+        a = make_logits(shared, 0, layer)
+        b = make_logits(own, 0, layer)
+        assert a.shape == b.shape == (64, 512)
+        d_shared.append(len(np.unique(oracle.route(a, shared.k)[0])))
+        d_own.append(len(np.unique(oracle.route(b, own.k)[0])))
+        # rows of one stream share a bias: their differences are bias-free
+        assert not np.allclose(b[0] - b[4], a[0] - a[4], atol=1e-3)
+        assert np.allclose(b[0] - b[1], a[0] - a[1], atol=1e-4)
+    assert 55 <= min(d_shared) and max(d_shared) <= 80, d_shared
+    assert 230 <= min(d_own) and max(d_own) <= 280, d_own
