@@ -68,11 +68,15 @@ def expert_plane_bytes(cfg) -> dict:
 class LayerInstance:
     """Device buffers and prebuilt C-ABI argument lists for one layer step."""
 
-    def __init__(self, cfg, host: dict, ws_bytes_fn):
+    def __init__(self, cfg, host: dict, ws_bytes_fn, router=None):
         import torch
         import bit_quantized_moe_topk_amd as moe
         self.cfg = cfg
         dev = "cuda"
+        self.hidden = router is not None   # steps start from hidden states (moe_layer_hidden)
+        if self.hidden:
+            self.rw = torch.from_numpy(router[0].view(np.int16)).to(dev)
+            self.rb = torch.from_numpy(router[1]).to(dev)
         self.logits = torch.from_numpy(host["logits"]).to(dev)
         x = torch.from_numpy(np.ascontiguousarray(host["x"]))
         if host["x"].dtype == np.uint16:
@@ -109,11 +113,20 @@ class LayerInstance:
                         P(gws) if gws is not None else None, 0 if gws is None else gws.numel())
         self.a_layer = (P(self.logits), P(self.x), xdt, cfg.T, self.ex.handle, cfg.k, P(self.idx),
                         P(self.gates), P(self.y), 0, P(lws), lws.numel())
+        if self.hidden:  # the router's logits land in the instance's logits buffer
+            self.a_hidden = (P(self.x), xdt, cfg.T, P(self.rw), P(self.rb), self.ex.handle, cfg.k,
+                             P(self.idx), P(self.gates), P(self.y), P(self.logits), 0, P(lws),
+                             lws.numel())
         self.a_ffn = (P(self.x), xdt, cfg.T, self.ex.handle, P(self.idx), P(self.gates), cfg.k,
                       P(self.counts), P(self.offsets), P(self.perm), P(self.slot_of), P(self.y),
                       0, P(fws), fws.numel())
 
     def step(self, L, stream) -> None:
+        if self.hidden:
+            st = L.moe_layer_hidden(*self.a_hidden, stream)
+            if st:
+                raise RuntimeError(f"moe_layer_hidden failed: {st}")
+            return
         if LAYER_CALL:
             st = L.moe_layer(*self.a_layer, stream)
             if st:
@@ -130,15 +143,16 @@ class LayerInstance:
             raise RuntimeError(f"C-ABI call failed: route={r} group={g} ffn={f}")
 
 
-def build_instances(cfg, n: int, seed: int, keep_host: int = 0):
+def build_instances(cfg, n: int, seed: int, keep_host: int = 0, hidden: bool = False):
     import torch
     import bit_quantized_moe_topk_amd as moe
-    from synth import make_layer
+    from synth import make_layer, make_router
     insts, hosts = [], []
     t0 = time.time()
     for i in range(n):
         host = make_layer(cfg, seed=seed, layer=i, threads=16)
-        insts.append(LayerInstance(cfg, host, None))
+        router = make_router(cfg, seed, layer=i) if hidden else None
+        insts.append(LayerInstance(cfg, host, None, router))
         if i < keep_host:
             hosts.append(host)
         del host
@@ -150,6 +164,8 @@ def build_instances(cfg, n: int, seed: int, keep_host: int = 0):
     fws_n = insts[0].ex.workspace_size(cfg.T, cfg.k, 0)
     fws = torch.empty(fws_n, dtype=torch.uint8, device="cuda")
     lws_n = L.moe_layer_workspace_size(insts[0].ex.handle, cfg.T, cfg.k, 0)
+    if hidden:
+        lws_n = max(lws_n, L.moe_layer_hidden_workspace_size(insts[0].ex.handle, cfg.T, cfg.k, 0))
     lws = torch.zeros(lws_n, dtype=torch.uint8, device="cuda")  # head: window counters
     for it in insts:
         it.bind(gws, fws, lws)
@@ -225,12 +241,14 @@ def kernel_profile(insts, L, stream, steps: int, chunk: int = 32) -> dict:
     return moe.profile_end()
 
 
-def run_decode(cfg, args, workload: str = "decode"):
-    """Time K layer steps over a rotation of distinct layer instances."""
+def run_decode(cfg, args, workload: str = "decode", hidden: bool = False):
+    """Time K layer steps over a rotation of distinct layer instances (from
+    logits, or from hidden states with the router product in the step)."""
     import torch
     import bit_quantized_moe_topk_amd as moe
     L = moe.lib()
-    insts, hosts, keep = build_instances(cfg, args.rotation, args.seed, keep_host=args.cpu_layers)
+    insts, hosts, keep = build_instances(cfg, args.rotation, args.seed, keep_host=args.cpu_layers,
+                                         hidden=hidden)
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
     for s in range(max(args.warmup, len(insts))):   # every instance runs once untimed
         insts[s % len(insts)].step(L, stream)
@@ -281,18 +299,20 @@ def run_decode(cfg, args, workload: str = "decode"):
     pb = expert_plane_bytes(cfg)
     step_layers = [stats[s % len(insts)] for s in range(K)]
     kname = max((k for k in prof
-                 if k in ("win_layer", "win_gateup", "gemv_gateup", "win_down", "gemv_down",
-                          "bat_gateup", "bat_down")),
+                 if k in ("win_layer", "win_layer_rt", "win_gateup", "gemv_gateup", "win_down",
+                          "gemv_down", "bat_gateup", "bat_down")),
                 key=lambda k: prof[k][1], default="")
     if not kname:
         raise RuntimeError(f"no decode expert kernel in the profile: {sorted(prof)}")
-    if kname == "win_layer":  # the whole window in one kernel: gate/up and down planes
+    if kname.startswith("win_layer"):  # the whole window in one kernel: gate/up and down planes
         unit = pb["gateup"] + pb["down"]
     else:
         unit = pb["gateup"] if "gateup" in kname else pb["down"]
     per_step_units = [st["touched"] if kname.startswith(("win", "bat")) else st["gemv_experts"]
                       for st in step_layers]
     k_bytes = sum(per_step_units) * unit
+    if kname == "win_layer_rt":  # the router rows (bf16 [E][H]) are read in the same launch
+        k_bytes += K * cfg.E * cfg.H * 2
     n_k, k_ms = prof[kname]
     touched_bytes = np.mean([st["touched"] for st in stats]) * (pb["gateup"] + pb["down"])
     kernels_us = {k: round(1e3 * v[1] / max(v[0], 1), 2) for k, v in prof.items()}
@@ -592,6 +612,8 @@ def main() -> int:
     ap.add_argument("--stage-calls", action="store_true",
                     help="decode steps call route_group + ffn_q instead of moe_layer")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-hidden", action="store_true",
+                    help="skip the decode stack that starts from hidden states")
     ap.add_argument("--no-batched", action="store_true", help="skip the config-4 batched decode")
     ap.add_argument("--prefill-layers", type=int, default=0, help="0 = all 48")
     ap.add_argument("--prefill-steps", type=int, default=3)
@@ -644,6 +666,24 @@ def main() -> int:
     del insts
     torch.cuda.empty_cache()
 
+    # the same stack from hidden states: router product, top-k and the window
+    # in one launch per layer
+    dech = None
+    if not args.no_hidden:
+        import copy
+        hargs = copy.copy(args)
+        hargs.cpu_layers = 0
+        h, _, hinsts = run_decode(cfg, hargs, workload="decode_hidden", hidden=True)
+        for it in hinsts:
+            it.ex.close()
+        del hinsts
+        torch.cuda.empty_cache()
+        dech = {"workload": "decode from hidden states: the router product (bf16 [512][2048] "
+                            "router rows + Zipf bias) in front of the same layer step, over the "
+                            "same 48-layer stack", **h}
+        log(f"decode from hidden states: {h['tokens_per_s']:.0f} tokens/s, "
+            f"{h['ms_per_step'] * 1e3:.1f} us/step, kernels {h['kernels_us']}")
+
     # batched decode (config 4: 16 streams x 4 tokens, Q3): reported beside the
     # headline, through the general path (route + group, GEMV and matrix-core
     # experts, combine)
@@ -693,7 +733,7 @@ def main() -> int:
     if not args.no_peaks:
         peaks = measured_peaks()
         log(f"measured peaks: {peaks}")
-        for r in (dec, bat, bat_own, pre, pre1k):
+        for r in (dec, dech, bat, bat_own, pre, pre1k):
             if r is not None:
                 r["roofline"] = with_measured(r["roofline"], peaks)
 
@@ -735,6 +775,7 @@ def main() -> int:
         "roofline": rf,
         "cpu_baseline": cpu,
         "decode_detail": {k: v for k, v in dec.items() if k not in ("roofline",)},
+        "decode_from_hidden": dech,
         "measured_peaks": peaks,
         "prefill_8k": pre,
         "prefill_1k": pre1k,

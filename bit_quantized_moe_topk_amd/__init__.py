@@ -77,6 +77,10 @@ def lib() -> C.CDLL:
         L.moe_layer.restype = C.c_int
         L.moe_layer_static.argtypes = [P, P, i32, i32, P, i32, P, P, P, i32, P]
         L.moe_layer_static.restype = C.c_int
+        L.moe_layer_hidden_workspace_size.argtypes = [P, i32, i32, i32]
+        L.moe_layer_hidden_workspace_size.restype = sz
+        L.moe_layer_hidden.argtypes = [P, i32, i32, P, P, P, i32, P, P, P, P, i32, P, sz, P]
+        L.moe_layer_hidden.restype = C.c_int
         L.moe_profile_begin.argtypes = [i32]
         L.moe_profile_begin.restype = C.c_int
         L.moe_profile_end.argtypes = []
@@ -341,6 +345,49 @@ def layer(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fa
                                         _ptr(gates), _ptr(y), mode, _ptr(workspace),
                                         workspace.numel(), _stream()))
     return idx, gates, y
+
+
+def layer_hidden(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor | None, ex: "Experts",
+                 k: int, mode="fast", workspace: torch.Tensor | None = None, out=None,
+                 logits: torch.Tensor | None = None):
+    """moe_layer_hidden: the router product, then the whole layer, from the
+    hidden states x [T, H]: returns (idx, gates, y, logits). w_router: bf16 [E, H]
+    (or its 16-bit patterns); bias: f32 [E] or None. `logits` (f32 [T, E]) receives
+    the router scores; when None, a new tensor does. `workspace` and `out` as
+    for layer()."""
+    mode = _MODES[mode]
+    _need_cuda("x", x, (torch.float32, torch.bfloat16))
+    if (w_router.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not w_router.is_cuda
+            or not w_router.is_contiguous()):
+        raise ValueError("w_router must be a contiguous CUDA bf16 (or 16-bit pattern) tensor [E, H]")
+    if bias is not None:
+        _need_cuda("bias", bias, torch.float32)
+    T, H = x.shape
+    if H != ex.H or tuple(w_router.shape) != (ex.E, H) or (bias is not None and bias.numel() != ex.E):
+        raise ValueError("shape mismatch between x, w_router, bias and the experts")
+    dev = x.device
+    ydtype = torch.float32 if mode == CHECK_F32 else x.dtype
+    if out is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+        y = torch.empty((T, H), dtype=ydtype, device=dev)
+    else:
+        idx, gates, y = out
+        _need_cuda("idx", idx, torch.int32)
+        _need_cuda("gates", gates, torch.float32)
+        _need_cuda("y", y, ydtype)
+    if logits is None:
+        logits = torch.empty((T, ex.E), dtype=torch.float32, device=dev)
+    _need_cuda("logits", logits, torch.float32)
+    nbytes = int(lib().moe_layer_hidden_workspace_size(ex.handle, T, k, mode))
+    if workspace is None:  # zero-filled: its head holds the decode window's counters
+        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    xdt = F32 if x.dtype == torch.float32 else BF16
+    _check("moe_layer_hidden", lib().moe_layer_hidden(
+        _ptr(x), xdt, T, _ptr(w_router), _ptr(bias) if bias is not None else None, ex.handle, k,
+        _ptr(idx), _ptr(gates), _ptr(y), _ptr(logits), mode, _ptr(workspace), workspace.numel(),
+        _stream()))
+    return idx, gates, y, logits
 
 
 def layer_static(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fast"):

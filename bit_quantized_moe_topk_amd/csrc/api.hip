@@ -376,6 +376,38 @@ int moe_layer(const float* logits, const void* x, int32_t xdtype, int32_t T, con
                     ws_bytes - L.ffn, stream, xs_done);
 }
 
+// ---- whole layer from hidden states -------------------------------------------
+
+size_t moe_layer_hidden_workspace_size(const moe_experts* ex, int32_t T, int32_t k, int32_t mode) {
+  const size_t base = moe_layer_workspace_size(ex, T, k, mode);
+  if (!base) return 0;
+  return base + align_up(sizeof(uint64_t) * (size_t)T * ex->d.E);  // tagged (window) or plain logits
+}
+
+int moe_layer_hidden(const void* x, int32_t xdtype, int32_t T, const uint16_t* w_router,
+                     const float* bias, const moe_experts* ex, int32_t k, int32_t* idx, float* gates,
+                     void* y, float* logits, int32_t mode, void* ws, size_t ws_bytes, void* stream) {
+  if (!ex || T < 0 || k < 1 || k > ex->d.E) return MOE_ERR_INVALID_ARG;
+  if (xdtype != MOE_F32 && xdtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_FAST && mode != MOE_CHECK_F32) return MOE_ERR_INVALID_ARG;
+  const Experts& d = ex->d;
+  if (!moe::router_supported(d.H, d.E)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * d.E > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !idx || !gates || !y || !aligned16(x) || !aligned16(y) || !aligned16(w_router))
+    return MOE_ERR_INVALID_ARG;
+  const LayerLayout L = layer_layout(d, T, k, mode);
+  if (!ws || ws_bytes < moe_layer_hidden_workspace_size(ex, T, k, mode)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L.window && moe::window_hidden_supported(d, T, k))
+    return status_of(moe::launch_window_hidden(logits, reinterpret_cast<uint64_t*>(at(ws, L.total)),
+                                               w_router, bias, T, k, d, x, xdtype, idx, gates, y,
+                                               xdtype == MOE_F32, ws, s));
+  float* lg = logits ? logits : reinterpret_cast<float*>(at(ws, L.total));
+  if (moe::launch_router(x, xdtype, T, d.H, w_router, bias, d.E, lg, s) != hipSuccess) return MOE_ERR_HIP;
+  return moe_layer(lg, x, xdtype, T, ex, k, idx, gates, y, mode, ws, L.total, stream);
+}
+
 }  // extern "C"
 
 // ---- whole layer without allocation ------------------------------------------

@@ -135,6 +135,15 @@ size_t window_workspace_bytes(const Experts& ex, int T, int k);
 hipError_t launch_window(const float* logits, int T, int k, const Experts& ex, const void* x,
                          int xdtype, int32_t* idx, float* gates, void* y, int out_f32, void* ws,
                          hipStream_t s);
+// The one-launch window starting from hidden states: router roles store the
+// logits [T][E] tagged with the launch into lgp (64-bit entries) and, when lg
+// is not null, plain into lg; then the window as launch_window. Only where
+// window_hidden_supported holds.
+bool window_hidden_supported(const Experts& ex, int T, int k);
+hipError_t launch_window_hidden(float* lg, uint64_t* lgp, const uint16_t* rw, const float* rbias,
+                                int T, int k, const Experts& ex, const void* x, int xdtype,
+                                int32_t* idx, float* gates, void* y, int out_f32, void* ws,
+                                hipStream_t s);
 hipError_t launch_ffn_fast(const Experts& ex, const FfnArgs& a, hipStream_t s);
 // MFMA tiles of fast mode (experts with more than gmax assignments); writes x16.
 bool mfma_supported(int H, int I);

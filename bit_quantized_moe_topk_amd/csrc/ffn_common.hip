@@ -2,9 +2,10 @@
 //
 // y[t] = sum_{j<k} o[slot_of[t*k+j]] + o[slot_of[T*k+t]] (shared expert), in
 // that order, where o already carries the gate (the down kernels multiply by
-// it); fp32 sums, one rounding to y. This is the path for fp32 check mode and
-// for fast mode with many tokens; with few tokens the down kernels add straight
-// into an fp32 accumulator instead.
+// it); fp32 sums, one rounding to y. Every call form except the decode-window
+// kernels (which sum in LDS and write y themselves) ends with this gather:
+// check mode, the small-batch kernels and the prefill tiles all store one o
+// row per assignment slot (fp32 below 256 tokens, bf16 above).
 #include "common.h"
 
 namespace moe {

@@ -651,6 +651,21 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
 // launch; its last down role sets it back to zero and raises epoch. `guard`
 // is never written: non-zero means the head was not zeroed. `spin`: 0, or a
 // bound in wall-clock ticks on the down roles' wait (a testing aid).
+// Launches that start from hidden states (RT launches): rt_seq[r] counts
+// the RT launches on the workspace for router role r (the role adds one at its
+// start; an RT launch without that role has its last down role add it), and
+// rt_epoch counts them too (raised by each RT launch's last down role), so the
+// role's add returns the launch's number n = rt_epoch, however late the role
+// runs; launches that start from logits touch neither. The role tags
+// every logit it stores with n + 1 (tag and value in one 64-bit store), then
+// adds one to rt_all without waiting for the stores; the role that completes
+// rt_all sets it back to zero (router roles never wait, so it is zero between
+// launches) and writes n + 1 into the 16 go lines. The other workgroups watch
+// one go line each (few waves per line), then read the logits, again until
+// every tag shows their launch (the tags, not the order of the stores, make
+// the values current). A workgroup whose wait runs out writes epoch + 1 into
+// `poison` before it counts; down roles that find it after their own wait
+// write NaN, so no launch mixes routings.
 constexpr int kSyncGroup = 16;   // workgroups per counter
 constexpr int kSyncLine = 32;    // uint32 per 128-byte line
 struct WinSync {
@@ -659,11 +674,26 @@ struct WinSync {
   uint32_t epoch[kSyncLine];     // launches completed
   uint32_t dn_all[kSyncLine];    // down roles finished (this launch)
   uint32_t up[16][kSyncLine];    // gate/up roles of group g whose h is released
+  uint32_t rt_epoch[kSyncLine];  // RT launches completed
+  uint32_t rt_seq[kSyncLine];    // RT launches seen by router role r (r < 32)
+  uint32_t rt_all[kSyncLine];    // router roles whose logits are issued (this launch)
+  uint32_t go[16][kSyncLine];    // n + 1 once every router role of launch n has issued its logits
+  uint32_t poison[kSyncLine];    // epoch + 1: a workgroup of that launch routed without logits
 };
 static_assert(sizeof(WinSync) <= kWinSyncBytes, "the window counters fit the workspace head");
 
 constexpr int kLayerPer = 8;  // logits per lane in the one-launch window: E <= 512
 constexpr long long kWinSpinTicks = 1ll << 24;  // wall-clock ticks a down role waits for h at most
+constexpr int kRtExperts = 2 * kWinWaves;       // experts per router role (two per wave)
+static_assert(64 * kLayerPer <= kSyncLine * kRtExperts, "a launch counter per router role");
+
+// A logit of the launch numbered n - 1 as stored by a router role: tag n in
+// the high word, the value's bits in the low word (one 64-bit store).
+__device__ inline void store_tagged(uint64_t* p, uint32_t tag, float v, float* plain) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  if (plain) *plain = v;
+}
 
 __device__ inline uint32_t sync_load(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -675,6 +705,136 @@ __device__ inline void sync_zero(uint32_t* p) {
   __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Router role r for bf16 x (matrix cores): the logits of experts 16 r ..
+// 16 r + 15 for the window's tokens. Wave w takes K slice w of H / 8 and runs
+// kM = H / 256 v_mfma_f32_16x16x32_bf16 on it (router rows as the 16 rows of
+// A, tokens as the columns of B, tokens past T zero): lane (i, c) = (lane %
+// 16, lane / 16) feeds 8 elements of row i per product from its own
+// contiguous quarter of the slice, for the router row and for the token row
+// alike (the same K permutation on both operands). Every load is issued at
+// entry. Products of bf16 values are exact in f32; the eight slices' partial
+// tiles are added in LDS in wave order, so the logits are reproducible.
+template <int NBG>
+__device__ inline void router_role_mma(int r, const uint16_t* __restrict__ x, int T, int H,
+                                       const uint16_t* __restrict__ rw,
+                                       const float* __restrict__ rbias, int E, uint32_t tag,
+                                       uint64_t* lgp, float* lg, float* red) {
+  constexpr int kM = 4 * NBG;  // products per wave (H = 1024 NBG)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, c = lane >> 4;
+  const int kq = H / 32;                            // elements of one lane quarter of a slice
+  const int k0 = wave * (H / 8) + c * kq;           // this lane's first element
+  const int e = min(kRtExperts * r + i, E - 1);
+  const uint4* wr = reinterpret_cast<const uint4*>(rw + (size_t)e * H + k0);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)min(i, T - 1) * H + k0);
+  uint4 wv[kM], xv[kM];
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    wv[m] = wr[m];
+    xv[m] = i < T ? xr[m] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const int eo = kRtExperts * r + (tid >> 2);  // expert and token of this thread's sum below
+  const float b = (tid < 64 && rbias && eo < E) ? rbias[eo] : 0.f;
+  floatx4_t acc = {};
+#pragma unroll
+  for (int m = 0; m < kM; ++m)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[m]),
+                                                  __builtin_bit_cast(bf16x8_t, xv[m]), acc, 0, 0, 0);
+  // acc[v]: expert 4 c + v of the role's 16, token i
+  if (i < kWinT) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * c + v) * kWinT + i] = acc[v];
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int el = tid >> 2, t = tid & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWinWaves; ++w) v += red[(w * 16 + el) * kWinT + t];
+    if (t < T && eo < E)
+      store_tagged(lgp + (size_t)t * E + eo, tag, v + b, lg ? lg + (size_t)t * E + eo : nullptr);
+  }
+}
+
+// Router role r of a launch that starts from hidden states: the router scores
+// ("Strata - the details", "How it works": each layer's router runs on the
+// GPU in front of its experts) of experts 16 r .. 16 r + 15 for the window's
+// tokens, logits[t][e] = x[t] . w[e] (+ bias[e]), stored agent-coherent into
+// lg [T][E]. Wave w takes experts 16 r + 2 w and 16 r + 2 w + 1: its router
+// rows' 16-byte chunks lane + 64 j (8 elements each) come into registers
+// first, the window's rows into LDS as f32 meanwhile; each lane runs an fp32
+// fma chain over its chunks and a fixed-order wave sum finishes every dot, so
+// the logits are reproducible (the error of an f32 sum of H products).
+template <bool XF32>
+__device__ inline void router_role(int r, const void* x, int T, int H, const uint16_t* __restrict__ rw,
+                                   const float* __restrict__ rbias, int E, uint32_t tag, uint64_t* lgp,
+                                   float* lg, float* xsf) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kU = kMmaMaxH / 512;
+  const int nu = H / 512;
+  uint4 wv[2][kU];
+  int e[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    e[i] = kRtExperts * r + 2 * wave + i;
+    const uint4* row = reinterpret_cast<const uint4*>(rw + (size_t)min(e[i], E - 1) * H);
+#pragma unroll
+    for (int j = 0; j < kU; ++j) wv[i][j] = j < nu ? row[lane + 64 * j] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  for (int i = tid; i < T * (H / 4); i += kWinThreads) {
+    const int t = i / (H / 4), q = i - t * (H / 4);
+    float4 f;
+    if (XF32) {
+      f = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)t * H)[q];
+    } else {
+      const uint2 u = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (size_t)t * H)[q];
+      f = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+    }
+    reinterpret_cast<float4*>(xsf)[i] = f;
+  }
+  __syncthreads();
+  float acc[2][kWinT] = {};
+#pragma unroll
+  for (int j = 0; j < kU; ++j) {
+    if (j < nu) {
+      const int q = lane + 64 * j;  // elements 8 q .. 8 q + 7
+#pragma unroll
+      for (int t = 0; t < kWinT; ++t) {
+        if (t < T) {
+          const float4 a = reinterpret_cast<const float4*>(xsf + t * H + 8 * q)[0];
+          const float4 b = reinterpret_cast<const float4*>(xsf + t * H + 8 * q)[1];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const uint4 w = wv[i][j];
+            float v = acc[i][t];
+            v = fmaf(a.x, bf16_lo(w.x), v);
+            v = fmaf(a.y, bf16_hi(w.x), v);
+            v = fmaf(a.z, bf16_lo(w.y), v);
+            v = fmaf(a.w, bf16_hi(w.y), v);
+            v = fmaf(b.x, bf16_lo(w.z), v);
+            v = fmaf(b.y, bf16_hi(w.z), v);
+            v = fmaf(b.z, bf16_lo(w.w), v);
+            v = fmaf(b.w, bf16_hi(w.w), v);
+            acc[i][t] = v;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float b = (rbias && e[i] < E) ? rbias[e[i]] : 0.f;
+#pragma unroll
+    for (int t = 0; t < kWinT; ++t) {
+      if (t < T) {
+        const float v = wave_sum(acc[i][t]) + b;
+        if (lane == 0 && e[i] < E)
+          store_tagged(lgp + (size_t)t * E + e[i], tag, v, lg ? lg + (size_t)t * E + e[i] : nullptr);
+      }
+    }
+  }
+}
+
 // The whole window in one launch on the matrix cores (H a multiple of 1,024 up
 // to 4,096; I 256 or 512). Every workgroup routes the window itself (top-k of
 // T logit rows, a few KB, and the active-expert list in LDS). Workgroups
@@ -683,11 +843,17 @@ __device__ inline void sync_zero(uint32_t* p) {
 // waits until every gate/up role has released h. Workgroups are dispatched in
 // index order, so a waiting down role never holds back a gate/up role; the
 // wait is also bounded in time, past which the role writes NaN rows.
-template <int Q, bool XF32, int NBG, int NBD>
+//
+// RT (start from hidden states): NR = E / 16 router roles come first and
+// store the logits into lg; every other workgroup waits for them (bounded as
+// above) before its top-k. A router wait that runs out routes the window to
+// experts 0 .. k-1 with NaN gates, so its rows become NaN while every count
+// stays balanced. Without RT, lg holds the caller's logits.
+template <int Q, bool XF32, int NBG, int NBD, bool RT>
 __global__ __launch_bounds__(kWinThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const void* x,
-               int32_t* idx_out, float* gates_out, uint16_t* hwin, void* y, int out_f32,
-               WinSync* sync) {
+void win_layer(float* lg, uint64_t* lgp, const uint16_t* __restrict__ rw, const float* __restrict__ rbias,
+               int T, int k, Experts ex, const void* x, int32_t* idx_out, float* gates_out,
+               uint16_t* hwin, void* y, int out_f32, WinSync* sync) {
   __shared__ LayerRoute R;
   // gate/up roles: activations (fp16, 32 KB) and partial tiles (16 KB); down roles: h
   __shared__ __attribute__((aligned(16))) char buf[kHsBytes];
@@ -701,9 +867,28 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
   const int tid = threadIdx.x;
   const int H = ex.H;
   const int G = ex.I / 16 * kMmaSlices, D = H / 16;
-  const int role = blockIdx.x;
+  const int NR = RT ? (ex.E + kRtExperts - 1) / kRtExperts : 0;
+  if (RT && (int)blockIdx.x < NR) {
+    __shared__ uint32_t tag_s;
+    if (tid == 0) tag_s = sync_add(&sync->rt_seq[blockIdx.x]) + 1u;
+    __syncthreads();
+    const uint32_t tag = tag_s;
+    if constexpr (XF32)
+      router_role<true>(blockIdx.x, x, T, H, rw, rbias, ex.E, tag, lgp, lg, reinterpret_cast<float*>(buf));
+    else
+      router_role_mma<NBG>(blockIdx.x, static_cast<const uint16_t*>(x), T, H, rw, rbias, ex.E, tag, lgp,
+                           lg, reinterpret_cast<float*>(buf));
+    __syncthreads();  // every wave's stores are issued
+    if (tid == 0 && sync_add(sync->rt_all) == (uint32_t)(NR - 1)) {
+      sync_zero(sync->rt_all);
+      for (int g = 0; g < 16; ++g)
+        __hip_atomic_store(sync->go[g], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  const int role = blockIdx.x - NR;
 
-  win_topk<kLayerPer>(R, logits, T, ex.E, k);
+  if (!RT) win_topk<kLayerPer>(R, lg, T, ex.E, k);
   // the window's activations -> LDS fp16 in the MFMA K order (tokens >= T
   // zero), by the waves that do not select experts, one token row per wave:
   // the row is scaled by 2^-e (row_exp of its largest |x|), e kept in xe_w
@@ -760,7 +945,62 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
     head_s[1] = sync_load(sync->spin);
     head_s[2] = sync_load(sync->epoch);
   }
+  __shared__ int rt_bad_w[kWinT];
+  if (RT) {
+    // lane 0 of wave 0 watches go line role % 16 (with pauses) until it shows
+    // this launch; then wave t < T reads token t's tagged logits
+    // (agent-coherent, all in flight at once) until every tag shows it too,
+    // and selects its experts from those values. Both waits are bounded like
+    // the down roles' wait; a wave that gives up routes to experts 0 .. k-1
+    // with NaN gates.
+    const int wave = tid >> 6, lane = tid & 63;
+    const uint32_t want = sync_load(sync->rt_epoch) + 1u;
+    const uint32_t sp = sync_load(sync->spin);
+    const long long spin = sp ? (long long)sp : kWinSpinTicks;
+    const long long t0 = wall_clock64();
+    if (tid == 0) {
+      const uint32_t* go = sync->go[role % 16];
+      while (sync_load(go) != want && wall_clock64() - t0 <= spin) __builtin_amdgcn_s_sleep(2);
+    }
+    __syncthreads();
+    if (wave < T) {
+      const uint64_t* l = lgp + (size_t)wave * ex.E;
+      float raw[kLayerPer];
+      bool bad = false;
+      for (;;) {
+        bool mine = true;
+#pragma unroll
+        for (int i = 0; i < kLayerPer; ++i) {
+          const uint64_t v = __hip_atomic_load(l + min(lane + 64 * i, ex.E - 1), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          mine = mine && (uint32_t)(v >> 32) == want;
+          raw[i] = __uint_as_float((uint32_t)v);
+        }
+        if (__ballot(!mine) == 0) break;
+        if (wall_clock64() - t0 > spin) {
+          bad = true;
+          break;
+        }
+      }
+      if (!bad) {
+        topk_select<kLayerPer>(raw, ex.E, k, R.lidx + wave * k, R.lgate + wave * k, &R.tks[wave]);
+      } else {
+        for (int j = lane; j < k; j += 64) {
+          R.lidx[wave * k + j] = j;
+          R.lgate[wave * k + j] = __uint_as_float(0x7FC00000u);
+        }
+      }
+      if (lane == 0) rt_bad_w[wave] = bad;
+    }
+  }
   const int n_act = win_list(R, ex, T, k, false, nullptr, nullptr, nullptr);  // ends with a barrier
+  if (RT && tid == 0) {
+    bool bad = false;
+    for (int t = 0; t < T; ++t) bad = bad || rt_bad_w[t];
+    // counted below (gate/up roles) behind their vmcnt(0); down roles' rows are NaN anyway
+    if (bad)
+      __hip_atomic_store(sync->poison, head_s[2] + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   if (head_s[0] != 0u) {  // the head was not zeroed: y becomes NaN
     for (int i = tid; i < T * H; i += kWinThreads) {
@@ -805,6 +1045,9 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
         }
         __builtin_amdgcn_s_sleep(4);
       }
+      // a workgroup of this launch that routed without the logits wrote the
+      // poison word before it counted
+      if (RT && !bad && lane == 0) bad = sync_load(sync->poison) == head_s[2] + 1u;
       if (lane == 0) bad_s = bad;
     }
     __syncthreads();
@@ -818,6 +1061,10 @@ void win_layer(const float* __restrict__ logits, int T, int k, Experts ex, const
     // groups this launch's shape has none of, reset the down count, close the
     // launch
     for (int g = G / kSyncGroup; g < 16; ++g) sync_add(sync->up[g], (uint32_t)kSyncGroup);
+    if (RT) {
+      for (int r = NR; r < kSyncLine; ++r) sync_add(&sync->rt_seq[r]);
+      sync_add(sync->rt_epoch);
+    }
     sync_zero(sync->dn_all);
     sync_add(sync->epoch);
   }
@@ -839,14 +1086,16 @@ hipError_t launch_w(const float* logits, int T, int k, const Experts& ex, const 
   return hipGetLastError();
 }
 
-template <int Q, bool XF32>
-hipError_t launch_layer(const float* logits, int T, int k, const Experts& ex, const void* x,
-                        int32_t* idx, float* gates, uint16_t* hwin, void* y, int out_f32,
-                        WinSync* sync, hipStream_t s) {
-  const dim3 grid(ex.I / 16 * kMmaSlices + ex.H / 16);
+template <int Q, bool XF32, bool RT>
+hipError_t launch_layer(float* lg, uint64_t* lgp, const uint16_t* rw, const float* rbias, int T, int k,
+                        const Experts& ex, const void* x, int32_t* idx, float* gates, uint16_t* hwin,
+                        void* y, int out_f32, WinSync* sync, hipStream_t s) {
+  const int NR = RT ? (ex.E + kRtExperts - 1) / kRtExperts : 0;
+  const dim3 grid(NR + ex.I / 16 * kMmaSlices + ex.H / 16);
+  const char* name = RT ? "win_layer_rt" : "win_layer";
 #define L(NBG, NBD)                                                                               \
-  MOE_LAUNCH("win_layer", s, (win_layer<Q, XF32, NBG, NBD>), grid, dim3(kWinThreads), 0, s, logits, \
-             T, k, ex, x, idx, gates, hwin, y, out_f32, sync)
+  MOE_LAUNCH(name, s, (win_layer<Q, XF32, NBG, NBD, RT>), grid, dim3(kWinThreads), 0, s, lg, lgp, \
+             rw, rbias, T, k, ex, x, idx, gates, hwin, y, out_f32, sync)
   const int nbg = ex.H / 1024, nbd = ex.I / 256;
   if (nbg == 1 && nbd == 1) L(1, 1);
   else if (nbg == 1) L(1, 2);
@@ -912,11 +1161,14 @@ hipError_t launch_window(const float* logits, int T, int k, const Experts& ex, c
   uint16_t* hwin = reinterpret_cast<uint16_t*>(base + L.h);
   if (win_mma_ok(ex, T, k)) {
     WinSync* sync = reinterpret_cast<WinSync*>(base + L.sync);
+    float* lg = const_cast<float*>(logits);  // read only without RT
     if (ex.qtype == 3)
-      return xdtype == 0 ? launch_layer<3, true>(logits, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s)
-                         : launch_layer<3, false>(logits, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s);
-    return xdtype == 0 ? launch_layer<2, true>(logits, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s)
-                       : launch_layer<2, false>(logits, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s);
+      return xdtype == 0
+                 ? launch_layer<3, true, false>(lg, nullptr, nullptr, nullptr, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s)
+                 : launch_layer<3, false, false>(lg, nullptr, nullptr, nullptr, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s);
+    return xdtype == 0
+               ? launch_layer<2, true, false>(lg, nullptr, nullptr, nullptr, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s)
+               : launch_layer<2, false, false>(lg, nullptr, nullptr, nullptr, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s);
   }
   const int bh = ex.H / 32, bi = ex.I / 32;
   if (ex.qtype == 3)
@@ -924,6 +1176,28 @@ hipError_t launch_window(const float* logits, int T, int k, const Experts& ex, c
                        : launch_wq<3, false>(bh, bi, logits, T, k, ex, x, idx, gates, meta, hwin, y, out_f32, s);
   return xdtype == 0 ? launch_wq<2, true>(bh, bi, logits, T, k, ex, x, idx, gates, meta, hwin, y, out_f32, s)
                      : launch_wq<2, false>(bh, bi, logits, T, k, ex, x, idx, gates, meta, hwin, y, out_f32, s);
+}
+
+bool window_hidden_supported(const Experts& ex, int T, int k) {
+  return window_supported(ex, T, k) && win_mma_ok(ex, T, k);
+}
+
+hipError_t launch_window_hidden(float* lg, uint64_t* lgp, const uint16_t* rw, const float* rbias,
+                                int T, int k, const Experts& ex, const void* x, int xdtype,
+                                int32_t* idx, float* gates, void* y, int out_f32, void* ws,
+                                hipStream_t s) {
+  if (!window_hidden_supported(ex, T, k)) return hipErrorInvalidValue;
+  const WinLayout L = win_layout(ex, T, k);
+  char* base = static_cast<char*>(ws);
+  uint16_t* hwin = reinterpret_cast<uint16_t*>(base + L.h);
+  WinSync* sync = reinterpret_cast<WinSync*>(base + L.sync);
+  if (ex.qtype == 3)
+    return xdtype == 0
+               ? launch_layer<3, true, true>(lg, lgp, rw, rbias, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s)
+               : launch_layer<3, false, true>(lg, lgp, rw, rbias, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s);
+  return xdtype == 0
+             ? launch_layer<2, true, true>(lg, lgp, rw, rbias, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s)
+             : launch_layer<2, false, true>(lg, lgp, rw, rbias, T, k, ex, x, idx, gates, hwin, y, out_f32, sync, s);
 }
 
 }  // namespace moe

@@ -264,6 +264,34 @@ int moe_layer(const float *logits, const void *x, int32_t xdtype, int32_t T, con
               int32_t k, int32_t *idx, float *gates, void *y, int32_t mode, void *ws,
               size_t ws_bytes, void *stream);
 
+/* ---- whole layer from hidden states --------------------------------------- */
+
+/* Workspace bytes moe_layer_hidden needs: moe_layer's plus room for the
+ * logits ([T][E] float32). */
+size_t moe_layer_hidden_workspace_size(const moe_experts *ex, int32_t T, int32_t k, int32_t mode);
+
+/* The layer from the tokens' hidden states: the router product
+ * (moe_router_logits: logits[t][e] = x[t] . w_router[e] (+ bias[e]); "Strata -
+ * the details", "How it works": each layer's router runs on the GPU in front
+ * of its experts), then moe_layer on those logits. x: [T][H] as for moe_layer
+ * (also the router's input); w_router: [E][H] bf16 (16-byte aligned); bias:
+ * [E] float32 or NULL; logits: [T][E] float32 output, or NULL to keep them in
+ * the workspace. idx, gates, y, mode and the workspace head as moe_layer; ws at
+ * least moe_layer_hidden_workspace_size bytes.
+ *
+ * A decode window that moe_layer runs as one kernel runs here as one kernel
+ * too: its first E / 16 workgroups compute the logits (an f32 sum of H
+ * products per entry, in a fixed order) and store them; the other workgroups
+ * wait for them through counters in the head (bounded like the window's other
+ * wait; a wait that runs out makes y NaN and idx 0 .. k-1) and route from
+ * them. Other calls launch the router product and then moe_layer. In either
+ * form idx and gates are the top-k of the logits written.
+ * Requires what moe_router_logits requires of H and E (else
+ * MOE_ERR_UNSUPPORTED); other errors as moe_layer. */
+int moe_layer_hidden(const void *x, int32_t xdtype, int32_t T, const uint16_t *w_router,
+                     const float *bias, const moe_experts *ex, int32_t k, int32_t *idx, float *gates,
+                     void *y, float *logits, int32_t mode, void *ws, size_t ws_bytes, void *stream);
+
 /* ---- whole layer without allocation --------------------------------------- */
 
 /* Bytes of the library's own scratch array per GPU (moe_layer_static). */
