@@ -440,6 +440,57 @@ def run_prefill(cfg, args, n_layers: int, K: int, workload: str):
     return res
 
 
+def fp8_variant(args, reps: int = 10) -> dict:
+    """One expert's gate/up + SwiGLU over the 8,192-token chunk on the FP8
+    matrix cores (moe_expert_gateup_fp8: operand preparation + the product
+    kernel), beside the layer's fp16 tiles on the same work (moe_ffn_q with
+    every token routed to that one expert; its gate/up kernel)."""
+    import torch
+    import bit_quantized_moe_topk_amd as moe
+    from synth import CONFIGS
+    from synth.gen import make_expert_planes, make_x
+    cfg = CONFIGS[3]
+    codes, hi, dm = make_expert_planes(cfg, args.seed, 0, cfg.E)  # the shared expert of layer 0
+    dev = "cuda"
+    ct = torch.from_numpy(np.ascontiguousarray(codes)).to(dev)
+    ht = None if hi is None else torch.from_numpy(np.ascontiguousarray(hi)).to(dev)
+    dt = torch.from_numpy(np.ascontiguousarray(dm).view(np.int16)).to(dev)
+    ex = moe.Experts(cfg.qtype, 1, False, cfg.H, cfg.I, ct, ht, dt)
+    x = torch.from_numpy(make_x(cfg, args.seed, 0).view(np.int16)).to(dev).view(torch.bfloat16)
+    T = cfg.T
+    idx = torch.zeros((T, 1), dtype=torch.int32, device=dev)
+    gates = torch.ones((T, 1), dtype=torch.float32, device=dev)
+    ws = torch.empty(int(moe.lib().moe_expert_gateup_fp8_workspace_size(ex.handle, T)),
+                     dtype=torch.uint8, device=dev)
+    moe.expert_gateup_fp8(x, ex, 0, workspace=ws)
+    moe.ffn_q(x, ex, idx, gates, mode="fast")
+    torch.cuda.synchronize()
+    moe.profile_begin(64 * reps)
+    gpu_hold(5.0)
+    for _ in range(reps):
+        moe.expert_gateup_fp8(x, ex, 0, workspace=ws)
+    torch.cuda.synchronize()
+    gpu_hold(5.0)
+    for _ in range(reps):
+        moe.ffn_q(x, ex, idx, gates, mode="fast")
+    torch.cuda.synchronize()
+    prof = moe.profile_end()
+    ex.close()
+    us = {k: round(1e3 * v[1] / max(v[0], 1), 1) for k, v in prof.items()}
+    flops = 2.0 * 2 * cfg.I * cfg.H * T
+    tf = lambda k: round(flops / (us[k] * 1e-6) / 1e12, 1) if us.get(k) else None  # noqa: E731
+    return {
+        "workload": f"gate/up + SwiGLU of one Q{cfg.qtype} expert (hidden {cfg.H}, intermediate "
+                    f"{cfg.I}) over {T} tokens: {flops / 1e9:.1f} GFLOP",
+        "kernels_us": us,
+        "fp8_gateup_TFLOP_s": tf("fp8_gateup"),
+        "fp16_tiles_gateup_TFLOP_s": tf("mfma_gateup"),
+        "fp8_with_operand_prep_us": round(sum(us.get(k, 0.0) for k in ("fp8_codes", "fp8_x", "fp8_gateup")), 1),
+        "accuracy": "per-row rel-L2 of h against the float64 oracle ~1e-5 (tests/test_gpu_fp8.py); "
+                    "the fp16 tiles ~3e-3",
+    }
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -554,6 +605,8 @@ def measured_peaks(reps: int = 5) -> dict:
     P.peaks_mfma_loop.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     P.peaks_mfma_loop_flops.argtypes = [C.c_int, C.c_int]
     P.peaks_mfma_loop_flops.restype = C.c_double
+    P.peaks_mfma_loop_fp8_flops.argtypes = [C.c_int, C.c_int]
+    P.peaks_mfma_loop_fp8_flops.restype = C.c_double
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = 2 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -571,7 +624,7 @@ def measured_peaks(reps: int = 5) -> dict:
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
     res = {"copy_GBps": round(copy_gbs, 1), "copy_bytes": f"{reps} copies of 2 GiB, read + write"}
-    for bf, name in ((1, "bf16"), (0, "f16")):
+    for bf, name in ((1, "bf16"), (0, "f16"), (2, "fp8")):
         if P.peaks_mfma_loop(bf, blocks, iters, C.c_void_p(out.data_ptr()), stream):
             raise RuntimeError("peaks_mfma_loop failed")
         torch.cuda.synchronize()
@@ -580,10 +633,10 @@ def measured_peaks(reps: int = 5) -> dict:
             P.peaks_mfma_loop(bf, blocks, iters, C.c_void_p(out.data_ptr()), stream)
         ev1.record()
         torch.cuda.synchronize()
-        fl = P.peaks_mfma_loop_flops(blocks, iters) * reps
+        fl = (P.peaks_mfma_loop_fp8_flops if bf == 2 else P.peaks_mfma_loop_flops)(blocks, iters) * reps
         res[f"mfma_loop_{name}_TFLOPs"] = round(fl / (ev0.elapsed_time(ev1) * 1e-3) / 1e12, 1)
     res["mfma_loop"] = (f"{blocks} workgroups x 4 waves, {iters} rounds of 4 independent "
-                        "32x32x16 products on register operands")
+                        "32x32x16 (bf16, f16) or 32x32x64 (fp8) products on register operands")
     return res
 
 
@@ -621,6 +674,7 @@ def main() -> int:
                     help="distinct layers of the 1,024-token chunk (0 = skip it)")
     ap.add_argument("--prefill-1k-steps", type=int, default=5)
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy/MFMA peaks")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 matrix-core gate/up variant")
     ap.add_argument("--cpu-full", action="store_true",
                     help="run every CPU oracle workload in full (no row samples; takes minutes)")
     ap.add_argument("--no-tiled", action="store_true",
@@ -740,6 +794,11 @@ def main() -> int:
     router = router_timing(args)
     log(f"router: {router}")
 
+    f8 = None
+    if not args.no_fp8:
+        f8 = fp8_variant(args)
+        log(f"fp8 variant: {f8}")
+
     cpu = None
     if not args.no_cpu_baseline and hosts:
         cpu = cpu_baseline(cfg, hosts, args)
@@ -782,6 +841,7 @@ def main() -> int:
         "batched_decode_q3": bat,
         "batched_decode_q3_stream_ranking": bat_own,
         "router": router,
+        "fp8_gateup_variant": f8,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -77,6 +77,10 @@ def lib() -> C.CDLL:
         L.moe_layer.restype = C.c_int
         L.moe_layer_static.argtypes = [P, P, i32, i32, P, i32, P, P, P, i32, P]
         L.moe_layer_static.restype = C.c_int
+        L.moe_expert_gateup_fp8_workspace_size.argtypes = [P, i32]
+        L.moe_expert_gateup_fp8_workspace_size.restype = sz
+        L.moe_expert_gateup_fp8.argtypes = [P, i32, P, i32, P, P, sz, P]
+        L.moe_expert_gateup_fp8.restype = C.c_int
         L.moe_layer_hidden_workspace_size.argtypes = [P, i32, i32, i32]
         L.moe_layer_hidden_workspace_size.restype = sz
         L.moe_layer_hidden.argtypes = [P, i32, i32, P, P, P, i32, P, P, P, P, i32, P, sz, P]
@@ -388,6 +392,23 @@ def layer_hidden(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor | N
         _ptr(idx), _ptr(gates), _ptr(y), _ptr(logits), mode, _ptr(workspace), workspace.numel(),
         _stream()))
     return idx, gates, y, logits
+
+
+def expert_gateup_fp8(x: torch.Tensor, ex: "Experts", expert: int,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_expert_gateup_fp8: h = silu(g) * u of one expert for every row of
+    x (bf16 [T, H]) on the FP8 matrix cores (a measured variant): f32 [T, I]."""
+    _need_cuda("x", x, torch.bfloat16)
+    T, H = x.shape
+    if H != ex.H:
+        raise ValueError("x does not match the experts' H")
+    h = torch.empty((T, ex.I), dtype=torch.float32, device=x.device)
+    n = int(lib().moe_expert_gateup_fp8_workspace_size(ex.handle, T))
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_expert_gateup_fp8", lib().moe_expert_gateup_fp8(
+        _ptr(x), T, ex.handle, expert, _ptr(h), _ptr(workspace), workspace.numel(), _stream()))
+    return h
 
 
 def layer_static(logits: torch.Tensor, x: torch.Tensor, ex: "Experts", k: int, mode="fast"):

@@ -408,6 +408,25 @@ int moe_layer_hidden(const void* x, int32_t xdtype, int32_t T, const uint16_t* w
   return moe_layer(lg, x, xdtype, T, ex, k, idx, gates, y, mode, ws, L.total, stream);
 }
 
+// ---- one expert's gate/up on the FP8 matrix cores (measured variant) ----------
+
+size_t moe_expert_gateup_fp8_workspace_size(const moe_experts* ex, int32_t T) {
+  if (!ex || T < 0) return 0;
+  return moe::fp8_gateup_workspace_bytes(ex->d, T);
+}
+
+int moe_expert_gateup_fp8(const void* x, int32_t T, const moe_experts* ex, int32_t expert, float* h,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!ex || T < 0 || expert < 0 || expert >= ex->d.E_tot) return MOE_ERR_INVALID_ARG;
+  if (!moe::fp8_gateup_supported(ex->d)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * ex->d.H > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !h || !aligned16(x)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe::fp8_gateup_workspace_bytes(ex->d, T)) return MOE_ERR_WORKSPACE;
+  return status_of(moe::launch_fp8_gateup(ex->d, expert, static_cast<const uint16_t*>(x), T, h, ws,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 // ---- whole layer without allocation ------------------------------------------

@@ -135,6 +135,13 @@ size_t window_workspace_bytes(const Experts& ex, int T, int k);
 hipError_t launch_window(const float* logits, int T, int k, const Experts& ex, const void* x,
                          int xdtype, int32_t* idx, float* gates, void* y, int out_f32, void* ws,
                          hipStream_t s);
+// Gate/up + SwiGLU of one expert on the FP8 matrix cores (a measured
+// variant, fp8.hip): workspace bytes, shapes it takes, launch.
+size_t fp8_gateup_workspace_bytes(const Experts& ex, int T);
+bool fp8_gateup_supported(const Experts& ex);
+hipError_t launch_fp8_gateup(const Experts& ex, int expert, const uint16_t* x, int T, float* h,
+                             void* ws, hipStream_t s);
+
 // The one-launch window starting from hidden states: router roles store the
 // logits [T][E] tagged with the launch into lgp (64-bit entries) and, when lg
 // is not null, plain into lg; then the window as launch_window. Only where

@@ -888,6 +888,14 @@ void win_layer(float* lg, uint64_t* lgp, const uint16_t* __restrict__ rw, const 
   }
   const int role = blockIdx.x - NR;
 
+  // the head's words are requested first (their round trip overlaps the
+  // activation and logit loads instead of following them)
+  uint32_t head_r[3] = {0u, 0u, 0u};
+  if (tid == kWinThreads - 64) {
+    head_r[0] = sync_load(sync->guard);
+    head_r[1] = sync_load(sync->spin);
+    head_r[2] = sync_load(sync->epoch);
+  }
   if (!RT) win_topk<kLayerPer>(R, lg, T, ex.E, k);
   // the window's activations -> LDS fp16 in the MFMA K order (tokens >= T
   // zero), by the waves that do not select experts, one token row per wave:
@@ -941,9 +949,9 @@ void win_layer(float* lg, uint64_t* lgp, const uint16_t* __restrict__ rw, const 
     }
   }
   if (tid == kWinThreads - 64) {
-    head_s[0] = sync_load(sync->guard);
-    head_s[1] = sync_load(sync->spin);
-    head_s[2] = sync_load(sync->epoch);
+    head_s[0] = head_r[0];
+    head_s[1] = head_r[1];
+    head_s[2] = head_r[2];
   }
   __shared__ int rt_bad_w[kWinT];
   if (RT) {

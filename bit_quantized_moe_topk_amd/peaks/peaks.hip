@@ -43,6 +43,28 @@ __global__ __launch_bounds__(256) void mfma_loop(int iters, float* out) {
   if (s == -1.0f) out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// The same loop on the FP8 matrix cores: v_mfma_scale_f32_32x32x64_f8f6f4
+// with E4M3 operands and unit scales, 2 * 32 * 32 * 64 = 131,072 flops each.
+__global__ __launch_bounds__(256) void mfma_loop_fp8(int iters, float* out) {
+  typedef int int8v_t __attribute__((ext_vector_type(8)));
+  const int lane = threadIdx.x & 63;
+  int8v_t a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = 0x38383838 + lane;  // E4M3 values near 1
+    b[i] = 0x30303030 + i;
+  }
+  floatx16_t acc[kChains] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 0, 0, 0, 127, 0, 127);
+  }
+  float s = 0.f;
+  for (int c = 0; c < kChains; ++c)
+    for (int v = 0; v < 16; ++v) s += acc[c][v];
+  if (s == -1.0f) out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -52,12 +74,19 @@ double peaks_mfma_loop_flops(int blocks, int iters) {
   return (double)blocks * 4 /* waves */ * iters * kChains * 32768.0;
 }
 
-// Launch the loop: `blocks` workgroups of 256 threads, bf16 (1) or fp16 (0)
-// operands, on `stream`. `out` (device, blocks * 256 floats) is never written
-// for the operands used here. Returns the hipError_t of the launch.
+// Flops one launch of the FP8 loop performs.
+double peaks_mfma_loop_fp8_flops(int blocks, int iters) {
+  return (double)blocks * 4 /* waves */ * iters * kChains * 131072.0;
+}
+
+// Launch the loop: `blocks` workgroups of 256 threads, bf16 (1), fp16 (0) or
+// FP8 (2) operands, on `stream`. `out` (device, blocks * 256 floats) is never
+// written for the operands used here. Returns the hipError_t of the launch.
 int peaks_mfma_loop(int bf16, int blocks, int iters, float* out, hipStream_t stream) {
   if (blocks <= 0 || iters <= 0 || out == nullptr) return (int)hipErrorInvalidValue;
-  if (bf16)
+  if (bf16 == 2)
+    hipLaunchKernelGGL(mfma_loop_fp8, dim3(blocks), dim3(256), 0, stream, iters, out);
+  else if (bf16)
     hipLaunchKernelGGL(mfma_loop<true>, dim3(blocks), dim3(256), 0, stream, iters, out);
   else
     hipLaunchKernelGGL(mfma_loop<false>, dim3(blocks), dim3(256), 0, stream, iters, out);

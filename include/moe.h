@@ -292,6 +292,26 @@ int moe_layer_hidden(const void *x, int32_t xdtype, int32_t T, const uint16_t *w
                      const float *bias, const moe_experts *ex, int32_t k, int32_t *idx, float *gates,
                      void *y, float *logits, int32_t mode, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- one expert's gate/up on the FP8 matrix cores (measured variant) -------- */
+
+/* Workspace bytes moe_expert_gateup_fp8 needs for T tokens. */
+size_t moe_expert_gateup_fp8_workspace_size(const moe_experts *ex, int32_t T);
+
+/* h[t][r] = silu(g) * u of expert `expert` (0 .. E + has_shared - 1) for every
+ * token row of x ([T][H] bf16, 16-byte aligned), g and u its gate and up
+ * products: the analogue of the pages' 8-bit tensor-core prompt kernels
+ * ("Strata - the details", "Speed (measured)") on the gfx950 FP8 matrix
+ * cores, kept as a measured variant beside the layer's fp16 prefill tiles.
+ * The codes enter the matrix cores as exact E4M3 values; each token row is
+ * scaled by a power of two and split into two E4M3 parts (hi + lo, about 8
+ * significant bits together); one product per 32-weight block, and d and m are
+ * applied per block in fp32. h: [T][I] float32. Requires H % 64 == 0,
+ * H <= 4096 and I % 32 == 0 (else MOE_ERR_UNSUPPORTED). ws: at least
+ * moe_expert_gateup_fp8_workspace_size bytes (no zeroing needed); it holds the
+ * E4M3 operands. Other errors as moe_ffn_q. */
+int moe_expert_gateup_fp8(const void *x, int32_t T, const moe_experts *ex, int32_t expert, float *h,
+                          void *ws, size_t ws_bytes, void *stream);
+
 /* ---- whole layer without allocation --------------------------------------- */
 
 /* Bytes of the library's own scratch array per GPU (moe_layer_static). */
