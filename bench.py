@@ -635,7 +635,7 @@ def measured_peaks(reps: int = 5) -> dict:
         torch.cuda.synchronize()
         fl = (P.peaks_mfma_loop_fp8_flops if bf == 2 else P.peaks_mfma_loop_flops)(blocks, iters) * reps
         res[f"mfma_loop_{name}_TFLOPs"] = round(fl / (ev0.elapsed_time(ev1) * 1e-3) / 1e12, 1)
-    res["mfma_loop"] = (f"{blocks} workgroups x 4 waves, {iters} rounds of 4 independent "
+    res["mfma_loop"] = (f"{blocks} workgroups x 4 waves, {iters} rounds of 8 independent "
                         "32x32x16 (bf16, f16) or 32x32x64 (fp8) products on register operands")
     return res
 

@@ -12,7 +12,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kChains = 4;  // independent accumulators per wave: the matrix pipe never waits
+constexpr int kChains = 8;  // independent accumulators per wave: the matrix pipe never waits
 
 // Every wave runs `iters` rounds of kChains products; each product is
 // 2 * 32 * 32 * 16 = 32,768 flops. The sum of the accumulators is written only
