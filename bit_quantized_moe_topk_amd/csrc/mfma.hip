@@ -40,9 +40,12 @@ namespace {
 constexpr int kBM = 128;          // assignments per tile
 constexpr int kBK = 64;           // K per stage
 // Activation stage in LDS: kBM rows of 64 halves (128 B), the eight 16-byte
-// chunks of row m stored at chunk position q ^ (m & 7), so that the 32 rows a
-// fragment read touches spread over all banks without padding rows (which
-// lets a wave's direct global-to-LDS load fill 8 whole rows).
+// chunks of row m stored at chunk position q ^ ((m >> 1) & 7). A fragment
+// read takes one logical chunk of 32 consecutive rows; 16 lanes at a time
+// are served from the 64 banks (256 bytes, two rows' worth), and with this
+// placement the 16 rows of such a group (8 even, 8 odd, each set on its own
+// half of the banks) hit every bank once. No padding rows, so a wave's
+// direct global-to-LDS load still fills 8 whole rows.
 constexpr int kRow = 64;
 // Epilogue staging per wave (16-bit outputs): down, 64 assignments x 64 rows
 // (stride 72); gate/up, 128 assignments x 32 rows (stride 40).
@@ -94,7 +97,7 @@ __device__ inline void stage_mma(const _Float16* xb, const WStage (&w)[2],
   const int lane = threadIdx.x & 63;
   // row 32 i + lane % 32, logical chunk 4 h + kk (h = lane / 32), swizzled
   const _Float16* ap = xb + (lane & 31) * kRow;
-  const int hq = 4 * (lane >> 5), sw = lane & 7;
+  const int hq = 4 * (lane >> 5), sw = (lane >> 1) & 7;  // ((row >> 1) & 7) of row lane % 32
   auto afrag = [](const _Float16* p) { return *reinterpret_cast<const op_t*>(p); };
   op_t af[2][NI], bf[2][2];
 #pragma unroll
@@ -256,14 +259,13 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
 
   // ---- activation cursor: wave w fills rows 8 (CH w + u) .. + 7 of a stage
   // (u < CH) with one direct global-to-LDS load each: lane l lands at chunk
-  // position l % 8 of row 8 (CH w + u) + l / 8, so it loads logical chunk
-  // q = (l % 8) ^ (l / 8). Logical chunk q of stage s holds K column
+  // position l % 8 of row m = 8 (CH w + u) + l / 8, so it loads logical chunk
+  // q = (l % 8) ^ ((m >> 1) & 7). Logical chunk q of stage s holds K column
   // 32 (s + S (q / 4)) + 8 (q % 4) (canonical planes) or 64 s + 8 q (tiled).
   const uint4* x4 = reinterpret_cast<const uint4*>(a16);
   uint32_t xoff[CH];      // next stage's source chunk in 16-byte units (~0u: row past M)
   int anext[CH];
   int xt = 0, xsg = 0;    // tile round and stage of the next activation load
-  const int xq = (lane & 7) ^ (lane >> 3);
   auto xrow = [&](int u) { return 8 * (CH * wave + u) + (lane >> 3); };
   auto xprep = [&](int r) {  // tile r's rows: permutation entries, not yet waited on
     const TileInfo t = tile_info(wm, offs, ex.E_tot, n_nt, item_of<kClasses>(r));
@@ -281,6 +283,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiles(Experts ex, FfnArgs a) {
         r = token_of(r, a.T, a.k);
         r = (unsigned)r < (unsigned)a.T ? r : -1;
       }
+      const int xq = (lane & 7) ^ ((xrow(u) >> 1) & 7);
       const int col = TILED ? 8 * xq : 32 * S * (xq >> 2) + 8 * (xq & 3);
       xoff[u] = r < 0 ? ~0u : (uint32_t)(((size_t)r * K + col) / 8);
     }
