@@ -375,6 +375,22 @@ def router_timing(args, reps: int = 50) -> dict:
         out[name] = {"kernel": kname, "us": round(us, 2), "router_bytes": cfg.E * cfg.H * 2,
                      "GB_s": round(cfg.E * cfg.H * 2 / (us * 1e-6) / 1e9, 1),
                      "TFLOP_s": round(flops / (us * 1e-6) / 1e12, 2)}
+        if cfg.T >= 256:  # router product + top-k: one launch, against the two kernels
+            for _ in range(3):
+                moe.router_topk(x, wt, bt, cfg.k)
+                moe.route_topk(moe.router_logits(x, wt, bt), cfg.k)
+            torch.cuda.synchronize()
+            moe.profile_begin(8 * reps)
+            gpu_hold(5.0)
+            for _ in range(reps):
+                moe.router_topk(x, wt, bt, cfg.k)
+            for _ in range(reps):
+                moe.route_topk(moe.router_logits(x, wt, bt), cfg.k)
+            torch.cuda.synchronize()
+            prof = moe.profile_end()
+            per = {kk: round(1e3 * v[1] / max(v[0], 1), 2) for kk, v in prof.items()}
+            out[name]["fused_router_topk_us"] = per.get("router_topk")
+            out[name]["separate_kernels_us"] = round(per.get("router_mfma", 0) + per.get("topk", 0), 2)
     return out
 
 

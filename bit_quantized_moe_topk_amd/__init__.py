@@ -77,6 +77,8 @@ def lib() -> C.CDLL:
         L.moe_layer.restype = C.c_int
         L.moe_layer_static.argtypes = [P, P, i32, i32, P, i32, P, P, P, i32, P]
         L.moe_layer_static.restype = C.c_int
+        L.moe_router_topk.argtypes = [P, i32, i32, i32, P, P, i32, i32, P, P, P, P]
+        L.moe_router_topk.restype = C.c_int
         L.moe_expert_gateup_fp8_workspace_size.argtypes = [P, i32]
         L.moe_expert_gateup_fp8_workspace_size.restype = sz
         L.moe_expert_gateup_fp8.argtypes = [P, i32, P, i32, P, P, sz, P]
@@ -159,6 +161,27 @@ def router_logits(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = 
                                                         _ptr(bias) if bias is not None else None,
                                                         E, _ptr(logits), _stream()))
     return logits
+
+
+def router_topk(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None, k: int):
+    """moe_router_topk: router product and top-k in one launch (bf16 x [T, H],
+    w bf16 [E, H]): returns (idx int32 [T, k], gates f32 [T, k], logits f32 [T, E])."""
+    _need_cuda("x", x, torch.bfloat16)
+    if w.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous CUDA bf16 (or 16-bit pattern) tensor [E, H]")
+    if bias is not None:
+        _need_cuda("bias", bias, torch.float32)
+    T, H = x.shape
+    E = w.shape[0]
+    if w.shape[1] != H or (bias is not None and bias.numel() != E):
+        raise ValueError("shape mismatch between x, w and bias")
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    gates = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check("moe_router_topk", lib().moe_router_topk(_ptr(x), BF16, T, H, _ptr(w),
+                                                    _ptr(bias) if bias is not None else None, E, k,
+                                                    _ptr(idx), _ptr(gates), _ptr(logits), _stream()))
+    return idx, gates, logits
 
 
 def route_topk(logits: torch.Tensor, k: int):

@@ -376,7 +376,23 @@ int moe_layer(const float* logits, const void* x, int32_t xdtype, int32_t T, con
                     ws_bytes - L.ffn, stream, xs_done);
 }
 
+// ---- router product + top-k in one launch ----------------------------------------
+
+int moe_router_topk(const void* x, int32_t xdtype, int32_t T, int32_t H, const uint16_t* w,
+                    const float* bias, int32_t E, int32_t k, int32_t* idx, float* gates, float* logits,
+                    void* stream) {
+  if (T < 0 || H < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (xdtype != MOE_F32 && xdtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!moe::router_topk_supported(xdtype, H, E, k)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * E > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w || !idx || !gates || !aligned16(x) || !aligned16(w)) return MOE_ERR_INVALID_ARG;
+  return status_of(moe::launch_router_topk(x, T, H, w, bias, E, k, logits, idx, gates,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 // ---- whole layer from hidden states -------------------------------------------
+
 
 size_t moe_layer_hidden_workspace_size(const moe_experts* ex, int32_t T, int32_t k, int32_t mode) {
   const size_t base = moe_layer_workspace_size(ex, T, k, mode);

@@ -128,6 +128,12 @@ constexpr size_t kWinSyncBytes = 8192;
 // Router product (router.hip): the matrix-core kernel from this many bf16 tokens.
 constexpr int kRouterMfmaMinT = 256;
 bool router_supported(int H, int E);
+// Router product and top-k in one launch for bf16 x (E 256 or 512, k <= 64):
+// idx, gates [T][k] as launch_topk of the product; logits [T][E] written when
+// not null.
+bool router_topk_supported(int xdtype, int H, int E, int k);
+hipError_t launch_router_topk(const void* x, int T, int H, const uint16_t* w, const float* bias, int E,
+                              int k, float* logits, int32_t* idx, float* gates, hipStream_t s);
 hipError_t launch_router(const void* x, int xdtype, int T, int H, const uint16_t* w,
                          const float* bias, int E, float* logits, hipStream_t s);
 bool window_supported(const Experts& ex, int T, int k);

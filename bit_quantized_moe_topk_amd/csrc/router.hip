@@ -165,7 +165,110 @@ __global__ __launch_bounds__(kRThreads) void router_mfma(const uint16_t* __restr
   }
 }
 
+// Router product and top-k in one launch (bf16 x, E = 256 NT): workgroup b
+// takes tokens 32 b .. 32 b + 31 against every expert, so the selection of
+// each of its tokens needs no other workgroup. Wave w computes experts
+// 32 NT w .. + 32 NT - 1 on v_mfma_f32_32x32x16_bf16 (router rows as A, tokens
+// as B) over K chunks of 128: lane (i, h) = (lane % 32, lane / 32) holds 64
+// contiguous elements of row i from half h of the chunk, for the router row and
+// for the token row alike (the same K permutation on both operands), all
+// loaded straight into registers one chunk ahead (each load instruction
+// touches 64 rows' lines, and every workgroup reads the whole router matrix:
+// at 8,192 tokens it measures about 5 times the router_mfma + topk pair, which
+// the layer calls use). The tiles go to LDS (rows
+// padded to E + 1 floats: the 32 token columns of a write then fall on
+// different banks); then each wave selects for four tokens: bias added, the
+// logits written out (coalesced) when asked for, top-k and gates as topk.h.
+constexpr int kRtTok = 32;     // tokens per workgroup
+constexpr int kRtKC = 128;     // K per chunk
+constexpr int kRtThreads = 512;
+
+template <int NT>
+__global__ __launch_bounds__(kRtThreads) void router_topk(const uint16_t* __restrict__ x, int T, int H,
+                                                          const uint16_t* __restrict__ w,
+                                                          const float* __restrict__ bias, int E, int k,
+                                                          float* __restrict__ logits, int32_t* __restrict__ idx,
+                                                          float* __restrict__ gates) {
+  constexpr int kE = 256 * NT;
+  __shared__ float ls[kRtTok][kE + 1];
+  __shared__ TopkScratch tks[kRtThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 31, h = lane >> 5;
+  const int t0 = blockIdx.x * kRtTok;
+  // this lane's 16-byte pieces: 8 per chunk (64 elements of half h)
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + i, T - 1) * H) + 8 * h;
+  const uint4* wr[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    wr[j] = reinterpret_cast<const uint4*>(w + (size_t)(32 * (NT * wave + j) + i) * H) + 8 * h;
+  const int nch = H / kRtKC;  // even (H % 256 == 0)
+  constexpr int kStep = kRtKC / 8;  // uint4 per row per chunk
+  uint4 xa[8], xb[8], wa[NT][8], wb[NT][8];
+  floatx16_t acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = floatx16_t{};
+  auto load = [&](int c, uint4 (&xv)[8], uint4 (&wv)[NT][8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xv[q] = xr[c * kStep + q];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wv[j][q] = wr[j][c * kStep + q];
+  };
+  auto compute = [&](const uint4 (&xv)[8], const uint4 (&wv)[NT][8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wv[j][q]),
+                                                         __builtin_bit_cast(bf16x8_t, xv[q]), acc[j], 0, 0, 0);
+  };
+  load(0, xa, wa);
+  for (int c = 0; c < nch; c += 2) {
+    load(c + 1, xb, wb);                  // nch is even: chunk c + 1 exists
+    compute(xa, wa);
+    load(min(c + 2, nch - 1), xa, wa);    // the last pass loads its own chunk again
+    compute(xb, wb);
+  }
+  // acc[j][v]: expert 32 (NT wave + j) + 8 (v / 4) + 4 h + v % 4, token i
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ls[i][32 * (NT * wave + j) + 8 * (v >> 2) + 4 * h + (v & 3)] = acc[j][v];
+  __syncthreads();
+  constexpr int kPer = kE / 64;
+#pragma unroll 1
+  for (int u = 0; u < kRtTok / (kRtThreads / 64); ++u) {
+    const int tl = wave * (kRtTok / (kRtThreads / 64)) + u, t = t0 + tl;
+    if (t >= T) break;
+    float raw[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = lane + 64 * q;
+      raw[q] = e < E ? ls[tl][e] + (bias ? bias[e] : 0.f) : 0.f;
+      if (logits && e < E) logits[(size_t)t * E + e] = raw[q];
+    }
+    topk_select<kPer>(raw, E, k, idx + (size_t)t * k, gates + (size_t)t * k, &tks[wave]);
+  }
+}
+
 }  // namespace
+
+bool router_topk_supported(int xdtype, int H, int E, int k) {
+  return xdtype != 0 && H % 256 == 0 && H <= kDotMaxH && (E == 256 || E == 512) && k >= 1 && k <= 64;
+}
+
+hipError_t launch_router_topk(const void* x, int T, int H, const uint16_t* w, const float* bias, int E,
+                              int k, float* logits, int32_t* idx, float* gates, hipStream_t s) {
+  const dim3 grid((T + kRtTok - 1) / kRtTok);
+  if (E == 512)
+    MOE_LAUNCH("router_topk", s, router_topk<2>, grid, dim3(kRtThreads), 0, s,
+               static_cast<const uint16_t*>(x), T, H, w, bias, E, k, logits, idx, gates);
+  else
+    MOE_LAUNCH("router_topk", s, router_topk<1>, grid, dim3(kRtThreads), 0, s,
+               static_cast<const uint16_t*>(x), T, H, w, bias, E, k, logits, idx, gates);
+  return hipGetLastError();
+}
 
 bool router_supported(int H, int E) { return H >= 256 && H % 256 == 0 && H <= kDotMaxH && E >= 1; }
 

@@ -559,7 +559,9 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
   // h of the round at r0 into half `half` of hs, straight into LDS (each
   // lane's 16 bytes land at the wave's base + 16 lane), no registers held;
   // every load in flight at once, agent-coherent (h was written in this
-  // launch on other CUs)
+  // launch on other CUs). Row (expert, token t)'s 16-byte chunk q lands at
+  // position q ^ t of the row, so the four token rows that a fragment read
+  // takes at one chunk sit on different banks.
   auto copy = [&](int r0, int half) {
     constexpr int kCopy = kHsHalf / 16 / kWinThreads;
     constexpr int kCoherent = 16;  // cache policy: agent scope
@@ -569,7 +571,7 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
 #pragma unroll
     for (int u = 0; u < kCopy; ++u)
       if (tid + u * kWinThreads < n16)
-        __builtin_amdgcn_global_load_lds(src + tid + u * kWinThreads,
+        __builtin_amdgcn_global_load_lds(src + ((tid + u * kWinThreads) ^ (((tid + u * kWinThreads) / (32 * NBL)) & (kWinT - 1))),
                                          (__attribute__((address_space(3))) void*)(dst + u * kWinThreads + 64 * wave),
                                          16, 0, kCoherent);
   };
@@ -596,12 +598,14 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
         if (p >= n_act) continue;
         // columns past T read token 0's row (finite; their gate is 0): no
         // branch, so all eight LDS reads of the expert issue together
-        const uint16_t* hp = hb + ((size_t)(p - r0) * kWinT + (tok ? r16 : 0)) * I;
+        const int tt = tok ? r16 : 0;
+        const uint16_t* hp = hb + ((size_t)(p - r0) * kWinT + tt) * I;
         bf16x8_t hv[NBL][4];
 #pragma unroll
         for (int b = 0; b < NBL; ++b)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) hv[b][t] = *reinterpret_cast<const bf16x8_t*>(hp + 32 * (kb0 + b) + 8 * t);
+          for (int t = 0; t < 4; ++t)
+            hv[b][t] = *reinterpret_cast<const bf16x8_t*>(hp + 8 * ((4 * (kb0 + b) + t) ^ tt));
         floatx4_t o = {};
 #pragma unroll
         for (int b = 0; b < NBL; ++b) {

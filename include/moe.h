@@ -264,6 +264,25 @@ int moe_layer(const float *logits, const void *x, int32_t xdtype, int32_t T, con
               int32_t k, int32_t *idx, float *gates, void *y, int32_t mode, void *ws,
               size_t ws_bytes, void *stream);
 
+/* Router product and top-k in one launch, for many bf16 tokens: the logits of
+ * moe_router_logits (written to `logits` [T][E] when not NULL) and their top-k
+ * and gates as moe_route_topk ("Strata - the details", "How it works": the
+ * router picks the experts that score highest), with no logits round trip
+ * through memory between the two. x: [T][H] bf16 (xdtype MOE_BF16), w: [E][H]
+ * bf16, both 16-byte aligned; bias: [E] float32 or NULL; idx, gates: [T][k].
+ * The logits are f32 sums of exact bf16 products (matrix cores, a fixed
+ * order), so idx and gates are exactly moe_route_topk of the logits written.
+ * Each workgroup takes 32 tokens against every expert, so it reads the whole
+ * router matrix from cache: measured at 8,192 tokens x 512 experts x 2,048 it
+ * takes about 5 times as long as moe_router_logits followed by moe_route_topk
+ * (which read the matrix once per 128 tokens on 4 times as many workgroups);
+ * the layer calls use those two.
+ * Requires H % 256 == 0, H <= 4096, E 256 or 512, 1 <= k <= 64 (else
+ * MOE_ERR_UNSUPPORTED); T == 0: no launch. */
+int moe_router_topk(const void *x, int32_t xdtype, int32_t T, int32_t H, const uint16_t *w,
+                    const float *bias, int32_t E, int32_t k, int32_t *idx, float *gates, float *logits,
+                    void *stream);
+
 /* ---- whole layer from hidden states --------------------------------------- */
 
 /* Workspace bytes moe_layer_hidden needs: moe_layer's plus room for the
@@ -284,8 +303,9 @@ size_t moe_layer_hidden_workspace_size(const moe_experts *ex, int32_t T, int32_t
  * products per entry, in a fixed order) and store them; the other workgroups
  * wait for them through counters in the head (bounded like the window's other
  * wait; a wait that runs out makes y NaN and idx 0 .. k-1) and route from
- * them. Other calls launch the router product and then moe_layer. In either
- * form idx and gates are the top-k of the logits written.
+ * them. Other calls launch the router product and then moe_layer (for many
+ * tokens that is faster than moe_router_topk's single launch, see there). In
+ * every form idx and gates are the top-k of the logits written.
  * Requires what moe_router_logits requires of H and E (else
  * MOE_ERR_UNSUPPORTED); other errors as moe_layer. */
 int moe_layer_hidden(const void *x, int32_t xdtype, int32_t T, const uint16_t *w_router,

@@ -89,6 +89,8 @@ def check_hidden(lay, w, bias, idx, gates, y, lg, mode, rows=None, name=""):
     ("check T=4", 1, {}, "check"),
     ("batched Q3 T=64", 4, {}, "fast"),
     ("prefill 1K", 2, {}, "fast"),
+    ("prefill T=300 (ragged)", 2, dict(T=300), "fast"),
+    ("check T=300", 2, dict(T=300), "check"),
 ])
 def test_layer_hidden(name, cid, kw, mode):
     torch = torch_cuda()

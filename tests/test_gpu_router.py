@@ -57,3 +57,41 @@ def test_router_parity(cid, T, E):
     idx_o, gates_o = oracle.route(got_np, cfg.k)
     assert np.array_equal(idx.cpu().numpy(), idx_o)
     assert np.max(np.abs(gates.cpu().numpy() - gates_o)) <= 1e-6
+
+
+@pytest.mark.parametrize("cid,T,E,k", [(3, None, None, None), (2, 300, None, None), (2, 512, 256, 8),
+                                       (2, 33, None, 64)])
+def test_router_topk_fused(cid, T, E, k):
+    """moe_router_topk: the logits within the float32 bound of the oracle's
+    product, idx and gates exactly the top-k of the logits written, and equal
+    to the separate router + top-k calls' logits within the same bound."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfg = CONFIGS[cid]
+    if T is not None:
+        cfg = cfg.with_(T=T)
+    if E is not None:
+        cfg = cfg.with_(E=E)
+    if k is not None:
+        cfg = cfg.with_(k=k)
+    w, bias = make_router(cfg, 32)
+    x = make_x(cfg, 32)
+    xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    wt = torch.from_numpy(w.view(np.int16)).cuda()
+    bt = torch.from_numpy(bias).cuda()
+    log(f"[router_topk] cfg{cfg.cid} T={cfg.T} E={cfg.E} k={cfg.k}")
+    idx, gates, lg = moe.router_topk(xt, wt, bt, cfg.k)
+    idx2, gates2, lg2 = moe.router_topk(xt, wt, bt, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(lg, lg2) and torch.equal(idx, idx2), "not reproducible"
+    got = lg.cpu().numpy()
+    ref = oracle.router_logits(x, w, bias)
+    absx = np.abs((x.astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+    absw = np.abs((w.astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+    bound = (cfg.H + 2) * 2.0 ** -24 * (absx @ absw.T) + 2.0 ** -24 * np.abs(bias)[None, :] + 1e-30
+    err = np.abs(got.astype(np.float64) - ref)
+    log(f"[router_topk] max err / bound {np.max(err / bound):.3e}")
+    assert np.all(err <= bound)
+    idx_o, gates_o = oracle.route(got, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_o)
+    assert np.max(np.abs(gates.cpu().numpy() - gates_o)) <= 1e-6
