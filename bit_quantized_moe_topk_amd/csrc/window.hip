@@ -490,7 +490,7 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
     for (int i = tid; i < kB * 8 * kWinT; i += kWinThreads) {
       const int j = i / (8 * kWinT), pr = (i / kWinT) % 8, t = i % kWinT;
       const int p = p0 + j * kMmaSlices;
-      if (p < n_act && t < T) {  // every token (finite values) for the down tiles
+      if (p < n_act && t < T && ((wl.act_mask[p] >> t) & 1)) {  // the down roles read routed rows only
         const int ra = 4 * (pr >> 1) + (pr & 1), rb = ra + 2;
         float ga = 0.f, ua = 0.f, gb = 0.f, ub = 0.f;
 #pragma unroll
@@ -510,132 +510,172 @@ __device__ inline void gateup_role(const WinList& wl, int n_act, int role, int T
   }
 }
 
-// Down role: rows 16 grp .. 16 grp + 15 of H for every active expert; wave w
-// takes K half w & 1 and the experts w / 2, w / 2 + 4, ...: per expert a
-// 16-row x 16-token tile (tokens past T zero) on v_mfma_f32_16x16x32_bf16
-// (bf16 weights, bf16 h in the MFMA K order), scaled by the routing gates and
-// summed in registers; the eight partial tiles are added in LDS in wave order
-// and the role writes its rows of y. The weights of up to 4 kDnW experts are
-// requested before wait(), which returns once h is complete (false: it never
-// was; the rows become NaN). h then comes into LDS a round of experts at a
-// time into the two halves of hs in turn: the next round's h is in flight
-// while the current round computes.
-// experts per wave and round: a round's h fills half of hs
-template <int NBL>
-constexpr int dn_batch() {
-  return 4 / NBL;
-}
-constexpr int kHsBytes = 64 * 1024;   // LDS for h: two rounds of 8 experts at I = 512, 16 at I = 256
-constexpr int kHsHalf = kHsBytes / 2;
-
-constexpr int kDnW = 8;  // experts per wave whose down weights are in registers (32 experts)
+// Down role: rows 8 grp .. 8 grp + 7 of H for every active expert, on
+// v_mfma_f32_16x16x32_bf16 (bf16 weights, bf16 h in the MFMA K order). Wave w
+// takes K half w & 1 and the experts w / 2, w / 2 + 4, ... in pairs (p, p + 4):
+// a pair shares one 16 x 16 tile, rows 0-7 expert p's rows and rows 8-15
+// expert p + 4's, columns 0-3 the tokens' h of p and columns 4-7 those of
+// p + 4, so each expert's products sit in its own quarter of the tile (the
+// other quarters are discarded): a 16-row tile carries 8 rows of two experts,
+// which halves each role's dequantisation (the phase is VALU-bound) against
+// 16-row roles, over twice the roles. The quarters are scaled by the routing
+// gates and summed in registers; the eight waves' sums and the two halves are
+// added in LDS in a fixed order and the role writes its rows of y. The
+// weights of the first kDnW pairs per wave are requested before wait(), which
+// returns once h is complete (false: it never was; the rows become NaN). Only
+// the rows of h of routed (expert, token) pairs are read, packed in expert
+// order into hs by one copy right after the wait (44 rows at a 4-token window
+// with k = 10): one round trip of h, not one per round of experts.
+constexpr int kHsBytes = 64 * 1024;   // LDS for h: 63 rows of I = 512 or 127 of I = 256, and a zero row
+constexpr int kDnW = 8;     // tiles (expert pairs) per wave whose down weights are in registers
+constexpr int kDnRows = 8;  // rows of H per down role
 
 template <int Q, int NBL, typename Wait>
 __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, const Experts& ex,
                                  const uint16_t* hwin, void* y, int out_f32, uint16_t* hs,
                                  float (&red)[kWinWaves][16][kWinT], Wait&& wait) {
-  constexpr int kDnBatch = dn_batch<NBL>();
-  constexpr int RS = 4 * kDnBatch;            // experts per round
-  constexpr int kRounds = 4 * kDnW / RS;      // rounds per chunk of 4 kDnW experts
-  static_assert(RS * kWinT * (256 * NBL) * 2 <= kHsHalf, "h of one round fits half of hs");
+  constexpr int kMaxAct = 64 + 1;       // T k <= 64 routed experts, the shared one
+  constexpr int kMaxRows = 64 + kWinT;  // routed (expert, token) pairs
+  constexpr int kChunk = 8 * kDnW;      // experts per chunk of registers (4 waves x kDnW pairs)
+  __shared__ int hoff[kMaxAct + 1];     // first compact row of expert p; hoff[n_act] = rows
+  __shared__ int16_t hsrc[kMaxRows];    // compact row -> slot p kWinT + t of hwin
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  n_act = __builtin_amdgcn_readfirstlane(n_act);  // uniform: scalar loop bounds
   const int I = ex.I;
   const int c = lane >> 4, r16 = lane & 15;
   const int ks = wave & 1, eq = wave >> 1;
   const int kb0 = ks * (I / 64) + NBL * c;  // this lane's first block of the wave's K half
-  const size_t roff = (size_t)(16 * grp + r16) * (I / 32) + kb0;
-  const bool tok = r16 < T;
-  // the chunk's weights: experts c0 + eq + 4 j (the first chunk's before the wait)
+  // the lane's weight row: row r16 & 7 of the role, of the pair's expert r16 >> 3
+  const size_t roff = (size_t)(kDnRows * grp + (r16 & 7)) * (I / 32) + kb0;
+  // the lane's h column: token r16 & 3 of the pair's expert (r16 >> 2) & 1
+  // (columns 8-15 unused); its output quarter: rows of expert c >> 1
+  const int tcol = r16 & 3, hcol = (r16 >> 2) & 1;
+  const bool mine = r16 < 8 && hcol == (c >> 1) && tcol < T;
+  const int cap = kHsBytes / (2 * I) - 1;  // rows of h that fit hs; the row after them stays zero
+  // pair j of the chunk at c0: experts c0 + 8 j + eq and c0 + 8 j + eq + 4
   WRow<NBL> wd[kDnW];
   auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int j = 0; j < kDnW; ++j) {
-      const int p = c0 + eq + 4 * j;
-      if (p < n_act) wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[p]) + roff);
+      const int p = c0 + 8 * j + eq + 4 * (r16 >> 3);
+      if (p < n_act) {
+        wd[j] = load_wrow<Q, NBL>(ex, blk_down(ex, wl.act_e[p]) + roff);
+      } else {  // no such expert: zero weights (d = m = 0)
+#pragma unroll
+        for (int b = 0; b < NBL; ++b) {
+          wd[j].c[2 * b] = wd[j].c[2 * b + 1] = 0u;
+          wd[j].hi[b] = wd[j].dm[b] = 0u;
+        }
+      }
     }
   };
-  load_chunk(0);
-  const bool ok = wait();
-  // h of the round at r0 into half `half` of hs, straight into LDS (each
-  // lane's 16 bytes land at the wave's base + 16 lane), no registers held;
-  // every load in flight at once, agent-coherent (h was written in this
-  // launch on other CUs). Row (expert, token t)'s 16-byte chunk q lands at
-  // position q ^ t of the row, so the four token rows that a fragment read
-  // takes at one chunk sit on different banks.
-  auto copy = [&](int r0, int half) {
-    constexpr int kCopy = kHsHalf / 16 / kWinThreads;
-    constexpr int kCoherent = 16;  // cache policy: agent scope
-    const int n16 = min(RS, n_act - r0) * kWinT * I / 8;
-    const uint4* src = reinterpret_cast<const uint4*>(hwin) + (size_t)r0 * kWinT * I / 8;
-    uint4* dst = reinterpret_cast<uint4*>(hs) + half * (kHsHalf / 16);
+  // The compact list of the rows of h the role reads: the (expert, token)
+  // pairs of the routing in expert order (wave 0; before the weight requests,
+  // which then stay in flight through the wait).
+  if (__builtin_amdgcn_readfirstlane(wave) == 0) {
+    const int tm = (1 << T) - 1;
+    const int m0 = lane < n_act ? wl.act_mask[lane] & tm : 0;
+    const int m1 = lane + 64 < n_act ? wl.act_mask[lane + 64] & tm : 0;
+    const int i0 = wave_inclusive_scan(__popc(m0));
+    const int tot0 = __builtin_amdgcn_readlane(i0, 63);
+    const int i1 = wave_inclusive_scan(__popc(m1)) + tot0;
+    int o0 = i0 - __popc(m0), o1 = i1 - __popc(m1);
+    if (lane < n_act) hoff[lane] = o0;
+    if (lane + 64 < n_act) hoff[lane + 64] = o1;
+    if (lane == 0) hoff[n_act] = __builtin_amdgcn_readlane(i1, 63);
 #pragma unroll
-    for (int u = 0; u < kCopy; ++u)
-      if (tid + u * kWinThreads < n16)
-        __builtin_amdgcn_global_load_lds(src + ((tid + u * kWinThreads) ^ (((tid + u * kWinThreads) / (32 * NBL)) & (kWinT - 1))),
-                                         (__attribute__((address_space(3))) void*)(dst + u * kWinThreads + 64 * wave),
-                                         16, 0, kCoherent);
-  };
-  copy(0, 0);
+    for (int t = 0; t < kWinT; ++t) {
+      if ((m0 >> t) & 1) hsrc[o0++] = (int16_t)(lane * kWinT + t);
+      if ((m1 >> t) & 1) hsrc[o1++] = (int16_t)((lane + 64) * kWinT + t);
+    }
+  }
+  load_chunk(0);
+  // the zero row that stands for every other pair (their gate is 0)
+  for (int i = tid; i < I / 8; i += kWinThreads) reinterpret_cast<uint4*>(hs + (size_t)cap * I)[i] = make_uint4(0u, 0u, 0u, 0u);
+  const bool ok = wait();  // ends with a barrier
+  // every routed row of h straight into LDS (each lane's 16 bytes land at the
+  // wave's base + 16 lane), all in flight at once, agent-coherent (h was
+  // written in this launch on other CUs); chunk q of compact row r lands at
+  // position q ^ (r & 3), so the rows a fragment read takes at one chunk sit
+  // on different banks. The launch keeps every window's rows within hs
+  // (win_mma_ok). A wave's load covers 64 chunks: one row at I = 512, two at
+  // I = 256; its rows' sources are wave-uniform (scalar registers).
+  {
+    constexpr int kCopy = kHsBytes / 16 / kWinThreads;
+    constexpr int kCoherent = 16;  // cache policy: agent scope
+    const int n16 = __builtin_amdgcn_readfirstlane(hoff[n_act]) * (I / 8);
+    const uint4* src = reinterpret_cast<const uint4*>(hwin);
+    uint4* dst = reinterpret_cast<uint4*>(hs);
+#pragma unroll
+    for (int u = 0; u < kCopy; ++u) {
+      const int i0 = u * kWinThreads + 64 * wave;
+      if (i0 >= n16) break;
+      const int rl = i0 / (I / 8);
+      const int s0 = __builtin_amdgcn_readfirstlane(hsrc[rl]);
+      const int s1 = __builtin_amdgcn_readfirstlane(hsrc[min(rl + 1, kMaxRows - 1)]);
+      const int i = i0 + lane;
+      if (i < n16) {
+        const int r = i / (I / 8), q = i % (I / 8);
+        __builtin_amdgcn_global_load_lds(src + (size_t)(r == rl ? s0 : s1) * (I / 8) + (q ^ (r & 3)),
+                                         (__attribute__((address_space(3))) void*)(dst + i0), 16, 0,
+                                         kCoherent);
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the LDS writes have landed
   __syncthreads();
   floatx4_t acc = {};
-  for (int c0 = 0; c0 < n_act; c0 += 4 * kDnW) {
-    if (c0 > 0) {  // more than 4 kDnW experts: the next chunk's weights
+  for (int c0 = 0; c0 < n_act; c0 += kChunk) {
+    if (c0 > 0) {  // more than kChunk experts: the next chunk's weights
       load_chunk(c0);
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
 #pragma unroll
-    for (int rr = 0; rr < kRounds; ++rr) {
-      const int r0 = c0 + rr * RS;
-      if (r0 >= n_act) break;
-      const int half = (r0 / RS) & 1;
-      if (r0 + RS < n_act) copy(r0 + RS, half ^ 1);  // the next round, in flight during this one
-      const uint16_t* hb = hs + half * (kHsHalf / 2);
+    for (int j = 0; j < kDnW; ++j) {
+      const int p = c0 + 8 * j + eq;  // the pair (p, p + 4)
+      if (p >= n_act) break;
+      // the column's row: compact when its token is routed to its expert,
+      // else the zero row (columns 8-15, tokens past T, a missing p + 4)
+      const int pc = p + 4 * hcol;
+      const int m = r16 < 8 && pc < n_act ? wl.act_mask[pc] : 0;
+      const bool cv = (m >> tcol) & 1;
+      const int r = cv ? hoff[pc] + __popc(m & ((1 << tcol) - 1)) : cap;
+      const uint16_t* hp = hs + (size_t)r * I;
+      bf16x8_t hv[NBL][4];
 #pragma unroll
-      for (int jj = 0; jj < kDnBatch; ++jj) {
-        const int j = rr * kDnBatch + jj;
-        const int p = r0 + eq + 4 * jj;
-        if (p >= n_act) continue;
-        // columns past T read token 0's row (finite; their gate is 0): no
-        // branch, so all eight LDS reads of the expert issue together
-        const int tt = tok ? r16 : 0;
-        const uint16_t* hp = hb + ((size_t)(p - r0) * kWinT + tt) * I;
-        bf16x8_t hv[NBL][4];
+      for (int b = 0; b < NBL; ++b)
 #pragma unroll
-        for (int b = 0; b < NBL; ++b)
+        for (int t = 0; t < 4; ++t)
+          hv[b][t] = *reinterpret_cast<const bf16x8_t*>(hp + 8 * ((4 * (kb0 + b) + t) ^ (r & 3)));
+      floatx4_t o = {};
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            hv[b][t] = *reinterpret_cast<const bf16x8_t*>(hp + 8 * ((4 * (kb0 + b) + t) ^ tt));
-        floatx4_t o = {};
+      for (int b = 0; b < NBL; ++b) {
+        const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
 #pragma unroll
-        for (int b = 0; b < NBL; ++b) {
-          const WStage sw = wstage_block<Q>(wd[j].c[2 * b], wd[j].c[2 * b + 1], wd[j].hi[b], wd[j].dm[b]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag_bf<Q>(sw, t), hv[b][t], o, 0, 0, 0);
-        }
-        const float ga = wl.act_gate[p][r16 & (kWinT - 1)];
-        const float g = tok ? ga : 0.f;  // o[v]: row 4 c + v, token r16
-#pragma unroll
-        for (int v2 = 0; v2 < 4; ++v2) acc[v2] += g * o[v2];
+        for (int t = 0; t < 4; ++t)
+          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag_bf<Q>(sw, t), hv[b][t], o, 0, 0, 0);
       }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // the next round's h has landed
-      __syncthreads();                     // and every wave is done with this half
+      // o[v]: tile row 4 c + v, column r16; kept where the row's expert is
+      // the column's (c >> 1 == hcol)
+      const float g = mine && cv ? wl.act_gate[pc][tcol] : 0.f;
+#pragma unroll
+      for (int v2 = 0; v2 < 4; ++v2) acc[v2] += g * o[v2];
+      __builtin_amdgcn_sched_barrier(0);  // one pair's h operands in registers at a time
     }
   }
-  if (r16 < kWinT) {
+  if (mine) {  // (half, row, token): rows 4 c + v of the tile are row (4 c + v) & 7 of expert half c >> 1
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * c + v][r16] = acc[v];
+    for (int v = 0; v < 4; ++v) red[wave][4 * c + v][tcol] = acc[v];
   }
   __syncthreads();
-  if (tid < 16 * kWinT) {
+  if (tid < kDnRows * kWinT) {
     const int r = tid / kWinT, t = tid % kWinT;
     if (t < T) {
       float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWinWaves; ++w) s += red[w][r][t];
+      for (int w = 0; w < kWinWaves; ++w) s += red[w][r][t] + red[w][kDnRows + r][t];
       if (!ok) s = __uint_as_float(0x7FC00000u);
-      const size_t o = (size_t)t * ex.H + 16 * grp + r;
+      const size_t o = (size_t)t * ex.H + kDnRows * grp + r;
       if (out_f32) static_cast<float*>(y)[o] = s;
       else static_cast<uint16_t*>(y)[o] = (uint16_t)f32_to_bf16_bits(s);
     }
@@ -651,8 +691,10 @@ __device__ inline void down_role(const WinList& wl, int n_act, int grp, int T, c
 // launch's groups. So after n complete launches every up[g] = 16 n and
 // epoch = n, and a launch finds them consistent whatever happened in earlier
 // ones, including waits that timed out (late gate/up roles still finish
-// before their launch ends). dn_all counts the down roles of the running
-// launch; its last down role sets it back to zero and raises epoch. `guard`
+// before their launch ends). dn[16] count the down roles of the running
+// launch (ceil(D / 16) per line) and dn_all the lines that completed; the
+// last role of a line zeroes it, the launch's last down role zeroes dn_all
+// and raises epoch, so both are zero between launches. `guard`
 // is never written: non-zero means the head was not zeroed. `spin`: 0, or a
 // bound in wall-clock ticks on the down roles' wait (a testing aid).
 // Launches that start from hidden states (RT launches): rt_seq[r] counts
@@ -676,13 +718,14 @@ struct WinSync {
   uint32_t guard[kSyncLine];
   uint32_t spin[kSyncLine];
   uint32_t epoch[kSyncLine];     // launches completed
-  uint32_t dn_all[kSyncLine];    // down roles finished (this launch)
+  uint32_t dn_all[kSyncLine];    // down-role lines complete (this launch)
   uint32_t up[16][kSyncLine];    // gate/up roles of group g whose h is released
   uint32_t rt_epoch[kSyncLine];  // RT launches completed
   uint32_t rt_seq[kSyncLine];    // RT launches seen by router role r (r < 32)
   uint32_t rt_all[kSyncLine];    // router roles whose logits are issued (this launch)
   uint32_t go[16][kSyncLine];    // n + 1 once every router role of launch n has issued its logits
   uint32_t poison[kSyncLine];    // epoch + 1: a workgroup of that launch routed without logits
+  uint32_t dn[16][kSyncLine];    // down roles finished (this launch), ceil(D / 16) per line
 };
 static_assert(sizeof(WinSync) <= kWinSyncBytes, "the window counters fit the workspace head");
 
@@ -870,7 +913,7 @@ void win_layer(float* lg, uint64_t* lgp, const uint16_t* __restrict__ rw, const 
   __shared__ int xe_w[kWinT];  // per-token exponents of the fp16 activations
   const int tid = threadIdx.x;
   const int H = ex.H;
-  const int G = ex.I / 16 * kMmaSlices, D = H / 16;
+  const int G = ex.I / 16 * kMmaSlices, D = H / kDnRows;
   const int NR = RT ? (ex.E + kRtExperts - 1) / kRtExperts : 0;
   if (RT && (int)blockIdx.x < NR) {
     __shared__ uint32_t tag_s;
@@ -1068,23 +1111,32 @@ void win_layer(float* lg, uint64_t* lgp, const uint16_t* __restrict__ rw, const 
   const int grp = role - G;
   down_role<Q, NBD>(R.wl, n_act, grp, T, ex, hwin, y, out_f32, reinterpret_cast<uint16_t*>(buf),
                     red_dn, wait);
-  if (tid == 0 && sync_add(sync->dn_all) == (uint32_t)(D - 1)) {
-    // the launch's last down role (timed-out roles count too): top up the
-    // groups this launch's shape has none of, reset the down count, close the
-    // launch
-    for (int g = G / kSyncGroup; g < 16; ++g) sync_add(sync->up[g], (uint32_t)kSyncGroup);
-    if (RT) {
-      for (int r = NR; r < kSyncLine; ++r) sync_add(&sync->rt_seq[r]);
-      sync_add(sync->rt_epoch);
+  // Completion: each down role counts on one of 16 lines (ceil(D / 16) roles
+  // per line; atomics on one address serialise, so no single counter takes
+  // all D adds); the last role of a line resets it and counts the line on
+  // dn_all, and the role that completes dn_all is the launch's last (timed-out
+  // roles count too): it tops up the groups this launch's shape has none of,
+  // resets dn_all and closes the launch.
+  const int per = (D + 15) / 16, line = grp / per, in_line = min(per, D - line * per);
+  if (tid == 0 && sync_add(sync->dn[line]) == (uint32_t)(in_line - 1)) {
+    sync_zero(sync->dn[line]);
+    if (sync_add(sync->dn_all) == (uint32_t)((D + per - 1) / per - 1)) {
+      for (int g = G / kSyncGroup; g < 16; ++g) sync_add(sync->up[g], (uint32_t)kSyncGroup);
+      if (RT) {
+        for (int r = NR; r < kSyncLine; ++r) sync_add(&sync->rt_seq[r]);
+        sync_add(sync->rt_epoch);
+      }
+      sync_zero(sync->dn_all);
+      sync_add(sync->epoch);
     }
-    sync_zero(sync->dn_all);
-    sync_add(sync->epoch);
   }
 }
 
 inline bool win_mma_ok(const Experts& ex, int T, int k) {
+  // the down roles hold every routed (expert, token) row of h in LDS at once
+  const int rows = T * k + T * ex.has_shared;
   return ex.H % 1024 == 0 && ex.H <= kMmaMaxH && (ex.I == 256 || ex.I == 512) &&
-         ex.E <= 64 * kLayerPer && T * k <= 64;
+         ex.E <= 64 * kLayerPer && T * k <= 64 && rows <= kHsBytes / (2 * ex.I) - 1;
 }
 
 template <int BPR_H, int BPR_I, int Q, bool XF32>
@@ -1103,7 +1155,7 @@ hipError_t launch_layer(float* lg, uint64_t* lgp, const uint16_t* rw, const floa
                         const Experts& ex, const void* x, int32_t* idx, float* gates, uint16_t* hwin,
                         void* y, int out_f32, WinSync* sync, hipStream_t s) {
   const int NR = RT ? (ex.E + kRtExperts - 1) / kRtExperts : 0;
-  const dim3 grid(NR + ex.I / 16 * kMmaSlices + ex.H / 16);
+  const dim3 grid(NR + ex.I / 16 * kMmaSlices + ex.H / kDnRows);
   const char* name = RT ? "win_layer_rt" : "win_layer";
 #define L(NBG, NBD)                                                                               \
   MOE_LAUNCH(name, s, (win_layer<Q, XF32, NBG, NBD, RT>), grid, dim3(kWinThreads), 0, s, lg, lgp, \

@@ -161,15 +161,18 @@ def test_layer_call(cid, T, mode):
 
 
 @pytest.mark.parametrize("name,kw", [("f32 activations", dict(xdtype="f32")),
-                                     ("k=16: 64 assignments", dict(k=16)),
+                                     ("k=14: 60 rows of h", dict(k=14)),
+                                     ("k=16: 64 assignments, two-kernel window", dict(k=16)),
                                      ("k=20: two-kernel window", dict(k=20)),
                                      ("H=4096, I=256", dict(H=4096, I=256, E=16, k=2)),
                                      ("Q3, H=1024", dict(qtype=3, H=1024, E=64, k=4))])
 def test_layer_window_variants(name, kw):
-    """The decode window at the config-1 shapes with float32 activations, at
-    the one-kernel form's assignment limit (T k = 64) and past it (the
-    two-kernel form at H = 2048), and at the one-kernel form's other shapes
-    (H = 4096 with I = 256; Q3 at H = 1024), against the oracle."""
+    """The decode window at the config-1 shapes with float32 activations, near
+    the one-kernel form's limit (its down roles hold every routed (expert,
+    token) row of h in 64 KB of LDS: 63 rows at I = 512, so T k + T <= 63 with
+    the shared expert) and past it (the two-kernel form at H = 2048), and at
+    the one-kernel form's other shapes (H = 4096 with I = 256; Q3 at
+    H = 1024), against the oracle."""
     torch = torch_cuda()
     import bit_quantized_moe_topk_amd as moe
     cfg = CONFIGS[1].with_(**kw)
