@@ -243,7 +243,9 @@ size_t moe_layer_workspace_size(const moe_experts *ex, int32_t T, int32_t k, int
  * A decode verify window ("Strata - the details", "How it works": the drafted
  * tokens are checked in one pass) is fast mode with T <= 4, k <= 64 and H/32,
  * I/32 in {4..64}. With H a multiple of 1024 up to 4096, I 256 or 512,
- * E <= 512 and T k <= 64 it runs as ONE kernel: every workgroup routes the
+ * E <= 512, T k <= 64 and T k + T (with a shared expert; T k without) at most
+ * 32768 / I - 1 (the routed rows of h that the down rows hold at once: 63 at
+ * I = 512, so k <= 14 at T = 4) it runs as ONE kernel: every workgroup routes the
  * window itself; the first workgroups compute gate/up rows, the others down
  * rows once counters at the head of `ws` show every gate/up row released; y is
  * reproducible run to run. Other windows run as two kernels (gate/up, then
