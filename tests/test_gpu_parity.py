@@ -190,6 +190,34 @@ def test_layer_window_variants(name, kw):
     ex.close()
 
 
+def test_layer_window_65_active_experts():
+    """A one-kernel window at I = 256 whose four tokens pick 16 distinct
+    experts each (64 routed + the shared expert = 65 active): the down roles
+    hold 64 experts' weights in registers at a time, so the 65th comes from a
+    second chunk of weight requests after the first chunk's products; against
+    the oracle."""
+    torch = torch_cuda()
+    import bit_quantized_moe_topk_amd as moe
+    cfg = CONFIGS[1].with_(I=256, k=16)
+    lay = make_layer(cfg, seed=27)
+    lg = lay["logits"].copy()
+    for t in range(cfg.T):  # token t's top 16: experts 16 t + 100 .. 16 t + 115
+        lg[t, 100 + 16 * t:116 + 16 * t] = 40.0 + np.arange(16, dtype=np.float32) * 0.25
+    lay = dict(lay, logits=lg)
+    dev = upload(lay)
+    ex = experts_of(lay, dev)
+    log("[window 65 experts] I=256 k=16")
+    idx, gates, y = moe.layer(dev["logits"], dev["x"], ex, cfg.k)
+    torch.cuda.synchronize()
+    idx_o, g_o = oracle.route(lg, cfg.k)
+    assert len(set(idx_o.ravel().tolist())) == 64
+    assert np.array_equal(idx.cpu().numpy(), idx_o)
+    err = rel_l2_rows(y_to_f64(y), oracle_rows(lay, idx_o, g_o))
+    log(f"[window 65 experts] max rel-L2 {err.max():.3e}")
+    assert err.max() <= TOL_FAST
+    ex.close()
+
+
 def test_layer_window_shared_workspace():
     """One zero-filled workspace serves window calls of two layer instances,
     repeated, with a 64-token call of the same experts in between: the
