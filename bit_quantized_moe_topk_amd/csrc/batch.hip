@@ -124,13 +124,22 @@ __device__ inline BatItem bat_item_seq(const int* base, const int* off, int E_to
   return it;
 }
 
-// Column of this workgroup: it takes items column * rows .. column * rows +
-// rows - 1. Neighbouring columns go to workgroups of one XCD (workgroup g runs
+// Column of this workgroup (its run of items is bat_run's). Neighbouring
+// columns go to workgroups of one XCD (workgroup g runs
 // on XCD g % 8) when the grid is a multiple of 8, so the token groups of one
 // expert, which read the same weights, meet in that XCD's L2.
 __device__ inline int bat_first() {
   const int g = blockIdx.x, G = gridDim.x;
   return (G % 8) ? g : (g % 8) * (G / 8) + g / 8;
+}
+
+// The run of this workgroup's column: items [c n / G, (c + 1) n / G), so the
+// runs differ by at most one item and every column has work when n >= G
+// (runs of ceil(n / G) would leave the last columns, i.e. whole XCDs, idle).
+__device__ inline void bat_run(int n_items, int& first, int& end) {
+  const long long c = bat_first(), G = gridDim.x;
+  first = (int)(c * n_items / G);
+  end = (int)((c + 1) * n_items / G);
 }
 
 // --- gate/up ----------------------------------------------------------------
@@ -268,9 +277,8 @@ void bat_gateup(Experts ex, FfnArgs a) {
   const int NC = I / (16 * R);
   const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
   // a run of consecutive items per workgroup
-  const int rows = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
-  int item = bat_first() * rows;
-  const int item_end = min(n_items, item + rows);
+  int item, item_end;
+  bat_run(n_items, item, item_end);
   if (item >= item_end) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
@@ -417,9 +425,8 @@ void bat_down(Experts ex, FfnArgs a) {
   const int n_items = __builtin_amdgcn_readfirstlane(bm.n * NC);  // uniform: scalar branches
   // runs of consecutive items in (expert, token group, chunk) order, as in
   // the gate/up kernel: a token group's h rows stay in LDS for its run
-  const int rows = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
-  int item = bat_first() * rows;
-  const int item_end = min(n_items, item + rows);
+  int item, item_end;
+  bat_run(n_items, item, item_end);
   if (item >= item_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane >> 4, r16 = lane & 15;
